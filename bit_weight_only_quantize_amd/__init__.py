@@ -1,0 +1,238 @@
+"""Python binding for libw4a16.so: group-wise 4-bit weight-only quantization with
+the dequantization fused into the matrix products, for AMD MI355X (gfx950).
+
+This module only marshals arguments: every step runs in the HIP library's
+kernels. PyTorch supplies device memory and the current stream. There is no
+CPU fallback: if the library is missing or fails to load, every call raises.
+
+Schemes (see include/w4a16.h):
+  "sym4_g128"  symmetric 4-bit, 128 weights/group, fp32 scale = absmax/7
+               (airllm article §2.1, §4.2)
+  "aff4_g64"   affine 4-bit, 64 weights/group, bf16 scale + bf16 bias
+               (TurboFieldfare article, section 量化和精度)
+  "aff8_g64"   the same affine format with 8-bit codes (the router)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "SCHEME_IDS", "W4Error", "QuantizedMatrix", "lib", "lib_path", "packed_sizes", "quantize_pack",
+    "empty_quantized", "gemv", "gemv_into", "gemm", "moe_route", "moe_workspace_bytes", "moe_gemv",
+]
+
+SCHEME_IDS = {"sym4_g128": 0, "aff4_g64": 1, "aff8_g64": 2}
+_ERRORS = {-1: "W4_EINVAL", -2: "W4_ESHAPE", -3: "W4_EALIGN", -4: "W4_EHIP", -5: "W4_EWORKSPACE"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libw4a16.so")
+_lib: Optional[ctypes.CDLL] = None
+
+
+class W4Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class _W4Matrix(ctypes.Structure):
+    _fields_ = [("scheme", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIGS = {
+    "w4_last_error": ([], ctypes.c_char_p),
+    "w4_packed_sizes": ([ctypes.c_int, _I64, _I64, ctypes.POINTER(ctypes.c_size_t),
+                         ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "w4_quantize_pack": ([ctypes.c_int, _P, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
+    "w4a16_gemv": ([ctypes.POINTER(_W4Matrix), _P, _I64, _P, _P], ctypes.c_int),
+    "w4a16_gemm": ([ctypes.POINTER(_W4Matrix), _P, _I64, _P, _P], ctypes.c_int),
+    "w4_moe_route": ([ctypes.POINTER(_W4Matrix), _P, _I64, ctypes.c_int, _P, _P, _P, _P], ctypes.c_int),
+    "w4_moe_workspace_bytes": ([_I64, ctypes.c_int, _I64, _I64, _I64, _I64], ctypes.c_size_t),
+    "w4a16_moe_gemv": ([ctypes.POINTER(_W4Matrix)] * 6 + [_P, _I64, _P, _P, ctypes.c_int, _P,
+                                                          ctypes.c_size_t, _P, _P], ctypes.c_int),
+}
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw4a16.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(hipcc --offload-arch=gfx950); there is no fallback path")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise W4Error(rc, lib().w4_last_error().decode(errors="replace"))
+
+
+def _stream(device=None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def packed_sizes(scheme: str, N: int, K: int):
+    c, s, b = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().w4_packed_sizes(SCHEME_IDS[scheme], N, K, ctypes.byref(c), ctypes.byref(s),
+                                 ctypes.byref(b)))
+    return c.value, s.value, b.value
+
+
+@dataclass
+class QuantizedMatrix:
+    """Storage form of one quantized matrix (or a fixed-stride stack of experts).
+
+    codes: uint8 [E][N][K*bits/8]; scale: fp32 [E][N][K/128] (sym) or bf16
+    [E][N][K/64]; bias: bf16 [E][N][K/64] or None. E = num_experts (leading
+    dimension omitted when 1)."""
+    scheme: str
+    N: int
+    K: int
+    codes: torch.Tensor
+    scale: torch.Tensor
+    bias: Optional[torch.Tensor]
+    num_experts: int = 1
+
+    def desc(self) -> _W4Matrix:
+        return _W4Matrix(SCHEME_IDS[self.scheme], self.num_experts, self.N, self.K,
+                         _ptr(self.codes), _ptr(self.scale), _ptr(self.bias))
+
+    def expert(self, e: int) -> "QuantizedMatrix":
+        if self.num_experts == 1:
+            return self
+        return QuantizedMatrix(self.scheme, self.N, self.K, self.codes[e], self.scale[e],
+                               None if self.bias is None else self.bias[e], 1)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.codes, self.scale, self.bias)
+                   if t is not None)
+
+
+def empty_quantized(scheme: str, N: int, K: int, num_experts: int = 1, device="cuda") -> QuantizedMatrix:
+    packed_sizes(scheme, N, K)  # validates the shape
+    lead = (num_experts,) if num_experts > 1 else ()
+    bits = 8 if scheme == "aff8_g64" else 4
+    codes = torch.empty(lead + (N, K * bits // 8), dtype=torch.uint8, device=device)
+    if scheme == "sym4_g128":
+        scale = torch.empty(lead + (N, K // 128), dtype=torch.float32, device=device)
+        bias = None
+    else:
+        scale = torch.empty(lead + (N, K // 64), dtype=torch.bfloat16, device=device)
+        bias = torch.empty(lead + (N, K // 64), dtype=torch.bfloat16, device=device)
+    return QuantizedMatrix(scheme, N, K, codes, scale, bias, num_experts)
+
+
+def quantize_pack(W: torch.Tensor, scheme: str, out: Optional[QuantizedMatrix] = None,
+                  expert: Optional[int] = None) -> QuantizedMatrix:
+    """Quantize fp32 weights W[N][K] on the device (into `out`, or expert `expert` of it)."""
+    _dev(W, "W")
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise ValueError("W must be a 2-D float32 tensor")
+    N, K = W.shape
+    q = out if out is not None else empty_quantized(scheme, N, K, device=W.device)
+    tgt = q.expert(expert) if expert is not None else q
+    _check(lib().w4_quantize_pack(SCHEME_IDS[scheme], _ptr(W), N, K, _ptr(tgt.codes),
+                                  _ptr(tgt.scale), _ptr(tgt.bias), _stream(W.device)))
+    return q
+
+
+def _as_bf16_bits(x: torch.Tensor, name: str) -> torch.Tensor:
+    _dev(x, name)
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError(f"{name} must hold bf16 values")
+    return x
+
+
+def gemv_into(W: QuantizedMatrix, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+    x = _as_bf16_bits(x, "x")
+    M = x.shape[0] if x.dim() == 2 else 1
+    d = W.desc()
+    _check(lib().w4a16_gemv(ctypes.byref(d), _ptr(x), M, _ptr(y), _stream(x.device)))
+    return y
+
+
+def gemv(W: QuantizedMatrix, x: torch.Tensor) -> torch.Tensor:
+    """y[M][N] (fp32) = x[M][K] (bf16) · dequant(W)^T, dequantization fused in the kernel."""
+    M = x.shape[0] if x.dim() == 2 else 1
+    y = torch.empty((M, W.N), dtype=torch.float32, device=x.device)
+    return gemv_into(W, x, y)
+
+
+def gemm(W: QuantizedMatrix, X: torch.Tensor, Y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Prefill: Y[M][N] (bf16) = X[M][K] (bf16) · dequant(W)^T with fp32 accumulation."""
+    X = _as_bf16_bits(X, "X")
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, W.N), dtype=torch.bfloat16, device=X.device)
+    d = W.desc()
+    _check(lib().w4a16_gemm(ctypes.byref(d), _ptr(X), M, _ptr(Y), _stream(X.device)))
+    return Y
+
+
+def moe_route(router: QuantizedMatrix, x: torch.Tensor, top_k: int = 8, want_logits: bool = False):
+    """(ids int32 [M][k], weights fp32 [M][k], logits fp32 [M][E] or None)."""
+    x = _as_bf16_bits(x, "x")
+    M = x.shape[0]
+    ids = torch.empty((M, top_k), dtype=torch.int32, device=x.device)
+    w = torch.empty((M, top_k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((M, router.N), dtype=torch.float32, device=x.device) if want_logits else None
+    d = router.desc()
+    _check(lib().w4_moe_route(ctypes.byref(d), _ptr(x), M, top_k, _ptr(logits), _ptr(ids), _ptr(w),
+                              _stream(x.device)))
+    return ids, w, logits
+
+
+def moe_workspace_bytes(M: int, top_k: int, E: int, D: int, F: int, Fs: int = 0) -> int:
+    return int(lib().w4_moe_workspace_bytes(M, top_k, E, D, F, Fs))
+
+
+def moe_gemv(gate: QuantizedMatrix, up: QuantizedMatrix, down: QuantizedMatrix, x: torch.Tensor,
+             ids: torch.Tensor, weights: torch.Tensor, shared=None, workspace=None,
+             y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MoE FFN over the selected experts plus an optional shared expert (gate, up, down)."""
+    x = _as_bf16_bits(x, "x")
+    M, top_k = ids.shape
+    E, F, D = gate.num_experts, gate.N, gate.K
+    Fs = shared[0].N if shared is not None else 0
+    need = moe_workspace_bytes(M, top_k, E, D, F, Fs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((M, D), dtype=torch.float32, device=x.device)
+    descs = [m.desc() for m in (gate, up, down)]
+    sh = [s.desc() for s in shared] if shared is not None else [None, None, None]
+    refs = [ctypes.byref(d) for d in descs] + [ctypes.byref(s) if s is not None else None for s in sh]
+    _check(lib().w4a16_moe_gemv(*refs, _ptr(x), M, _ptr(ids), _ptr(weights), top_k, _ptr(workspace),
+                                workspace.numel(), _ptr(y), _stream(x.device)))
+    return y

@@ -1,0 +1,138 @@
+// C-ABI entry points: host-side validation, error reporting and dispatch.
+// Every check runs before anything is enqueued, so a failing call launches nothing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/w4a16.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return W4_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(W4_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int group_of(int scheme) { return scheme == W4_SYM4_G128 ? 128 : 64; }
+int bits_of(int scheme) { return scheme == W4_AFF8_G64 ? 8 : 4; }
+bool known(int scheme) {
+    return scheme == W4_SYM4_G128 || scheme == W4_AFF4_G64 || scheme == W4_AFF8_G64;
+}
+
+// Checks a w4_matrix descriptor; `experts` = required num_experts (0 = any >= 1).
+int check_matrix(const w4_matrix* W, const char* name, int experts) {
+    if (!W) return fail(W4_EINVAL, "%s: null descriptor", name);
+    if (!known(W->scheme)) return fail(W4_EINVAL, "%s: unknown scheme %d", name, (int)W->scheme);
+    if (W->num_experts < 1 || (experts && W->num_experts != experts))
+        return fail(W4_ESHAPE, "%s: num_experts %d", name, (int)W->num_experts);
+    if (W->N < 0 || W->K <= 0) return fail(W4_ESHAPE, "%s: N=%lld K=%lld", name, (long long)W->N,
+                                          (long long)W->K);
+    if (W->K % group_of(W->scheme))
+        return fail(W4_ESHAPE, "%s: K=%lld is not a multiple of the group size %d", name,
+                    (long long)W->K, group_of(W->scheme));
+    if (W->N > 0x7fffffffLL || W->K > 0x7fffffffLL)
+        return fail(W4_ESHAPE, "%s: N and K must fit in 31 bits", name);
+    if (!W->codes || !W->scale) return fail(W4_EINVAL, "%s: null codes or scale", name);
+    if (W->scheme != W4_SYM4_G128 && !W->bias)
+        return fail(W4_EINVAL, "%s: affine scheme needs a bias array", name);
+    if (!aligned16(W->codes) || !aligned16(W->scale) || (W->bias && !aligned16(W->bias)))
+        return fail(W4_EALIGN, "%s: codes/scale/bias must be 16-byte aligned", name);
+    return W4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4_last_error(void) { return g_err; }
+
+int w4_packed_sizes(int scheme, int64_t N, int64_t K, size_t* codes_bytes, size_t* scale_bytes,
+                    size_t* bias_bytes) {
+    if (!known(scheme)) return fail(W4_EINVAL, "unknown scheme %d", scheme);
+    if (N < 0 || K < 0 || K % group_of(scheme))
+        return fail(W4_ESHAPE, "N=%lld K=%lld (K must be a multiple of %d)", (long long)N,
+                    (long long)K, group_of(scheme));
+    const size_t groups = (size_t)N * (size_t)(K / group_of(scheme));
+    if (codes_bytes) *codes_bytes = (size_t)N * (size_t)K * bits_of(scheme) / 8;
+    if (scale_bytes) *scale_bytes = groups * (scheme == W4_SYM4_G128 ? 4 : 2);
+    if (bias_bytes) *bias_bytes = scheme == W4_SYM4_G128 ? 0 : groups * 2;
+    return ok();
+}
+
+int w4_quantize_pack(int scheme, const float* W, int64_t N, int64_t K, void* codes, void* scale,
+                     void* bias, void* stream) {
+    if (!known(scheme)) return fail(W4_EINVAL, "unknown scheme %d", scheme);
+    if (N < 0 || K <= 0 || K % group_of(scheme))
+        return fail(W4_ESHAPE, "N=%lld K=%lld (K must be a positive multiple of %d)",
+                    (long long)N, (long long)K, group_of(scheme));
+    if (N == 0) return ok();
+    if (!W || !codes || !scale || (scheme != W4_SYM4_G128 && !bias))
+        return fail(W4_EINVAL, "null pointer argument");
+    if (!aligned16(W) || !aligned16(codes) || !aligned16(scale) || (bias && !aligned16(bias)))
+        return fail(W4_EALIGN, "device pointers must be 16-byte aligned");
+    return hip_status(w4::launch_quantize_pack(scheme, W, N, K, codes, scale, bias,
+                                               (hipStream_t)stream),
+                      "quantize_pack launch");
+}
+
+int w4a16_gemv(const w4_matrix* W, const uint16_t* x, int64_t M, float* y, void* stream) {
+    int rc = check_matrix(W, "W", 1);
+    if (rc) return rc;
+    if (M < 0 || M > 64) return fail(W4_ESHAPE, "M=%lld out of range [0, 64]", (long long)M);
+    if (M == 0 || W->N == 0) return ok();
+    if (W->K > w4::kMaxSkinnyK)
+        return fail(W4_ESHAPE, "K=%lld exceeds the GEMV limit %lld", (long long)W->K,
+                    (long long)w4::kMaxSkinnyK);
+    if (!x || !y) return fail(W4_EINVAL, "null x or y");
+    if (!aligned16(x) || !aligned16(y)) return fail(W4_EALIGN, "x and y must be 16-byte aligned");
+    return hip_status(w4::launch_gemv(W->scheme, W->codes, W->scale, W->bias, W->N, W->K, x, M, y,
+                                      (hipStream_t)stream),
+                      "gemv launch");
+}
+
+int w4a16_gemm(const w4_matrix* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream) {
+    (void)W; (void)X; (void)M; (void)Y; (void)stream;
+    return fail(W4_EINVAL, "w4a16_gemm: not built yet");
+}
+
+int w4_moe_route(const w4_matrix* router, const uint16_t* x, int64_t M, int top_k, float* logits,
+                 int32_t* ids, float* weights, void* stream) {
+    (void)router; (void)x; (void)M; (void)top_k; (void)logits; (void)ids; (void)weights; (void)stream;
+    return fail(W4_EINVAL, "w4_moe_route: not built yet");
+}
+
+size_t w4_moe_workspace_bytes(int64_t M, int top_k, int64_t E, int64_t D, int64_t F, int64_t Fs) {
+    (void)M; (void)top_k; (void)E; (void)D; (void)F; (void)Fs;
+    return 0;
+}
+
+int w4a16_moe_gemv(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
+                   const w4_matrix* shared_gate, const w4_matrix* shared_up,
+                   const w4_matrix* shared_down, const uint16_t* x, int64_t M,
+                   const int32_t* ids, const float* weights, int top_k, void* workspace,
+                   size_t workspace_bytes, float* y, void* stream) {
+    (void)gate; (void)up; (void)down; (void)shared_gate; (void)shared_up; (void)shared_down;
+    (void)x; (void)M; (void)ids; (void)weights; (void)top_k; (void)workspace;
+    (void)workspace_bytes; (void)y; (void)stream;
+    return fail(W4_EINVAL, "w4a16_moe_gemv: not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,184 @@
+// Decode GEMV / skinny GEMM with the dequantization fused into the product.
+//
+// airllm article §2.2: dequantize inside the matmul kernel, in registers, right
+// after the weights are loaded; §3.3: decode is memory-bound, so the kernel is
+// built to stream the packed codes at HBM speed. See skinny.hpp for the
+// per-lane arithmetic.
+#include "common.hpp"
+#include "launch.hpp"
+#include "skinny.hpp"
+
+namespace w4 {
+
+constexpr int kThreads = 256;  // 4 wavefronts per workgroup
+
+template <int S, int MT, int LPR, int V, int R>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ scale,
+                                                        const uint8_t* __restrict__ bias, int N,
+                                                        int K, const uint16_t* __restrict__ x,
+                                                        int M, float* __restrict__ y) {
+    using T = Traits<S>;
+    using Core = SkinnyCore<S, MT, LPR, V, R>;
+    extern __shared__ __align__(16) uint32_t smem[];
+    constexpr int RSW = 64 / LPR;  // row slots per wavefront
+    const int VR = K / T::KV;
+    const int xstride = K / 2;
+    uint32_t* xs = smem;
+    float* XS = reinterpret_cast<float*>(smem + MT * xstride);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int slot = lane / LPR, sl = lane % LPR;
+    const int64_t rowbytes = (int64_t)K * T::BITS / 8;
+    const int64_t groups = K / T::GROUP;
+    constexpr int SB = T::AFFINE ? 2 : 4;
+
+    Core core;
+    core.VR = VR;
+    core.sl = sl;
+    int n[R];
+    const int base = blockIdx.x * (4 * RSW * R) + wave * (RSW * R) + slot;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        n[r] = base + r * RSW;
+        const int64_t nl = n[r] < N ? n[r] : N - 1;  // rows past the end re-read the last row
+        core.crow[r] = codes + nl * rowbytes;
+        core.srow[r] = scale + nl * groups * SB;
+        core.brow[r] = T::AFFINE ? bias + nl * groups * 2 : nullptr;
+    }
+    typename Core::Buf A, B;
+    for (int t0 = 0; t0 < M; t0 += MT) {
+        const int mt = min(MT, M - t0);
+        core.load(A, 0);  // first code vectors in flight while the activations are staged
+        if (t0) __syncthreads();
+        stage_x<S, MT, V, kThreads>(x + (int64_t)t0 * K, K, nullptr, mt, K, xs, XS);
+        __syncthreads();
+        float acc[R][MT];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
+        core.run(A, B, xs, XS, xstride, acc);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[r][m] = group_sum<LPR>(acc[r][m]);
+        if (sl == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    if (n[r] < N && m < mt) y[(int64_t)(t0 + m) * N + n[r]] = acc[r][m];
+        }
+    }
+}
+
+static size_t lds_bytes(int scheme, int64_t K, int mt) {
+    const int kv = scheme == AFF8_G64 ? 16 : 32;
+    return (size_t)mt * (size_t)(K / 2 + K / kv) * 4;
+}
+
+GemvPlan plan_gemv(int scheme, int64_t N, int64_t K, int64_t M) {
+    const int kv = scheme == AFF8_G64 ? 16 : 32;
+    const int vpg = scheme == AFF4_G64 ? 2 : 4;
+    const int64_t VR = K / kv;
+    GemvPlan best{64, 1, 2, 1, 0, 0};
+    double best_score = -1;
+    int mt = M >= 4 ? 4 : (M >= 2 ? 2 : 1);
+    while (mt > 1 && lds_bytes(scheme, K, mt) > 65536) mt /= 2;
+    const int lprs8[] = {64, 16};
+    const int lprs4[] = {64, 32, 16, 8};
+    const int* lprs = scheme == AFF8_G64 ? lprs8 : lprs4;
+    const int nl = scheme == AFF8_G64 ? 2 : 4;
+    for (int li = 0; li < nl; ++li) {
+        const int lpr = lprs[li];
+        for (int v = 2; v >= 1; --v) {
+            if (scheme == AFF8_G64 && v != 1) continue;
+            if (v > vpg) continue;
+            for (int r = 4; r >= 2; r -= 2) {
+                if (scheme == AFF8_G64 && r != 2) continue;
+                const int64_t rows_wg = 4LL * (64 / lpr) * r;
+                const int64_t wgs = (N + rows_wg - 1) / rows_wg;
+                const int64_t steps = (VR + lpr * v - 1) / (lpr * v);
+                const double lane_eff = (double)VR / (double)(steps * lpr * v);
+                const double row_eff = (double)N / (double)(wgs * rows_wg);
+                const double fill = wgs >= 512 ? 1.0 : (double)wgs / 512.0;
+                const double score = lane_eff * row_eff * fill;
+                if (score > best_score + 1e-9) {
+                    best_score = score;
+                    best = GemvPlan{lpr, v, r, mt, wgs, lds_bytes(scheme, K, mt)};
+                }
+            }
+        }
+    }
+    return best;
+}
+
+template <int S, int MT, int LPR, int V, int R>
+static hipError_t go(const GemvPlan& p, const void* codes, const void* scale, const void* bias,
+                     int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                     hipStream_t st) {
+    hipLaunchKernelGGL((gemv_kernel<S, MT, LPR, V, R>), dim3((unsigned)p.blocks), dim3(kThreads),
+                       p.lds, st, (const uint8_t*)codes, (const uint8_t*)scale,
+                       (const uint8_t*)bias, (int)N, (int)K, x, (int)M, y);
+    return hipGetLastError();
+}
+
+template <int S, int MT, int LPR, int V>
+static hipError_t pick_r(const GemvPlan& p, const void* c, const void* s, const void* b,
+                         int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                         hipStream_t st) {
+    if constexpr (S == AFF8_G64) return go<S, MT, LPR, V, 2>(p, c, s, b, N, K, x, M, y, st);
+    else if (p.r == 4) return go<S, MT, LPR, V, 4>(p, c, s, b, N, K, x, M, y, st);
+    else return go<S, MT, LPR, V, 2>(p, c, s, b, N, K, x, M, y, st);
+}
+
+template <int S, int MT, int LPR>
+static hipError_t pick_v(const GemvPlan& p, const void* c, const void* s, const void* b,
+                         int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                         hipStream_t st) {
+    if constexpr (S == AFF8_G64) return pick_r<S, MT, LPR, 1>(p, c, s, b, N, K, x, M, y, st);
+    else if (p.v == 2) return pick_r<S, MT, LPR, 2>(p, c, s, b, N, K, x, M, y, st);
+    else return pick_r<S, MT, LPR, 1>(p, c, s, b, N, K, x, M, y, st);
+}
+
+template <int S, int MT>
+static hipError_t pick_lpr(const GemvPlan& p, const void* c, const void* s, const void* b,
+                           int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                           hipStream_t st) {
+    if constexpr (S == AFF8_G64) {
+        if (p.lpr == 64) return pick_v<S, MT, 64>(p, c, s, b, N, K, x, M, y, st);
+        return pick_v<S, MT, 16>(p, c, s, b, N, K, x, M, y, st);
+    } else {
+        switch (p.lpr) {
+            case 64: return pick_v<S, MT, 64>(p, c, s, b, N, K, x, M, y, st);
+            case 32: return pick_v<S, MT, 32>(p, c, s, b, N, K, x, M, y, st);
+            case 16: return pick_v<S, MT, 16>(p, c, s, b, N, K, x, M, y, st);
+            default: return pick_v<S, MT, 8>(p, c, s, b, N, K, x, M, y, st);
+        }
+    }
+}
+
+template <int S>
+static hipError_t pick_mt(const GemvPlan& p, const void* c, const void* s, const void* b,
+                          int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                          hipStream_t st) {
+    switch (p.mt) {
+        case 4: return pick_lpr<S, 4>(p, c, s, b, N, K, x, M, y, st);
+        case 2: return pick_lpr<S, 2>(p, c, s, b, N, K, x, M, y, st);
+        default: return pick_lpr<S, 1>(p, c, s, b, N, K, x, M, y, st);
+    }
+}
+
+hipError_t launch_gemv(int scheme, const void* codes, const void* scale, const void* bias,
+                       int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                       hipStream_t st) {
+    const GemvPlan p = plan_gemv(scheme, N, K, M);
+    switch (scheme) {
+        case SYM4_G128: return pick_mt<SYM4_G128>(p, codes, scale, bias, N, K, x, M, y, st);
+        case AFF4_G64: return pick_mt<AFF4_G64>(p, codes, scale, bias, N, K, x, M, y, st);
+        default: return pick_mt<AFF8_G64>(p, codes, scale, bias, N, K, x, M, y, st);
+    }
+}
+
+}  // namespace w4

@@ -1,0 +1,161 @@
+/*
+ * w4a16.h - group-wise 4-bit weight-only quantization with the dequantization
+ * fused into the matrix products, for AMD MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [airllm]          airllm article, cf-1.com/news/5708464: §2.1 (groups of 128
+ *                     consecutive weights), §2.2 (row-grouped layout; dequant fused
+ *                     into the matmul kernel, converted in registers right after the
+ *                     weight load), §3.3 (prefill compute-dense, decode memory-bound),
+ *                     §4.2 (group_quantize: scale = absmax/7, clamp_min 1e-8,
+ *                     round, clamp to +-7, two codes per byte, low nibble first).
+ *   [TurboFieldfare]  TurboFieldfare / Gemma 4 26B-A4B article,
+ *                     cnblogs.com/32bin/p/23195374: section 量化和精度 (affine
+ *                     4-bit, 64 weights per group, one bf16 scale and one bf16 bias
+ *                     per group; 8-bit router; codes used exactly as stored); the
+ *                     model section (128 routed experts, 8 per token, an always-on
+ *                     shared expert added without routing weight); the .gturbo
+ *                     layout (128 experts per layer at a fixed stride).
+ *
+ * Conventions shared by every entry point
+ *   - Weights W are [N][K] (output rows x input columns). Groups run along K inside
+ *     one row. K must be a multiple of the scheme's group size.
+ *   - 4-bit codes: uint8 [N][K/2]; byte j of a row holds element 2j in its low
+ *     nibble and element 2j+1 in its high nibble. Symmetric codes are two's
+ *     complement nibbles in [-7, 7]; affine codes are unsigned [0, 15].
+ *     8-bit codes: uint8 [N][K], one per byte, unsigned [0, 255].
+ *   - Scales: W4_SYM4_G128 -> fp32 [N][K/128]; affine -> bf16 [N][K/64] scale and
+ *     bf16 [N][K/64] bias. A weight is scale*q (sym) or scale*q + bias (affine).
+ *   - Activations are bf16 (raw uint16 bit patterns), row-major [M][K].
+ *   - Every pointer except those documented as host pointers is a DEVICE pointer.
+ *     The caller owns every buffer; the library never allocates, frees or keeps a
+ *     pointer after the call returns. Work is enqueued on `stream` (a hipStream_t
+ *     passed as void*, NULL = the default stream); no call synchronizes the device.
+ *   - Device pointers must be 16-byte aligned (W4_EALIGN otherwise).
+ *   - Arguments are validated on the host before anything is enqueued; on error
+ *     nothing is launched and the return value is negative. w4_last_error() gives
+ *     a message for the last failing call on the calling thread.
+ *   - M == 0 or N == 0 is a successful no-op. NaN/Inf inputs give unspecified
+ *     (but memory-safe) results.
+ *   - Results are deterministic: no floating-point atomics; a call repeated on the
+ *     same inputs returns the same bits.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---- */
+#define W4_OK          0
+#define W4_EINVAL     (-1) /* null pointer, unknown scheme or flag */
+#define W4_ESHAPE     (-2) /* K not a multiple of the group, sizes out of range */
+#define W4_EALIGN     (-3) /* a device pointer not 16-byte aligned */
+#define W4_EHIP       (-4) /* HIP runtime or launch error */
+#define W4_EWORKSPACE (-5) /* workspace missing or too small */
+
+/* ---- quantization schemes ---- */
+#define W4_SYM4_G128 0 /* symmetric 4-bit, group 128, fp32 scale = absmax/7 [airllm] §4.2 */
+#define W4_AFF4_G64  1 /* affine 4-bit, group 64, bf16 scale + bf16 bias [TurboFieldfare] 量化和精度 */
+#define W4_AFF8_G64  2 /* affine 8-bit, group 64, bf16 scale + bf16 bias (router) [TurboFieldfare] 量化和精度 */
+
+/*
+ * A quantized matrix, or a stack of `num_experts` matrices of identical shape
+ * stored back to back at a fixed stride ([TurboFieldfare]: 128 fixed-stride expert
+ * blobs per layer). All three arrays are [num_experts][N][...] as described above.
+ * `bias` is NULL for W4_SYM4_G128 and required otherwise.
+ */
+typedef struct w4_matrix {
+    int32_t scheme;      /* W4_SYM4_G128, W4_AFF4_G64 or W4_AFF8_G64 */
+    int32_t num_experts; /* >= 1 */
+    int64_t N;           /* rows per matrix (output features) */
+    int64_t K;           /* columns (input features) */
+    const void* codes;
+    const void* scale;
+    const void* bias;
+} w4_matrix;
+
+/*
+ * Host-only. Byte sizes of the three storage arrays of one N x K matrix.
+ * Any of the output pointers (host) may be NULL. Returns W4_EINVAL for an unknown
+ * scheme, W4_ESHAPE for N < 0, K < 0 or K not a multiple of the group.
+ */
+int w4_packed_sizes(int scheme, int64_t N, int64_t K,
+                    size_t* codes_bytes, size_t* scale_bytes, size_t* bias_bytes);
+
+/*
+ * quantize_pack. W: fp32 [N][K]. Writes codes/scale/bias in the storage form above.
+ * sym  ([airllm] §4.2): per group a = max|w|; s = max(a/7, 1e-8) in fp32;
+ *      q = clamp(rint(w/s), -7, 7) (round half to even).
+ * aff  ([TurboFieldfare] 量化和精度; the min/max rule is a reading):
+ *      s = bf16(max((max-min)/(2^b-1), 1e-8)), b = bf16(min) (round to nearest even);
+ *      q = clamp(rint((w-b)/s), 0, 2^b-1) using the stored bf16 values.
+ * All arithmetic is IEEE fp32 with correctly rounded division and no contraction,
+ * so the output is bit-identical to a host implementation of the same steps.
+ */
+int w4_quantize_pack(int scheme, const float* W, int64_t N, int64_t K,
+                     void* codes, void* scale, void* bias, void* stream);
+
+/*
+ * Decode GEMV / skinny GEMM with the dequantization fused into the product
+ * ([airllm] §2.2, §3.3): y[m][n] = sum_k x[m][k] * w[n][k] for m < M, n < N,
+ * accumulated in fp32. x: bf16 [M][K]; y: fp32 [M][N]. 1 <= M <= 64.
+ * W must be a single matrix (num_experts == 1).
+ */
+int w4a16_gemv(const w4_matrix* W, const uint16_t* x, int64_t M, float* y, void* stream);
+
+/*
+ * Prefill GEMM ([airllm] §3.3: prefill is compute-dense): Y = X * dequant(W)^T with
+ * bf16 inputs, fp32 accumulation and bf16 output (round to nearest even).
+ * X: bf16 [M][K]; Y: bf16 [M][N]; any M >= 0. W: single matrix, 4-bit scheme.
+ */
+int w4a16_gemm(const w4_matrix* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream);
+
+/*
+ * MoE router ([TurboFieldfare], model section and 量化和精度): logits = x * Wr^T
+ * (fp32 accumulate; Wr is [E][K], usually W4_AFF8_G64), then per token the top_k
+ * experts by logit, largest first, ties to the lower expert index, and their
+ * softmax probabilities over all E raw logits (no softcap, not renormalized).
+ * x: bf16 [M][K]. Outputs: ids int32 [M][top_k], weights fp32 [M][top_k], and
+ * optionally logits fp32 [M][E] (may be NULL). 1 <= top_k <= min(E, 32), E <= 1024.
+ */
+int w4_moe_route(const w4_matrix* router, const uint16_t* x, int64_t M, int top_k,
+                 float* logits, int32_t* ids, float* weights, void* stream);
+
+/*
+ * Host-only. Workspace bytes w4a16_moe_gemv needs for these sizes
+ * (E experts, d_model D, expert FFN width F, shared FFN width Fs, 0 = none).
+ */
+size_t w4_moe_workspace_bytes(int64_t M, int top_k, int64_t E, int64_t D, int64_t F, int64_t Fs);
+
+/*
+ * Mixture-of-experts FFN that reads only the selected experts
+ * ([TurboFieldfare]: 8 of 128 experts per token; shared expert added unweighted;
+ * shared and routed FFNs computed side by side):
+ *   y[m] = sum_j weights[m][j] * FFN_{ids[m][j]}(x[m])  +  FFN_shared(x[m])
+ *   FFN(x) = W_down * h,  h = bf16(gelu_tanh(W_gate x) * (W_up x))
+ * gate, up: stacks [E][F][D]; down: stack [E][D][F]. shared_gate/up: [Fs][D],
+ * shared_down: [D][Fs]; pass all three shared pointers NULL for no shared expert.
+ * All six matrices must use the same 4-bit scheme. ids/weights as produced by
+ * w4_moe_route (ids outside [0, E) give W4_EINVAL only if detected on the host;
+ * on the device they are skipped). x: bf16 [M][D]; y: fp32 [M][D].
+ * workspace: device memory of at least w4_moe_workspace_bytes(...) bytes.
+ */
+int w4a16_moe_gemv(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
+                   const w4_matrix* shared_gate, const w4_matrix* shared_up,
+                   const w4_matrix* shared_down,
+                   const uint16_t* x, int64_t M, const int32_t* ids, const float* weights,
+                   int top_k, void* workspace, size_t workspace_bytes, float* y, void* stream);
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+const char* w4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,76 @@
+"""Host-side checks of the C-ABI library (no GPU): it loads, exports every function
+include/w4a16.h declares, sizes storage like the oracle, and rejects bad arguments
+with the documented error codes before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_weight_only_quantize_amd as w4
+import oracle
+
+pytestmark = pytest.mark.cpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(w4[a-z0-9_]*)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"w4_quantize_pack", "w4a16_gemv", "w4a16_gemm", "w4a16_moe_gemv", "w4_moe_route",
+            "w4_packed_sizes", "w4_last_error", "w4_moe_workspace_bytes"} <= set(names)
+    L = ctypes.CDLL(w4.lib_path())
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@pytest.mark.parametrize("scheme", oracle.SCHEMES)
+@pytest.mark.parametrize("N,K", [(1, 128), (1024, 1024), (4096, 11008 if True else 0), (128, 2048)])
+def test_packed_sizes_match_oracle(scheme, N, K):
+    if K % oracle.GROUP[scheme]:
+        pytest.skip("shape not valid for scheme")
+    assert w4.packed_sizes(scheme, N, K) == oracle.packed_nbytes(scheme, N, K)
+
+
+def test_packed_sizes_rejects_bad_shapes():
+    with pytest.raises(w4.W4Error) as e:
+        w4.packed_sizes("sym4_g128", 4, 192)
+    assert e.value.code == -2
+    rc = w4.lib().w4_packed_sizes(7, 4, 128, None, None, None)
+    assert rc == -1
+
+
+def _desc(scheme=0, N=64, K=128, codes=16, scale=16, bias=16, E=1):
+    return w4._W4Matrix(scheme, E, N, K, codes, scale, bias)
+
+
+def test_gemv_argument_validation_without_a_device():
+    L = w4.lib()
+    d = _desc()
+    assert L.w4a16_gemv(ctypes.byref(d), 16, 0, 16, None) == 0            # M == 0: no-op
+    assert L.w4a16_gemv(ctypes.byref(_desc(N=0)), 16, 1, 16, None) == 0   # N == 0: no-op
+    assert L.w4a16_gemv(None, 16, 1, 16, None) == -1
+    assert L.w4a16_gemv(ctypes.byref(_desc(scheme=9)), 16, 1, 16, None) == -1
+    assert L.w4a16_gemv(ctypes.byref(_desc(K=192)), 16, 1, 16, None) == -2   # 192 % 128
+    assert b"multiple" in L.w4_last_error()
+    assert L.w4a16_gemv(ctypes.byref(_desc(scheme=1, bias=None)), 16, 1, 16, None) == -1
+    assert L.w4a16_gemv(ctypes.byref(_desc(codes=8)), 16, 1, 16, None) == -3
+    assert L.w4a16_gemv(ctypes.byref(d), 8, 1, 16, None) == -3
+    assert L.w4a16_gemv(ctypes.byref(d), 16, 65, 16, None) == -2
+    assert L.w4a16_gemv(ctypes.byref(d), None, 1, 16, None) == -1
+    assert L.w4a16_gemv(ctypes.byref(_desc(E=2)), 16, 1, 16, None) == -2
+
+
+def test_quantize_argument_validation_without_a_device():
+    L = w4.lib()
+    assert L.w4_quantize_pack(0, 16, 0, 128, 16, 16, None, None) == 0   # N == 0: no-op
+    assert L.w4_quantize_pack(0, 16, 4, 100, 16, 16, None, None) == -2
+    assert L.w4_quantize_pack(1, 16, 4, 64, 16, 16, None, None) == -1   # affine without bias
+    assert L.w4_quantize_pack(0, 24, 4, 128, 16, 16, None, None) == -3
+    assert L.w4_quantize_pack(5, 16, 4, 128, 16, 16, None, None) == -1

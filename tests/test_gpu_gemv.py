@@ -1,0 +1,124 @@
+"""GPU parity: the fused-dequant decode GEMV / skinny GEMM against the oracle's
+fp64 product, per element within 2e-3·sum|w||x| + 1e-5 (fp32 accumulation of
+bf16 activations), and bit-exact on dyadic toys where fp32 is exact."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_only_quantize_amd as w4
+import oracle
+import synth
+from gpu_util import dev_bf16, dev_f32, tolerance_ratio, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(scheme, N, K, M, name, rows=None, quantize_on_gpu=True):
+    print(f"[gemv] {name} scheme={scheme} N={N} K={K} M={M}", flush=True)
+    W = synth.weights(N, K, 0.02, seed=0, name=name)
+    x = synth.activations_bf16(M, K, seed=0, name=name + ".x")
+    c, s, b = oracle.quantize_pack(W, scheme)
+    q = w4.quantize_pack(dev_f32(W), scheme) if quantize_on_gpu else upload(c, s, b, scheme)
+    y = w4.gemv(q, dev_bf16(x)).cpu().numpy()
+    yr, S = oracle.gemv_reference(c, s, b, scheme, x, rows=rows)
+    if rows is not None:
+        y = y[:, rows]
+    r = tolerance_ratio(y, yr, S)
+    assert r <= 1.0, f"worst error is {r:.3f} x tolerance"
+    return r
+
+
+@pytest.mark.parametrize("scheme,N,K,M", [
+    ("aff4_g64", 1024, 1024, 1),      # single-GEMV workload
+    ("sym4_g128", 1000, 4096, 1),
+    ("sym4_g128", 1000, 4096, 2),
+    ("sym4_g128", 1000, 4096, 3),
+    ("sym4_g128", 1000, 4096, 5),
+    ("aff4_g64", 333, 768, 1),
+    ("aff4_g64", 333, 768, 4),
+    ("sym4_g128", 257, 11008, 1),
+    ("aff8_g64", 128, 2048, 1),
+    ("aff8_g64", 130, 2048, 7),
+    ("aff4_g64", 64, 64, 1),
+    ("aff4_g64", 7, 192, 2),
+    ("sym4_g128", 1, 128, 1),
+    ("aff4_g64", 520, 13824, 2),
+])
+def test_gemv_matches_oracle(scheme, N, K, M):
+    _run(scheme, N, K, M, f"small.{scheme}.{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("N,K,mat", [(4096, 4096, "wq"), (11008, 4096, "gate"), (4096, 11008, "down")])
+def test_gemv_llama7b_shapes(N, K, mat, M):
+    _run("sym4_g128", N, K, M, f"llama7b.{mat}")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+@pytest.mark.parametrize("N,K,mat", [(5120, 5120, "wq"), (13824, 5120, "gate"), (5120, 13824, "down")])
+def test_gemv_llama13b_shapes(N, K, mat, M):
+    _run("aff4_g64", N, K, M, f"llama13b.{mat}")
+
+
+def test_gemv_head_sampled_rows():
+    rows = np.sort(np.random.default_rng(0).choice(152064, 1536, replace=False))
+    _run("aff4_g64", 152064, 5120, 1, "llama13b.head", rows=rows)
+
+
+@pytest.mark.parametrize("scheme", ["aff4_g64", "sym4_g128", "aff8_g64"])
+def test_gemv_exact_on_dyadic_toy(scheme):
+    """8 x 64/128 toy with dyadic scales/biases and small-integer activations:
+    every partial sum is exactly representable, so the fp32 result is exact."""
+    rng = np.random.default_rng(21)
+    g = 128 if scheme == "sym4_g128" else 64
+    K, N = 2 * g, 8
+    if scheme == "sym4_g128":
+        q = rng.integers(-7, 8, size=(N, K))
+        s = np.array([2.0 ** -(2 + n % 3) for n in range(N)] * (K // g), np.float32).reshape(K // g, N).T.copy()
+        codes, sb, bb = oracle.pack(q, 4), s, None
+        sf, bf = s.astype(np.float64), None
+    else:
+        bits = 8 if scheme == "aff8_g64" else 4
+        q = rng.integers(0, 2 ** bits, size=(N, K))
+        sf = np.array([[2.0 ** -(3 + (n + j) % 3) for j in range(K // g)] for n in range(N)])
+        bf = np.array([[-(n + j + 1) * 2.0 ** -5 for j in range(K // g)] for n in range(N)])
+        sb = (sf.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        bb = (bf.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        codes = oracle.pack(q, bits)
+    xi = rng.integers(-3, 4, size=(2, K))
+    xb = (xi.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = w4.gemv(upload(codes, sb, bb, scheme), dev_bf16(xb)).cpu().numpy()
+    for m in range(2):
+        for n in range(N):
+            ex = Fraction(0)
+            for k in range(K):
+                w_ = Fraction(float(sf[n, k // g])) * int(q[n, k])
+                if bf is not None:
+                    w_ += Fraction(float(bf[n, k // g]))
+                ex += w_ * int(xi[m, k])
+            assert Fraction(float(y[m, n])) == ex, (m, n)
+
+
+def test_gemv_is_deterministic_and_noops():
+    W = synth.weights(2048, 4096, 0.02, seed=3, name="det")
+    q = w4.quantize_pack(dev_f32(W), "sym4_g128")
+    x = dev_bf16(synth.activations_bf16(3, 4096, seed=3, name="det.x"))
+    a = w4.gemv(q, x)
+    b = w4.gemv(q, x)
+    assert torch.equal(a, b)
+    y = torch.full((1, 2048), 7.0, device="cuda")
+    w4.gemv_into(q, x[:0], y)           # M == 0: nothing is written
+    torch.cuda.synchronize()
+    assert torch.equal(y, torch.full((1, 2048), 7.0, device="cuda"))
+
+
+def test_gemv_rejects_bad_arguments():
+    q = w4.quantize_pack(dev_f32(synth.weights(64, 256, 0.02, 4, "bad")), "aff4_g64")
+    x = dev_bf16(synth.activations_bf16(65, 256, 4, "bad.x"))
+    with pytest.raises(w4.W4Error):
+        w4.gemv(q, x)                    # M > 64
+    xs = torch.empty(257, dtype=torch.int16, device="cuda")[1:].view(1, 256)
+    with pytest.raises(w4.W4Error):
+        w4.gemv(q, xs)
