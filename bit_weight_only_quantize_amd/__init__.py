@@ -23,7 +23,7 @@ import torch
 
 __all__ = [
     "SCHEME_IDS", "W4Error", "QuantizedMatrix", "lib", "lib_path", "packed_sizes", "quantize_pack",
-    "empty_quantized", "gemv", "gemv_into", "gemm", "moe_route", "moe_workspace_bytes", "moe_gemv",
+    "empty_quantized", "gemv", "gemv_into", "gemv_multi", "gemv_multi_into", "gemm", "moe_route", "moe_workspace_bytes", "moe_gemv",
 ]
 
 SCHEME_IDS = {"sym4_g128": 0, "aff4_g64": 1, "aff8_g64": 2}
@@ -55,6 +55,8 @@ _SIGS = {
     "w4_quantize_pack": ([ctypes.c_int, _P, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "w4a16_gemv": ([ctypes.POINTER(_W4Matrix), _P, _I64, _P, _P], ctypes.c_int),
     "w4a16_gemm": ([ctypes.POINTER(_W4Matrix), _P, _I64, _P, _P], ctypes.c_int),
+    "w4a16_gemv_multi": ([ctypes.POINTER(ctypes.POINTER(_W4Matrix)), ctypes.c_int, _P, _I64,
+                          ctypes.POINTER(ctypes.c_void_p), _P], ctypes.c_int),
     "w4_moe_route": ([ctypes.POINTER(_W4Matrix), _P, _I64, ctypes.c_int, _P, _P, _P, _P], ctypes.c_int),
     "w4_moe_workspace_bytes": ([_I64, ctypes.c_int, _I64, _I64, _I64, _I64], ctypes.c_size_t),
     "w4a16_moe_gemv": ([ctypes.POINTER(_W4Matrix)] * 6 + [_P, _I64, _P, _P, ctypes.c_int, _P,
@@ -180,6 +182,24 @@ def gemv_into(W: QuantizedMatrix, x: torch.Tensor, y: torch.Tensor) -> torch.Ten
     d = W.desc()
     _check(lib().w4a16_gemv(ctypes.byref(d), _ptr(x), M, _ptr(y), _stream(x.device)))
     return y
+
+
+def gemv_multi_into(Ws, x: torch.Tensor, ys) -> list:
+    """Several GEMVs sharing x (one launch at M == 1): ys[i] = x · dequant(Ws[i])^T."""
+    x = _as_bf16_bits(x, "x")
+    M = x.shape[0] if x.dim() == 2 else 1
+    n = len(Ws)
+    descs = [W.desc() for W in Ws]
+    arr = (ctypes.POINTER(_W4Matrix) * n)(*[ctypes.pointer(d) for d in descs])
+    yp = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    _check(lib().w4a16_gemv_multi(arr, n, _ptr(x), M, yp, _stream(x.device)))
+    return ys
+
+
+def gemv_multi(Ws, x: torch.Tensor) -> list:
+    M = x.shape[0] if x.dim() == 2 else 1
+    ys = [torch.empty((M, W.N), dtype=torch.float32, device=x.device) for W in Ws]
+    return gemv_multi_into(Ws, x, ys)
 
 
 def gemv(W: QuantizedMatrix, x: torch.Tensor) -> torch.Tensor:

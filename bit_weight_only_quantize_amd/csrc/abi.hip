@@ -50,6 +50,7 @@ int check_matrix(const w4_matrix* W, const char* name, int experts) {
                     (long long)W->K, group_of(W->scheme));
     if (W->N > 0x7fffffffLL || W->K > 0x7fffffffLL)
         return fail(W4_ESHAPE, "%s: N and K must fit in 31 bits", name);
+    if (W->N == 0) return W4_OK;  // an empty matrix needs no storage
     if (!W->codes || !W->scale) return fail(W4_EINVAL, "%s: null codes or scale", name);
     if (W->scheme != W4_SYM4_G128 && !W->bias)
         return fail(W4_EINVAL, "%s: affine scheme needs a bias array", name);
@@ -106,6 +107,55 @@ int w4a16_gemv(const w4_matrix* W, const uint16_t* x, int64_t M, float* y, void*
     return hip_status(w4::launch_gemv(W->scheme, W->codes, W->scale, W->bias, W->N, W->K, x, M, y,
                                       (hipStream_t)stream),
                       "gemv launch");
+}
+
+int w4a16_gemv_multi(const w4_matrix* const* Ws, int count, const uint16_t* x, int64_t M,
+                     float* const* ys, void* stream) {
+    if (!Ws || !ys) return fail(W4_EINVAL, "null Ws or ys");
+    if (count < 1 || count > 4) return fail(W4_ESHAPE, "count=%d out of range [1, 4]", count);
+    for (int i = 0; i < count; ++i) {
+        char name[16];
+        snprintf(name, sizeof(name), "Ws[%d]", i);
+        int rc = check_matrix(Ws[i], name, 1);
+        if (rc) return rc;
+        if (Ws[i]->scheme != Ws[0]->scheme || Ws[i]->K != Ws[0]->K)
+            return fail(W4_ESHAPE, "Ws[%d]: scheme and K must match Ws[0]", i);
+        if (Ws[i]->N > 0 && (!ys[i] || !aligned16(ys[i])))
+            return fail(ys[i] ? W4_EALIGN : W4_EINVAL, "ys[%d] null or misaligned", i);
+    }
+    if (M < 0 || M > 64) return fail(W4_ESHAPE, "M=%lld out of range [0, 64]", (long long)M);
+    if (M == 0) return ok();
+    const int64_t K = Ws[0]->K;
+    if (K > w4::kMaxSkinnyK)
+        return fail(W4_ESHAPE, "K=%lld exceeds the GEMV limit %lld", (long long)K,
+                    (long long)w4::kMaxSkinnyK);
+    if (!x) return fail(W4_EINVAL, "null x");
+    if (!aligned16(x)) return fail(W4_EALIGN, "x must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    if (M == 1 && w4::gemv_wave_ok(Ws[0]->scheme, K)) {
+        const void* c[4];
+        const void* sc[4];
+        const void* b[4];
+        int64_t N[4];
+        float* y[4];
+        int n = 0;
+        for (int i = 0; i < count; ++i) {
+            if (Ws[i]->N == 0) continue;
+            c[n] = Ws[i]->codes; sc[n] = Ws[i]->scale; b[n] = Ws[i]->bias; N[n] = Ws[i]->N;
+            y[n] = ys[i];
+            ++n;
+        }
+        if (n == 0) return ok();
+        return hip_status(w4::launch_gemv_wave(Ws[0]->scheme, n, c, sc, b, N, K, x, y, st),
+                          "gemv_multi launch");
+    }
+    for (int i = 0; i < count; ++i) {
+        if (Ws[i]->N == 0) continue;
+        hipError_t e = w4::launch_gemv(Ws[i]->scheme, Ws[i]->codes, Ws[i]->scale, Ws[i]->bias,
+                                       Ws[i]->N, K, x, M, ys[i], st);
+        if (e != hipSuccess) return hip_status(e, "gemv_multi launch");
+    }
+    return ok();
 }
 
 int w4a16_gemm(const w4_matrix* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream) {

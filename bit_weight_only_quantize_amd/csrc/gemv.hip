@@ -7,6 +7,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "skinny.hpp"
+#include "gemv_wave.hpp"
 
 namespace w4 {
 
@@ -170,9 +171,92 @@ static hipError_t pick_mt(const GemvPlan& p, const void* c, const void* s, const
     }
 }
 
+// ---------------------------------------------------------------- M = 1, wave per row
+// Instantiated code-vector counts per lane (ceil(VR / 64) rounded up to one of these).
+static int wave_nv(int64_t VR) {
+    const int64_t need = (VR + 63) / 64;
+    const int nvs[] = {1, 2, 3, 4, 6, 7, 8};
+    for (int nv : nvs)
+        if (nv >= need) return nv;
+    return 0;
+}
+
+bool gemv_wave_ok(int scheme, int64_t K) {
+    const int kv = scheme == AFF8_G64 ? 16 : 32;
+    const int64_t VR = K / kv;
+    return VR >= 64 && wave_nv(VR) > 0;
+}
+
+template <int S, int NV, int R>
+static void go_wave(const GemvGroupArgs& a, int blocks, int K, const uint16_t* x, size_t lds,
+                    hipStream_t st) {
+    constexpr int SW = 2;                 // staging wavefronts per workgroup
+    constexpr int XV = (NV + 1) / 2;      // activation vectors per staging lane
+    hipLaunchKernelGGL((gemv_wave_kernel<S, NV, R, XV, SW>), dim3(blocks), dim3(256 + 64 * SW), lds,
+                       st, a, K, x);
+}
+
+template <int S, int R>
+static void pick_nv(int nv, const GemvGroupArgs& a, int blocks, int K, const uint16_t* x,
+                    size_t lds, hipStream_t st) {
+    switch (nv) {
+        case 1: go_wave<S, 1, R>(a, blocks, K, x, lds, st); break;
+        case 2: go_wave<S, 2, R>(a, blocks, K, x, lds, st); break;
+        case 3: go_wave<S, 3, R>(a, blocks, K, x, lds, st); break;
+        case 4: go_wave<S, 4, R>(a, blocks, K, x, lds, st); break;
+        case 6: go_wave<S, 6, R>(a, blocks, K, x, lds, st); break;
+        case 7: go_wave<S, 7, R>(a, blocks, K, x, lds, st); break;
+        default: go_wave<S, 8, R>(a, blocks, K, x, lds, st); break;
+    }
+}
+
+hipError_t launch_gemv_wave(int scheme, int count, const void* const* codes,
+                            const void* const* scale, const void* const* bias, const int64_t* N,
+                            int64_t K, const uint16_t* x, float* const* y, hipStream_t st) {
+    const int kv = scheme == AFF8_G64 ? 16 : 32;
+    const int64_t VR = K / kv;
+    const int nv = wave_nv(VR);
+    int64_t total_rows = 0;
+    for (int i = 0; i < count; ++i) total_rows += N[i];
+    // 4 rows per wavefront once there are enough rows to keep every CU busy
+    const int R = total_rows >= 8192 ? 4 : 2;
+    GemvGroupArgs a{};
+    int blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        a.codes[i] = (const uint8_t*)codes[i];
+        a.scale[i] = (const uint8_t*)scale[i];
+        a.bias[i] = (const uint8_t*)bias[i];
+        a.y[i] = y[i];
+        a.N[i] = (int)N[i];
+        a.tile_start[i] = blocks;
+        blocks += (int)((N[i] + 4 * R - 1) / (4 * R));
+    }
+    a.tile_start[count] = blocks;
+    a.count = count;
+    if (blocks == 0) return hipSuccess;
+    const size_t lds = (size_t)(K / 2 + VR) * 4;
+    switch (scheme) {
+        case SYM4_G128:
+            if (R == 4) pick_nv<SYM4_G128, 4>(nv, a, blocks, (int)K, x, lds, st);
+            else pick_nv<SYM4_G128, 2>(nv, a, blocks, (int)K, x, lds, st);
+            break;
+        case AFF4_G64:
+            if (R == 4) pick_nv<AFF4_G64, 4>(nv, a, blocks, (int)K, x, lds, st);
+            else pick_nv<AFF4_G64, 2>(nv, a, blocks, (int)K, x, lds, st);
+            break;
+        default:
+            if (R == 4) pick_nv<AFF8_G64, 4>(nv, a, blocks, (int)K, x, lds, st);
+            else pick_nv<AFF8_G64, 2>(nv, a, blocks, (int)K, x, lds, st);
+            break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv(int scheme, const void* codes, const void* scale, const void* bias,
                        int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                        hipStream_t st) {
+    if (M == 1 && gemv_wave_ok(scheme, K))
+        return launch_gemv_wave(scheme, 1, &codes, &scale, &bias, &N, K, x, &y, st);
     const GemvPlan p = plan_gemv(scheme, N, K, M);
     switch (scheme) {
         case SYM4_G128: return pick_mt<SYM4_G128>(p, codes, scale, bias, N, K, x, M, y, st);

@@ -1,0 +1,182 @@
+// Single-token decode GEMV, one wavefront per weight row (K >= 64 code vectors).
+//
+// Design for gfx950 (airllm article §2.2: dequantize in registers right after
+// the load; §3.3: decode is memory-bound):
+//   * a wavefront owns R whole rows, so row addresses are wave-uniform (SGPRs)
+//     and lane l reads 16-byte code vectors l, l+64, ... of each row: every load
+//     instruction moves 1 KiB of contiguous codes;
+//   * all code and scale loads of a lane are issued before anything else
+//     (single shot), so the whole matrix is in flight at once;
+//   * the activation vector is staged once per workgroup in LDS as bf16 pairs
+//     matching the unpack order, with per-vector sums for the offset removal,
+//     by dedicated staging wavefronts: vmcnt retires a wavefront's loads in
+//     order, so a row wavefront that also loaded activations would have to wait
+//     for all of its weight bytes before staging them. Row wavefronts issue only
+//     weight loads, meet the staging wavefronts at the barrier (no memory wait)
+//     and consume code vector j as soon as its own loads have retired;
+//   * one v_and_or_b32 (affine) or v_bitop3_b32 (sym: and + xor with 0x43084308,
+//     which also moves the two's-complement code to q + 8) turns a nibble pair
+//     into a bf16 pair (128 + u); v_dot2_f32_bf16 accumulates in fp32;
+//   * the 64-lane reduction is DPP only (quad perms, row mirrors, row_bcast15/31).
+// Several matrices that share the activation vector (Q/K/V, gate/up) can be
+// served by one launch: blocks are split among up to kMaxGroup matrices.
+#pragma once
+
+#include "common.hpp"
+#include "skinny.hpp"
+
+namespace w4 {
+
+constexpr int kMaxGroup = 4;
+
+struct GemvGroupArgs {
+    const uint8_t* codes[kMaxGroup];
+    const uint8_t* scale[kMaxGroup];
+    const uint8_t* bias[kMaxGroup];
+    float* y[kMaxGroup];
+    int N[kMaxGroup];
+    int tile_start[kMaxGroup + 1];  // first block of each matrix; tile_start[count] = grid
+    int count;
+};
+
+// Opaque VGPR copy of a constant: keeps the compiler from folding it into
+// literal operands (VOP3 encodings on gfx9 take no literals), so the unpack
+// stays one three-operand instruction per nibble pair.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+    return r;
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                 ROW_MASK, 0xF, false));
+}
+
+// Full 64-lane sum; lane 63 holds the total (DPP only, no LDS traffic).
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+    v += dpp_f<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f<0x141, 0xF>(v);  // row_half_mirror
+    v += dpp_f<0x140, 0xF>(v);  // row_mirror: every lane holds its 16-lane row sum
+    v += dpp_f<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+    v += dpp_f<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+    return v;
+}
+
+// Workgroup = 4 row wavefronts + SW staging wavefronts (see the file comment).
+template <int S, int NV, int R, int XV, int SW>
+__global__ __launch_bounds__(256 + 64 * SW) void gemv_wave_kernel(GemvGroupArgs a, int K,
+                                                                  const uint16_t* __restrict__ x) {
+    using T = Traits<S>;
+    using L = XLayout<S, 1>;
+    constexpr int XW = L::XW;
+    extern __shared__ __align__(16) uint32_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int VR = K / T::KV;
+
+    // which matrix of the group this block serves (uniform)
+    const int t = blockIdx.x;
+    int i = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxGroup; ++q)
+        if (q < a.count && t >= a.tile_start[q]) i = q;
+    const int N = a.N[i];
+    const int row0 = (t - a.tile_start[i]) * (4 * R) + wave * R;
+    const int64_t rowbytes = (int64_t)K * T::BITS / 8;
+    const int64_t groups = K / T::GROUP;
+    constexpr int SB = T::AFFINE ? 2 : 4;
+
+    uint32_t* xs = smem;
+    float* XS = reinterpret_cast<float*>(smem + K / 2);
+    if (wave >= 4) {
+        // staging wavefront(s): activations -> LDS, then done
+        XStage<S, XV, 64 * SW> xstage;
+        xstage.fetch(x, VR, threadIdx.x - 256);
+        xstage.commit(VR, xs, XS, threadIdx.x - 256);
+        __syncthreads();
+        return;
+    }
+
+    u32x4_t c[R][NV];
+    float sc[R][NV], bi[R][NV];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t n = row0 + r < N ? row0 + r : N - 1;
+        const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(a.codes[i] + n * rowbytes);
+        const uint8_t* sp = a.scale[i] + n * groups * SB;
+        const uint8_t* bp = T::AFFINE ? a.bias[i] + n * groups * 2 : nullptr;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            // unconditional (clamped) loads keep the wait counts exact; the
+            // duplicates past the row end are never used
+            const int v = min(lane + 64 * j, VR - 1);
+            c[r][j] = __builtin_nontemporal_load(cp + v);
+            const int g = v / T::VPG;
+            if constexpr (T::AFFINE) {
+                sc[r][j] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(sp)[g]);
+                bi[r][j] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(bp)[g]);
+            } else {
+                sc[r][j] = reinterpret_cast<const float*>(sp)[g];
+            }
+        }
+    }
+
+    __syncthreads();  // activations staged; weight loads still in flight
+
+    const uint32_t MASK = opaque(0x000F000Fu);
+    const uint32_t MAGIC = opaque(S == SYM4_G128 ? 0x43084308u : 0x43004300u);
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int v = lane + 64 * j;
+        if (v >= VR) break;
+        uint32_t xp[XW];
+#pragma unroll
+        for (int p = 0; p < XW / 4; ++p) {
+            const uint4 q = *reinterpret_cast<const uint4*>(xs + L::piece(v, p));
+            xp[4 * p] = q.x; xp[4 * p + 1] = q.y; xp[4 * p + 2] = q.z; xp[4 * p + 3] = q.w;
+        }
+        const float X = XS[v];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float D = 0.f, Dh = 0.f;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t w = c[r][j][d];
+                if constexpr (T::BITS == 4) {
+                    // sym: (nib & 0xF) ^ 0x..08 = 0x43 | (q + 8); affine: | 0x43 -> 128 + u
+                    auto pair = [&](uint32_t s) {
+                        return S == SYM4_G128 ? ((s & MASK) ^ MAGIC) : ((s & MASK) | MAGIC);
+                    };
+                    D = dot2_bf16(pair(w), xp[4 * d + 0], D);
+                    D = dot2_bf16(pair(w >> 4), xp[4 * d + 1], D);
+                    D = dot2_bf16(pair(w >> 8), xp[4 * d + 2], D);
+                    D = dot2_bf16(pair(w >> 12), xp[4 * d + 3], D);
+                } else {
+                    const uint32_t xa = xp[2 * d], xb = xp[2 * d + 1];
+                    D = dot2_bf16((w & MASK) | MAGIC, xa, D);
+                    D = dot2_bf16(((w >> 8) & MASK) | MAGIC, xb, D);
+                    Dh = dot2_bf16(((w >> 4) & MASK) | MAGIC, xa, Dh);
+                    Dh = dot2_bf16(((w >> 12) & MASK) | MAGIC, xb, Dh);
+                }
+            }
+            if constexpr (T::BITS == 8) D = fmaf(16.f, Dh, D);
+            const float s = sc[r][j];
+            const float corr = T::AFFINE ? fmaf(-T::BIAS, s, bi[r][j]) : -T::BIAS * s;
+            acc[r] = fmaf(s, D, acc[r]);
+            acc[r] = fmaf(corr, X, acc[r]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float tot = wave_sum_to_lane63(acc[r]);
+        if (lane == 63 && row0 + r < N) a.y[i][row0 + r] = tot;
+    }
+}
+
+}  // namespace w4

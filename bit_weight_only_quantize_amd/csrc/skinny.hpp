@@ -100,6 +100,64 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int64_t 
     }
 }
 
+// Staging of one token's activations by NT threads (thread index `tid`):
+// fetch(): up to XV vectors per thread into registers; commit(): pair
+// permutation (v_perm_b32), per-vector sums (v_dot2 with ones) and the LDS
+// writes. Same layout as stage_x with V = 1.
+template <int S, int XV, int NT>
+struct XStage {
+    using T = Traits<S>;
+    using L = XLayout<S, 1>;
+    static constexpr int Q = T::BITS == 4 ? 4 : 2;  // 16-byte activation loads per code vector
+    u32x4_t d[XV][Q];
+
+    // Loads are unconditional (index clamped into the row) so that no branch
+    // blurs the compiler's in-order wait counts; extra lanes re-read vector VR-1.
+    __device__ __forceinline__ void fetch(const uint16_t* __restrict__ x, int VR, int tid) {
+#pragma unroll
+        for (int t = 0; t < XV; ++t) {
+            const int v = min(tid + NT * t, VR - 1);
+            const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + (int64_t)v * T::KV);
+#pragma unroll
+            for (int q = 0; q < Q; ++q) d[t][q] = src[q];
+        }
+    }
+
+    __device__ __forceinline__ void commit(int VR, uint32_t* __restrict__ xs, float* __restrict__ XS,
+                                           int tid) const {
+        constexpr uint32_t ONES = 0x3F803F80u;  // bf16 pair (1, 1)
+#pragma unroll
+        for (int t = 0; t < XV; ++t) {
+            const int v = tid + NT * t;
+            if (v < VR) {
+                float sum = 0.f;
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const u32x4_t e = d[t][q];
+                    uint4 o;
+                    if constexpr (T::BITS == 4) {  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+                        o.x = __builtin_amdgcn_perm(e[2], e[0], 0x05040100u);
+                        o.y = __builtin_amdgcn_perm(e[2], e[0], 0x07060302u);
+                        o.z = __builtin_amdgcn_perm(e[3], e[1], 0x05040100u);
+                        o.w = __builtin_amdgcn_perm(e[3], e[1], 0x07060302u);
+                    } else {                       // (x0,x2) (x1,x3) (x4,x6) (x5,x7)
+                        o.x = __builtin_amdgcn_perm(e[1], e[0], 0x05040100u);
+                        o.y = __builtin_amdgcn_perm(e[1], e[0], 0x07060302u);
+                        o.z = __builtin_amdgcn_perm(e[3], e[2], 0x05040100u);
+                        o.w = __builtin_amdgcn_perm(e[3], e[2], 0x07060302u);
+                    }
+                    *reinterpret_cast<uint4*>(xs + L::piece(v, q)) = o;
+                    sum = dot2_bf16(ONES, e[0], sum);
+                    sum = dot2_bf16(ONES, e[1], sum);
+                    sum = dot2_bf16(ONES, e[2], sum);
+                    sum = dot2_bf16(ONES, e[3], sum);
+                }
+                XS[v] = sum;
+            }
+        }
+    }
+};
+
 // One lane's share of R weight rows against MT staged tokens.
 template <int S, int MT, int LPR, int V, int R>
 struct SkinnyCore {

@@ -109,6 +109,18 @@ int w4_quantize_pack(int scheme, const float* W, int64_t N, int64_t K,
 int w4a16_gemv(const w4_matrix* W, const uint16_t* x, int64_t M, float* y, void* stream);
 
 /*
+ * Several decode GEMVs that share one activation input x, served by a single
+ * launch when M == 1 (the Q, K and V projections of a layer, or its gate and up
+ * projections). [airllm] §3.1 fuses operators to cut kernel launches;
+ * [TurboFieldfare] runs the projections that share an input side by side.
+ * Ws: host array of `count` descriptors (1 <= count <= 4), all single matrices
+ * with the same scheme and K; ys: host array of device pointers, ys[i] fp32
+ * [M][Ws[i]->N]. Results are identical to `count` separate w4a16_gemv calls.
+ */
+int w4a16_gemv_multi(const w4_matrix* const* Ws, int count, const uint16_t* x, int64_t M,
+                     float* const* ys, void* stream);
+
+/*
  * Prefill GEMM ([airllm] §3.3: prefill is compute-dense): Y = X * dequant(W)^T with
  * bf16 inputs, fp32 accumulation and bf16 output (round to nearest even).
  * X: bf16 [M][K]; Y: bf16 [M][N]; any M >= 0. W: single matrix, 4-bit scheme.

@@ -122,3 +122,30 @@ def test_gemv_rejects_bad_arguments():
     xs = torch.empty(257, dtype=torch.int16, device="cuda")[1:].view(1, 256)
     with pytest.raises(w4.W4Error):
         w4.gemv(q, xs)
+
+
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("scheme,K,Ns", [
+    ("sym4_g128", 4096, [1000, 1000, 1000]),      # Q/K/V-like
+    ("sym4_g128", 4096, [700, 0, 333]),           # an empty member
+    ("aff4_g64", 5120, [1300, 1300]),             # gate/up-like
+    ("aff4_g64", 2048, [768, 768, 2048, 5]),      # four members, ragged
+])
+def test_gemv_multi_matches_oracle_and_separate_calls(scheme, K, Ns, M):
+    print(f"[gemv_multi] {scheme} K={K} Ns={Ns} M={M}", flush=True)
+    x = synth.activations_bf16(M, K, seed=1, name=f"multi.x.{K}")
+    xd = dev_bf16(x)
+    qs, refs = [], []
+    for i, N in enumerate(Ns):
+        W = synth.weights(max(N, 1), K, 0.02, seed=1, name=f"multi.{scheme}.{i}")[:N]
+        c, s, b = oracle.quantize_pack(np.ascontiguousarray(W), scheme)
+        qs.append(w4.quantize_pack(dev_f32(W), scheme) if N else
+                  w4.empty_quantized(scheme, 0, K))
+        refs.append(oracle.gemv_reference(c, s, b, scheme, x) if N else None)
+    ys = w4.gemv_multi(qs, xd)
+    for q, y, ref in zip(qs, ys, refs):
+        if ref is None:
+            assert y.shape[1] == 0
+            continue
+        assert tolerance_ratio(y.cpu().numpy(), *ref) <= 1.0
+        assert torch.equal(y, w4.gemv(q, xd))       # one launch == separate launches, bit for bit
