@@ -79,25 +79,27 @@ def _expert(stack, e):
 
 def moe_sparse(x_bf16, ids, p, gate_stack, up_stack, down_stack, shared=None,
                scheme: str = "aff4_g64"):
-    """y[m] = sum_j p[m][j] * FFN_{ids[m][j]}(x[m]) + FFN_shared(x[m]), only the
-    selected experts evaluated. Returns (y fp64 [M][D], S fp64 [M][D])."""
+    """y[m] = sum_j p[m][j] * FFN_{ids[m][j]}(x[m]) + FFN_shared(x[m]), evaluating only
+    the selected experts (each selected expert once, for all of its (token, slot)
+    pairs; ids outside [0, E) contribute nothing). Returns (y fp64 [M][D], S fp64 [M][D])."""
     x_bf16 = np.atleast_2d(x_bf16)
     M = x_bf16.shape[0]
+    E = gate_stack[0].shape[0]
     D = gate_stack[0].shape[2] * (2 if scheme != "aff8_g64" else 1)
     y = np.zeros((M, D), dtype=np.float64)
     S = np.zeros((M, D), dtype=np.float64)
-    for m in range(M):
-        xm = x_bf16[m:m + 1]
-        for j in range(ids.shape[1]):
-            e = int(ids[m, j])
-            ye, Se, _ = ffn(xm, _expert(gate_stack, e), _expert(up_stack, e),
-                            _expert(down_stack, e), scheme)
-            y[m] += p[m, j] * ye[0]
-            S[m] += p[m, j] * Se[0]
-        if shared is not None:
-            ys, Ss, _ = ffn(xm, shared[0], shared[1], shared[2], scheme)
-            y[m] += ys[0]
-            S[m] += Ss[0]
+    for e in sorted({int(v) for v in np.asarray(ids).ravel() if 0 <= int(v) < E}):
+        sel = [(m, j) for m in range(M) for j in range(ids.shape[1]) if int(ids[m, j]) == e]
+        rows = x_bf16[[m for m, _ in sel]]
+        ye, Se, _ = ffn(rows, _expert(gate_stack, e), _expert(up_stack, e),
+                        _expert(down_stack, e), scheme)
+        for r, (m, j) in enumerate(sel):
+            y[m] += p[m, j] * ye[r]
+            S[m] += p[m, j] * Se[r]
+    if shared is not None:
+        ys, Ss, _ = ffn(x_bf16, shared[0], shared[1], shared[2], scheme)
+        y += ys
+        S += Ss
     return y, S
 
 
