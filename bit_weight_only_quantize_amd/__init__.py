@@ -220,13 +220,13 @@ def gemm(W: QuantizedMatrix, X: torch.Tensor, Y: Optional[torch.Tensor] = None) 
     return Y
 
 
-def moe_route(router: QuantizedMatrix, x: torch.Tensor, top_k: int = 8, want_logits: bool = False):
-    """(ids int32 [M][k], weights fp32 [M][k], logits fp32 [M][E] or None)."""
+def moe_route(router: QuantizedMatrix, x: torch.Tensor, top_k: int = 8):
+    """Router: (ids int32 [M][k], weights fp32 [M][k], logits fp32 [M][E])."""
     x = _as_bf16_bits(x, "x")
     M = x.shape[0]
     ids = torch.empty((M, top_k), dtype=torch.int32, device=x.device)
     w = torch.empty((M, top_k), dtype=torch.float32, device=x.device)
-    logits = torch.empty((M, router.N), dtype=torch.float32, device=x.device) if want_logits else None
+    logits = torch.empty((M, router.N), dtype=torch.float32, device=x.device)
     d = router.desc()
     _check(lib().w4_moe_route(ctypes.byref(d), _ptr(x), M, top_k, _ptr(logits), _ptr(ids), _ptr(w),
                               _stream(x.device)))

@@ -165,13 +165,29 @@ int w4a16_gemm(const w4_matrix* W, const uint16_t* X, int64_t M, uint16_t* Y, vo
 
 int w4_moe_route(const w4_matrix* router, const uint16_t* x, int64_t M, int top_k, float* logits,
                  int32_t* ids, float* weights, void* stream) {
-    (void)router; (void)x; (void)M; (void)top_k; (void)logits; (void)ids; (void)weights; (void)stream;
-    return fail(W4_EINVAL, "w4_moe_route: not built yet");
+    int rc = check_matrix(router, "router", 1);
+    if (rc) return rc;
+    const int64_t E = router->N;
+    if (E < 1 || E > 1024) return fail(W4_ESHAPE, "router: E=%lld out of range [1, 1024]", (long long)E);
+    if (top_k < 1 || top_k > 32 || top_k > E)
+        return fail(W4_ESHAPE, "top_k=%d out of range [1, min(E, 32)]", top_k);
+    if (M < 0 || M > 4096) return fail(W4_ESHAPE, "M=%lld out of range [0, 4096]", (long long)M);
+    if (M == 0) return ok();
+    if (router->K > w4::kMaxSkinnyK)
+        return fail(W4_ESHAPE, "router K=%lld exceeds %lld", (long long)router->K,
+                    (long long)w4::kMaxSkinnyK);
+    if (!x || !logits || !ids || !weights) return fail(W4_EINVAL, "null x, logits, ids or weights");
+    if (!aligned16(x) || !aligned16(logits) || !aligned16(ids) || !aligned16(weights))
+        return fail(W4_EALIGN, "x, logits, ids and weights must be 16-byte aligned");
+    return hip_status(w4::launch_route(router->scheme, router->codes, router->scale, router->bias, E,
+                                       router->K, x, M, top_k, logits, ids, weights,
+                                       (hipStream_t)stream),
+                      "moe_route launch");
 }
 
 size_t w4_moe_workspace_bytes(int64_t M, int top_k, int64_t E, int64_t D, int64_t F, int64_t Fs) {
-    (void)M; (void)top_k; (void)E; (void)D; (void)F; (void)Fs;
-    return 0;
+    if (M < 0 || top_k < 0 || E < 0 || D < 0 || F < 0 || Fs < 0) return 0;
+    return w4::moe_workspace_layout(M, top_k, E, D, F, Fs).total;
 }
 
 int w4a16_moe_gemv(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
@@ -179,10 +195,64 @@ int w4a16_moe_gemv(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* 
                    const w4_matrix* shared_down, const uint16_t* x, int64_t M,
                    const int32_t* ids, const float* weights, int top_k, void* workspace,
                    size_t workspace_bytes, float* y, void* stream) {
-    (void)gate; (void)up; (void)down; (void)shared_gate; (void)shared_up; (void)shared_down;
-    (void)x; (void)M; (void)ids; (void)weights; (void)top_k; (void)workspace;
-    (void)workspace_bytes; (void)y; (void)stream;
-    return fail(W4_EINVAL, "w4a16_moe_gemv: not built yet");
+    int rc;
+    if ((rc = check_matrix(gate, "gate", 0)) || (rc = check_matrix(up, "up", 0)) ||
+        (rc = check_matrix(down, "down", 0)))
+        return rc;
+    const int scheme = gate->scheme;
+    if (scheme == W4_AFF8_G64) return fail(W4_EINVAL, "experts must use a 4-bit scheme");
+    const int64_t E = gate->num_experts, F = gate->N, D = gate->K;
+    if (up->scheme != scheme || down->scheme != scheme)
+        return fail(W4_EINVAL, "gate, up and down must share one scheme");
+    if (up->num_experts != E || down->num_experts != E)
+        return fail(W4_ESHAPE, "gate, up and down must have the same number of experts");
+    if (up->N != F || up->K != D || down->N != D || down->K != F)
+        return fail(W4_ESHAPE, "expected gate/up [E][F][D] and down [E][D][F]");
+    if (E > 1024) return fail(W4_ESHAPE, "E=%lld exceeds 1024", (long long)E);
+    const bool any_shared = shared_gate || shared_up || shared_down;
+    const bool all_shared = shared_gate && shared_up && shared_down;
+    if (any_shared && !all_shared) return fail(W4_EINVAL, "pass all three shared matrices or none");
+    int64_t Fs = 0;
+    if (all_shared) {
+        if ((rc = check_matrix(shared_gate, "shared_gate", 1)) ||
+            (rc = check_matrix(shared_up, "shared_up", 1)) ||
+            (rc = check_matrix(shared_down, "shared_down", 1)))
+            return rc;
+        Fs = shared_gate->N;
+        if (shared_gate->scheme != scheme || shared_up->scheme != scheme ||
+            shared_down->scheme != scheme)
+            return fail(W4_EINVAL, "shared expert must use the experts' scheme");
+        if (shared_gate->K != D || shared_up->K != D || shared_up->N != Fs ||
+            shared_down->N != D || shared_down->K != Fs || Fs < 1)
+            return fail(W4_ESHAPE, "expected shared gate/up [Fs][D] and down [D][Fs]");
+    }
+    if (top_k < 1 || top_k > 32) return fail(W4_ESHAPE, "top_k=%d out of range [1, 32]", top_k);
+    if (M < 0 || M > 256) return fail(W4_ESHAPE, "M=%lld out of range [0, 256]", (long long)M);
+    if (M == 0 || D == 0) return ok();
+    if (F < 1) return fail(W4_ESHAPE, "F must be positive");
+    if (D > w4::kMaxSkinnyK / 4 || F > w4::kMaxSkinnyK / 4 || Fs > w4::kMaxSkinnyK / 4)
+        return fail(W4_ESHAPE, "D, F and Fs must not exceed %lld", (long long)(w4::kMaxSkinnyK / 4));
+    if (!x || !ids || !weights || !y || !workspace)
+        return fail(W4_EINVAL, "null x, ids, weights, y or workspace");
+    if (!aligned16(x) || !aligned16(ids) || !aligned16(weights) || !aligned16(y) ||
+        !aligned16(workspace))
+        return fail(W4_EALIGN, "x, ids, weights, y and workspace must be 16-byte aligned");
+    const size_t need = w4::moe_workspace_layout(M, top_k, E, D, F, Fs).total;
+    if (workspace_bytes < need)
+        return fail(W4_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    w4::MoeMats W{};
+    W.E = E; W.D = D; W.F = F; W.Fs = Fs;
+    const w4_matrix* mats[6] = {gate, up, down, shared_gate, shared_up, shared_down};
+    const void** dst[6] = {W.gate, W.up, W.down, W.sgate, W.sup, W.sdown};
+    for (int i = 0; i < 6; ++i) {
+        if (!mats[i]) continue;
+        dst[i][0] = mats[i]->codes;
+        dst[i][1] = mats[i]->scale;
+        dst[i][2] = mats[i]->bias;
+    }
+    return hip_status(w4::launch_moe(scheme, W, x, M, ids, weights, top_k, workspace, y,
+                                     (hipStream_t)stream),
+                      "moe_gemv launch");
 }
 
 }  // extern "C"

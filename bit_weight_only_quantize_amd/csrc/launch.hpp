@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace w4 {
@@ -28,5 +29,27 @@ hipError_t launch_gemv_wave(int scheme, int count, const void* const* codes,
 hipError_t launch_gemv(int scheme, const void* codes, const void* scale, const void* bias,
                        int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                        hipStream_t st);
+
+// ---- mixture of experts
+struct MoeMats {
+    int64_t E, D, F, Fs;  // experts, d_model, expert FFN width, shared FFN width (0 = none)
+    const void* gate[3];  // codes, scale, bias of the stacked matrices
+    const void* up[3];
+    const void* down[3];
+    const void* sgate[3];
+    const void* sup[3];
+    const void* sdown[3];
+};
+
+struct MoeWorkspace {  // byte offsets inside the caller's workspace
+    size_t offsets, active, n_active, pairs, h, hs, part, sout, total;
+};
+MoeWorkspace moe_workspace_layout(int64_t M, int k, int64_t E, int64_t D, int64_t F, int64_t Fs);
+
+hipError_t launch_route(int scheme, const void* codes, const void* scale, const void* bias,
+                        int64_t E, int64_t K, const uint16_t* x, int64_t M, int k, float* logits,
+                        int32_t* ids, float* wts, hipStream_t st);
+hipError_t launch_moe(int scheme, const MoeMats& W, const uint16_t* x, int64_t M, const int32_t* ids,
+                      const float* wts, int k, void* ws, float* y, hipStream_t st);
 
 }  // namespace w4

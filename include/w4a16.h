@@ -132,8 +132,8 @@ int w4a16_gemm(const w4_matrix* W, const uint16_t* X, int64_t M, uint16_t* Y, vo
  * (fp32 accumulate; Wr is [E][K], usually W4_AFF8_G64), then per token the top_k
  * experts by logit, largest first, ties to the lower expert index, and their
  * softmax probabilities over all E raw logits (no softcap, not renormalized).
- * x: bf16 [M][K]. Outputs: ids int32 [M][top_k], weights fp32 [M][top_k], and
- * optionally logits fp32 [M][E] (may be NULL). 1 <= top_k <= min(E, 32), E <= 1024.
+ * x: bf16 [M][K]. Outputs: logits fp32 [M][E], ids int32 [M][top_k] and weights
+ * fp32 [M][top_k] (all required). 1 <= top_k <= min(E, 32), E <= 1024.
  */
 int w4_moe_route(const w4_matrix* router, const uint16_t* x, int64_t M, int top_k,
                  float* logits, int32_t* ids, float* weights, void* stream);
@@ -152,10 +152,12 @@ size_t w4_moe_workspace_bytes(int64_t M, int top_k, int64_t E, int64_t D, int64_
  *   FFN(x) = W_down * h,  h = bf16(gelu_tanh(W_gate x) * (W_up x))
  * gate, up: stacks [E][F][D]; down: stack [E][D][F]. shared_gate/up: [Fs][D],
  * shared_down: [D][Fs]; pass all three shared pointers NULL for no shared expert.
- * All six matrices must use the same 4-bit scheme. ids/weights as produced by
- * w4_moe_route (ids outside [0, E) give W4_EINVAL only if detected on the host;
- * on the device they are skipped). x: bf16 [M][D]; y: fp32 [M][D].
- * workspace: device memory of at least w4_moe_workspace_bytes(...) bytes.
+ * All six matrices must use the same 4-bit scheme, with D, F, Fs multiples of its
+ * group. ids/weights as produced by w4_moe_route; a slot whose id lies outside
+ * [0, E) contributes nothing. 1 <= M <= 256, 1 <= top_k <= 32, E <= 1024.
+ * x: bf16 [M][D]; y: fp32 [M][D]. workspace: device memory of at least
+ * w4_moe_workspace_bytes(...) bytes (W4_EWORKSPACE otherwise); its contents on
+ * entry do not matter and on return are unspecified.
  */
 int w4a16_moe_gemv(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
                    const w4_matrix* shared_gate, const w4_matrix* shared_up,
