@@ -159,8 +159,16 @@ int w4a16_gemv_multi(const w4_matrix* const* Ws, int count, const uint16_t* x, i
 }
 
 int w4a16_gemm(const w4_matrix* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream) {
-    (void)W; (void)X; (void)M; (void)Y; (void)stream;
-    return fail(W4_EINVAL, "w4a16_gemm: not built yet");
+    int rc = check_matrix(W, "W", 1);
+    if (rc) return rc;
+    if (W->scheme == W4_AFF8_G64) return fail(W4_EINVAL, "w4a16_gemm takes a 4-bit scheme");
+    if (M < 0 || M > 0x7fffffffLL) return fail(W4_ESHAPE, "M=%lld out of range", (long long)M);
+    if (M == 0 || W->N == 0) return ok();
+    if (!X || !Y) return fail(W4_EINVAL, "null X or Y");
+    if (!aligned16(X) || !aligned16(Y)) return fail(W4_EALIGN, "X and Y must be 16-byte aligned");
+    return hip_status(w4::launch_gemm(W->scheme, W->codes, W->scale, W->bias, W->N, W->K, X, M, Y,
+                                      (hipStream_t)stream),
+                      "gemm launch");
 }
 
 int w4_moe_route(const w4_matrix* router, const uint16_t* x, int64_t M, int top_k, float* logits,

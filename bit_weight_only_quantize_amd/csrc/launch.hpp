@@ -30,6 +30,11 @@ hipError_t launch_gemv(int scheme, const void* codes, const void* scale, const v
                        int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                        hipStream_t st);
 
+// ---- prefill GEMM (4-bit schemes), bf16 out
+hipError_t launch_gemm(int scheme, const void* codes, const void* scale, const void* bias,
+                       int64_t N, int64_t K, const uint16_t* X, int64_t M, uint16_t* Y,
+                       hipStream_t st);
+
 // ---- mixture of experts
 struct MoeMats {
     int64_t E, D, F, Fs;  // experts, d_model, expert FFN width, shared FFN width (0 = none)
