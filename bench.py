@@ -1,16 +1,21 @@
 #!/usr/bin/env python3
-"""Decode benchmark: a Llama-7B-shaped W4A16 layer stack on one MI355X.
+"""Benchmarks of the W4A16 hot path on one MI355X.
 
-One step = one decode pass of M tokens through 32 distinct layers, each with the
-seven projections Wq, Wk, Wv, Wo (4096x4096), gate, up (11008x4096) and down
-(4096x11008), quantized symmetric INT4 with 128-weight groups (scale = absmax/7),
-every product a fused-dequant GEMV in the HIP library. Weights are drawn on the
-device (seeded N(0, 0.02)) and quantized with the library's quantize_pack; the
-whole step is captured once in a HIP graph and replayed.
+Default workload (the one the headline metric is quoted on): a Llama-7B-shaped
+decode layer stack. One step = one decode pass of M tokens (default 1) through
+32 distinct layers, each with the projections Wq, Wk, Wv, Wo (4096x4096), gate,
+up (11008x4096) and down (4096x11008), symmetric INT4 with 128-weight groups
+(scale = absmax/7). Per layer the launches a decode layer's data dependencies
+allow: Q/K/V in one launch (shared input), O, gate+up in one launch, down.
 
-Prints one JSON line: HBM throughput of the step (algorithmic bytes / time),
-decode tokens/s, the dominant kernel's roofline (timed live with HIP events on
-its own stream) and the CPU oracle timed on a bounded sample.
+Other workloads (--workload): moe26b (Gemma-4-26B-A4B-shaped MoE FFN stack),
+prefill (the two prefill GEMMs), llama13b (13B-shaped stack + tied head),
+gemv1024 (the single 1024x1024 GEMV, cache-hot and cold).
+
+Weights are seeded N(0, 0.02) drawn on the device and quantized with the
+library's quantize_pack; activations are seeded bf16 N(0, 1). Every step is
+captured once in a HIP graph and replayed; times come from HIP events on the
+stream the kernels run on. Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -25,20 +30,27 @@ sys.path.insert(0, ROOT)
 
 METRIC = "W4A16 decode GEMV achieved HBM TB/s (% of peak); 7B-layer decode tok/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 LLAMA7B = [("wq", 4096, 4096), ("wk", 4096, 4096), ("wv", 4096, 4096), ("wo", 4096, 4096),
            ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008)]
-SCHEME = "sym4_g128"
+LLAMA13B = [("wq", 5120, 5120), ("wk", 5120, 5120), ("wv", 5120, 5120), ("wo", 5120, 5120),
+            ("gate", 13824, 5120), ("up", 13824, 5120), ("down", 5120, 13824)]
 
 
-def matrix_bytes(N: int, K: int, M: int) -> int:
-    """Algorithmic HBM bytes of one sym4_g128 GEMV: codes + fp32 scales + x in + y out."""
-    return N * K // 2 + N * (K // 128) * 4 + M * K * 2 + M * N * 4
+def weight_bytes(scheme: str, N: int, K: int) -> int:
+    """Stored bytes of one quantized N x K matrix (codes + scales + biases)."""
+    if scheme == "sym4_g128":
+        return N * K // 2 + N * (K // 128) * 4
+    if scheme == "aff4_g64":
+        return N * K // 2 + N * (K // 64) * 4
+    return N * K + N * (K // 64) * 4
 
 
-def group_bytes(shapes, M: int) -> int:
-    """Algorithmic bytes of one launch serving several matrices that share x (x read once)."""
+def gemv_bytes(scheme: str, shapes, M: int) -> int:
+    """Algorithmic HBM bytes of one launch serving matrices that share x: weights,
+    x once, every y."""
     K = shapes[0][1]
-    return sum(matrix_bytes(N, K, M) for N, K in shapes) - (len(shapes) - 1) * M * K * 2
+    return sum(weight_bytes(scheme, N, K) + M * N * 4 for N, _ in shapes) + M * K * 2
 
 
 def parse():
@@ -46,8 +58,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--M", type=int, default=1, help="decode tokens per step (1..16)")
-    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--workload", default="llama7b",
+                    choices=["llama7b", "moe26b", "prefill", "llama13b", "gemv1024"])
+    ap.add_argument("--M", type=int, default=None, help="decode tokens per step")
+    ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU oracle time budget")
     ap.add_argument("--dominant-only", action="store_true",
@@ -55,9 +69,111 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(layer, xs_host, M, budget_s):
+# ---------------------------------------------------------------- helpers
+class Ctx:
+    def __init__(self, a):
+        import numpy as np
+        import torch
+
+        import bit_weight_only_quantize_amd as w4
+        import synth
+
+        self.np, self.torch, self.w4, self.synth, self.a = np, torch, w4, synth, a
+        self.dev = torch.device("cuda:0")
+        torch.cuda.set_device(self.dev)
+
+    def quant(self, N, K, scheme, name, out=None, expert=None):
+        W = self.synth.device_weights(N, K, 0.02, 0, name, self.dev)
+        q = self.w4.quantize_pack(W, scheme, out=out, expert=expert)
+        del W
+        return q
+
+    def x(self, M, K, name):
+        host = self.synth.activations_bf16(M, K, 0, name)
+        return host, self.torch.from_numpy(host.view(self.np.int16)).to(self.dev).view(self.torch.bfloat16)
+
+    def graph(self, fn):
+        torch = self.torch
+        side = torch.cuda.Stream(self.dev)
+        side.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream(self.dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    def time_graph(self, g, reps, warmup):
+        """ms per replay, HIP events on the stream the graph replays on."""
+        torch = self.torch
+        stream = torch.cuda.current_stream(self.dev)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+
+def base_line(a, metric, value, unit, ms, config, dtype="bf16"):
+    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps,
+            "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+            "config": config}
+
+
+def hbm_roofline(kernel, nbytes, us):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "bytes_per_launch": nbytes, "avg_launch_us": round(us, 3)}
+
+
+# ---------------------------------------------------------------- dense decode stacks
+def decode_stack(c: Ctx, shapes, scheme, layers, M, head=None):
+    """Build `layers` distinct layers (and an optional head) and return the step
+    and dominant-kernel closures plus byte counts."""
+    w4 = c.w4
+    mats = []
+    for l in range(layers):
+        mats.append({nm: c.quant(N, K, scheme, f"{scheme}.L{l}.{nm}") for nm, N, K in shapes})
+    hq = c.quant(head[0], head[1], scheme, f"{scheme}.head") if head else None
+    c.torch.cuda.synchronize()
+    d = shapes[0][2]
+    f = shapes[4][1]
+    xh = {K: c.x(M, K, f"{scheme}.x{K}") for K in (d, f)}
+    xs = {K: v[1] for K, v in xh.items()}
+    ys = {nm: c.torch.empty((M, N), dtype=c.torch.float32, device=c.dev) for nm, N, _ in shapes}
+    yh = c.torch.empty((M, head[0]), dtype=c.torch.float32, device=c.dev) if head else None
+
+    def step():
+        for m in mats:
+            w4.gemv_multi_into([m["wq"], m["wk"], m["wv"]], xs[d], [ys["wq"], ys["wk"], ys["wv"]])
+            w4.gemv_into(m["wo"], xs[d], ys["wo"])
+            w4.gemv_multi_into([m["gate"], m["up"]], xs[d], [ys["gate"], ys["up"]])
+            w4.gemv_into(m["down"], xs[f], ys["down"])
+        if hq is not None:
+            w4.gemv_into(hq, xs[d], yh)
+
+    def dominant():
+        for m in mats:
+            w4.gemv_multi_into([m["gate"], m["up"]], xs[d], [ys["gate"], ys["up"]])
+
+    per_layer = (gemv_bytes(scheme, [(d, d)] * 3, M) + gemv_bytes(scheme, [(d, d)], M)
+                 + gemv_bytes(scheme, [(f, d)] * 2, M) + gemv_bytes(scheme, [(d, f)], M))
+    step_bytes = layers * per_layer + (gemv_bytes(scheme, [(head[0], head[1])], M) if head else 0)
+    dom_bytes = gemv_bytes(scheme, [(f, d)] * 2, M)
+    return mats, xh, step, dominant, step_bytes, dom_bytes
+
+
+def cpu_baseline(layer, xs_host, M, budget_s, shapes, scheme, layers):
     """The oracle as it stands, on layer 0's matrices (host copies), until the budget."""
-    import numpy as np
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -65,24 +181,172 @@ def cpu_baseline(layer, xs_host, M, budget_s):
     except Exception:
         threads = os.cpu_count() or 1
     done_bytes, done, t0 = 0, [], time.perf_counter()
-    for name, N, K in LLAMA7B:
+    for name, N, K in shapes:
         q = layer[name]
-        codes = q.codes.cpu().numpy()
-        scale = q.scale.cpu().numpy()
-        ts = time.perf_counter()
-        oracle.gemv_reference(codes, scale, None, SCHEME, xs_host[K])
-        done_bytes += matrix_bytes(N, K, M)
+        bias = None if q.bias is None else q.bias.view(__import__("torch").int16).cpu().numpy().view("uint16")
+        scale = q.scale.cpu().numpy() if scheme == "sym4_g128" else \
+            q.scale.view(__import__("torch").int16).cpu().numpy().view("uint16")
+        oracle.gemv_reference(q.codes.cpu().numpy(), scale, bias, scheme, xs_host[K])
+        done_bytes += gemv_bytes(scheme, [(N, K)], M)
         done.append(name)
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    layer_frac = done_bytes / sum(matrix_bytes(N, K, M) for _, N, K in LLAMA7B)
+    layer_frac = done_bytes / sum(gemv_bytes(scheme, [(N, K)], M) for _, N, K in shapes)
     return {
         "value": done_bytes / dt / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
         "sample": (f"layer 0 matrices {','.join(done)} ({layer_frac:.0%} of one layer), M={M}: "
                    f"numpy fp64 dequantize + BLAS product, {dt:.1f} s; "
-                   f"equivalent {M * layer_frac / (dt * 32):.4f} tok/s for 32 layers"),
+                   f"equivalent {M * layer_frac / (dt * layers):.4f} tok/s for {layers} layers"),
     }
+
+
+def run_llama(c: Ctx, a, big: bool):
+    shapes, scheme = (LLAMA13B, "aff4_g64") if big else (LLAMA7B, "sym4_g128")
+    layers = a.layers or (40 if big else 32)
+    M = a.M or 1
+    head = (152064, 5120) if big else None
+    mats, xh, step, dominant, step_bytes, dom_bytes = decode_stack(c, shapes, scheme, layers, M, head)
+    g_dom = c.graph(dominant)
+    if a.dominant_only:
+        for _ in range(a.warmup + a.steps):
+            g_dom.replay()
+        c.torch.cuda.synchronize()
+        return {"dominant_only": True, "launches": layers * (a.warmup + a.steps)}
+    g_step = c.graph(step)
+    ms = c.time_graph(g_step, a.steps, a.warmup)
+    us_dom = c.time_graph(g_dom, max(4, a.steps // 2), 2) * 1e3 / layers
+    tbs = step_bytes / (ms * 1e-3) / 1e12
+    d, f = shapes[0][2], shapes[4][1]
+    name = "llama13b-shaped decode layer stack + tied head" if big else "llama7b-shaped decode layer stack"
+    out = base_line(a, METRIC, round(tbs, 4), "TB/s", ms, {
+        "workload": name, "layers": layers, "M": M, "scheme": scheme,
+        "matrices": ", ".join(f"{nm} {N}x{K}" for nm, N, K in shapes) + (f", head {head[0]}x{head[1]}" if head else ""),
+        "launches_per_layer": "qkv (one launch), o, gate+up (one launch), down",
+        "weights": "seeded N(0,0.02) drawn on device", "activations": "bf16 N(0,1)"})
+    out["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
+    out["tok_per_s"] = round(M / (ms * 1e-3), 1)
+    out["step_bytes"] = step_bytes
+    out["roofline"] = hbm_roofline(f"gemv_wave_kernel (gate+up, 2 x {f}x{d} {scheme}, one launch)",
+                                   dom_bytes, us_dom)
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(mats[0], {K: v[0] for K, v in xh.items()}, M,
+                                           a.cpu_seconds, shapes, scheme, layers)
+    return out
+
+
+# ---------------------------------------------------------------- MoE
+def run_moe(c: Ctx, a):
+    torch, w4 = c.torch, c.w4
+    E, D, F, Fs, k = 128, 2048, 768, 2048, 8
+    layers = a.layers or 30
+    M = a.M or 1
+    L = []
+    for l in range(layers):
+        gate = w4.empty_quantized("aff4_g64", F, D, num_experts=E)
+        up = w4.empty_quantized("aff4_g64", F, D, num_experts=E)
+        down = w4.empty_quantized("aff4_g64", D, F, num_experts=E)
+        for e in range(E):
+            c.quant(F, D, "aff4_g64", f"moe.L{l}.gate.{e}", out=gate, expert=e)
+            c.quant(F, D, "aff4_g64", f"moe.L{l}.up.{e}", out=up, expert=e)
+            c.quant(D, F, "aff4_g64", f"moe.L{l}.down.{e}", out=down, expert=e)
+        shared = [c.quant(Fs, D, "aff4_g64", f"moe.L{l}.sg"), c.quant(Fs, D, "aff4_g64", f"moe.L{l}.su"),
+                  c.quant(D, Fs, "aff4_g64", f"moe.L{l}.sd")]
+        router = c.quant(E, D, "aff8_g64", f"moe.L{l}.router")
+        L.append((router, gate, up, down, shared))
+    torch.cuda.synchronize()
+    _, x = c.x(M, D, "moe.x")
+    ws = torch.empty(w4.moe_workspace_bytes(M, k, E, D, F, Fs), dtype=torch.uint8, device=c.dev)
+    ids = [torch.empty((M, k), dtype=torch.int32, device=c.dev) for _ in range(layers)]
+    wts = [torch.empty((M, k), dtype=torch.float32, device=c.dev) for _ in range(layers)]
+    logits = torch.empty((M, E), dtype=torch.float32, device=c.dev)
+    y = torch.empty((M, D), dtype=torch.float32, device=c.dev)
+    import ctypes
+
+    lib = w4.lib()
+
+    def step():
+        st = torch.cuda.current_stream(c.dev).cuda_stream
+        for l, (router, gate, up, down, shared) in enumerate(L):
+            rd = router.desc()
+            w4._check(lib.w4_moe_route(ctypes.byref(rd), x.data_ptr(), M, k, logits.data_ptr(),
+                                       ids[l].data_ptr(), wts[l].data_ptr(), st))
+            w4.moe_gemv(gate, up, down, x, ids[l], wts[l], shared=shared, workspace=ws, y=y)
+
+    g = c.graph(step)
+    ms = c.time_graph(g, a.steps, a.warmup)
+    expert_b = 3 * weight_bytes("aff4_g64", F, D)
+    shared_b = 2 * weight_bytes("aff4_g64", Fs, D) + weight_bytes("aff4_g64", D, Fs)
+    router_b = weight_bytes("aff8_g64", E, D)
+    distinct = [len(set(i.cpu().numpy().ravel().tolist())) for i in ids]
+    step_bytes = sum(router_b + u * expert_b + shared_b for u in distinct)
+    tbs = step_bytes / (ms * 1e-3) / 1e12
+    out = base_line(a, "MoE decode tok/s; HBM TB/s over the expert bytes read", round(M / (ms * 1e-3), 1),
+                    "tok/s", ms, {
+                        "workload": "gemma-4-26b-a4b-shaped MoE FFN stack", "layers": layers, "M": M,
+                        "experts": E, "top_k": k, "d_model": D, "expert_ffn": F, "shared_ffn": Fs,
+                        "scheme": "aff4_g64 experts/shared, aff8_g64 router",
+                        "launches_per_layer": "router gemv, top-k, bucket, gate/up, down, combine"})
+    out["hbm_TBps"] = round(tbs, 4)
+    out["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
+    out["distinct_experts_per_layer"] = sum(distinct) / len(distinct)
+    out["step_bytes"] = step_bytes
+    out["roofline"] = hbm_roofline("whole MoE layer (6 launches)", step_bytes // layers, ms * 1e3 / layers)
+    return out
+
+
+# ---------------------------------------------------------------- prefill
+def run_prefill(c: Ctx, a):
+    torch, w4 = c.torch, c.w4
+    M = a.M or 2048
+    res = {}
+    for tag, N, K in (("gate_up", 11008, 4096), ("down", 4096, 11008)):
+        q = c.quant(N, K, "sym4_g128", f"prefill.{tag}")
+        _, X = c.x(M, K, f"prefill.X.{tag}")
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=c.dev)
+
+        def fn(q=q, X=X, Y=Y):
+            for _ in range(10):
+                w4.gemm(q, X, Y)
+
+        g = c.graph(fn)
+        ms = c.time_graph(g, a.steps, a.warmup) / 10
+        res[tag] = (ms, 2.0 * M * N * K)
+    ms = sum(v[0] for v in res.values())
+    fl = sum(v[1] for v in res.values())
+    tfs = fl / (ms * 1e-3) / 1e12
+    out = base_line(a, "Prefill W4A16 GEMM TFLOP/s (% of bf16 MFMA peak)", round(tfs, 2), "TFLOP/s", ms, {
+        "workload": "prefill GEMMs 2048x4096 . 4096->11008 and 2048x11008 . 11008->4096",
+        "M": M, "scheme": "sym4_g128"})
+    for tag, (t, f) in res.items():
+        out[f"{tag}_us"] = round(t * 1e3, 2)
+        out[f"{tag}_TFLOPs"] = round(f / (t * 1e-3) / 1e12, 2)
+    t, f = res["gate_up"]
+    out["roofline"] = {"bound": "mfma", "kernel": "gemm_kernel (2048x4096 . 4096->11008, sym4_g128)",
+                       "achieved": round(f / (t * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(f / (t * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "traffic": None, "flops_per_launch": f, "avg_launch_us": round(t * 1e3, 3)}
+    return out
+
+
+# ---------------------------------------------------------------- single GEMV
+def run_gemv1024(c: Ctx, a):
+    torch, w4 = c.torch, c.w4
+    copies = 1024
+    qs = [c.quant(1024, 1024, "aff4_g64", f"gemv1024.{i}") for i in range(copies)]
+    _, x = c.x(1, 1024, "gemv1024.x")
+    y = torch.empty((1, 1024), dtype=torch.float32, device=c.dev)
+    hot = c.graph(lambda: [w4.gemv_into(qs[0], x, y) for _ in range(copies)])
+    cold = c.graph(lambda: [w4.gemv_into(q, x, y) for q in qs])
+    us_hot = c.time_graph(hot, a.steps, a.warmup) * 1e3 / copies
+    us_cold = c.time_graph(cold, a.steps, a.warmup) * 1e3 / copies
+    nb = gemv_bytes("aff4_g64", [(1024, 1024)], 1)
+    out = base_line(a, "single 1024x1024 W4A16 GEMV latency (us)", round(us_cold, 3), "us", us_cold * 1e-3, {
+        "workload": "gemv 1024x1024 aff4_g64, M=1", "cold": "1024 distinct copies (> MALL)"})
+    out["higher_is_better"] = False
+    out["hot_us"] = round(us_hot, 3)
+    out["cold_GBs"] = round(nb / (us_cold * 1e-6) / 1e9, 1)
+    return out
 
 
 def main():
@@ -92,117 +356,15 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE={world}); "
               "the multi-GPU layout is a design note, not a measured path", file=sys.stderr)
         sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    import bit_weight_only_quantize_amd as w4
-    import synth
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    M = a.M
-
-    # ---- weights: distinct seeded layers, quantized on the device
-    layers = []
-    for l in range(a.layers):
-        mats = {}
-        for name, N, K in LLAMA7B:
-            W = synth.device_weights(N, K, 0.02, 0, f"llama7b.L{l}.{name}", dev)
-            mats[name] = w4.quantize_pack(W, SCHEME)
-            del W
-        layers.append(mats)
-    torch.cuda.synchronize()
-    xs_host = {K: synth.activations_bf16(M, K, 0, f"llama7b.x{K}") for K in (4096, 11008)}
-    xs = {K: torch.from_numpy(v.view(np.int16)).to(dev).view(torch.bfloat16) for K, v in xs_host.items()}
-    ys = {name: torch.empty((M, N), dtype=torch.float32, device=dev) for name, N, _ in LLAMA7B}
-
-    # per layer: Q/K/V share their input (one launch), O, gate/up share theirs (one
-    # launch), down -- the launches a decode layer's data dependencies allow
-    def step():
-        for mats in layers:
-            w4.gemv_multi_into([mats["wq"], mats["wk"], mats["wv"]], xs[4096],
-                               [ys["wq"], ys["wk"], ys["wv"]])
-            w4.gemv_into(mats["wo"], xs[4096], ys["wo"])
-            w4.gemv_multi_into([mats["gate"], mats["up"]], xs[4096], [ys["gate"], ys["up"]])
-            w4.gemv_into(mats["down"], xs[11008], ys["down"])
-
-    def dominant():
-        for mats in layers:
-            w4.gemv_multi_into([mats["gate"], mats["up"]], xs[4096], [ys["gate"], ys["up"]])
-
-    side = torch.cuda.Stream(dev)
-    side.wait_stream(torch.cuda.current_stream(dev))
-    with torch.cuda.stream(side):
-        step()
-        dominant()
-    torch.cuda.current_stream(dev).wait_stream(side)
-    torch.cuda.synchronize()
-
-    g_dom = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_dom):
-        dominant()
-    if a.dominant_only:
-        for _ in range(a.warmup + a.steps):
-            g_dom.replay()
-        torch.cuda.synchronize()
-        print(json.dumps({"dominant_only": True, "launches": a.layers * (a.warmup + a.steps)}))
-        return
-    g_step = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_step):
-        step()
-
-    # ---- timed region: whole step
-    stream = torch.cuda.current_stream(dev)
-    for _ in range(a.warmup):
-        g_step.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(a.steps):
-        g_step.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / a.steps
-
-    # ---- dominant kernel (gate/up GEMV, 11008x4096): average launch duration
-    for _ in range(2):
-        g_dom.replay()
-    torch.cuda.synchronize()
-    reps = max(4, a.steps // 2)
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for _ in range(reps):
-        g_dom.replay()
-    d1.record(stream)
-    torch.cuda.synchronize()
-    us_dom = d0.elapsed_time(d1) * 1e3 / (reps * a.layers)
-    dom_bytes = group_bytes([(11008, 4096), (11008, 4096)], M)
-    dom_gbs = dom_bytes / (us_dom * 1e-6) / 1e9
-
-    step_bytes = a.layers * (group_bytes([(4096, 4096)] * 3, M) + matrix_bytes(4096, 4096, M)
-                             + group_bytes([(11008, 4096)] * 2, M) + matrix_bytes(4096, 11008, M))
-    tbs = step_bytes / (ms_step * 1e-3) / 1e12
-    plan = None
-    out = {
-        "metric": METRIC, "value": round(tbs, 4), "unit": "TB/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "llama7b-shaped decode layer stack", "layers": a.layers, "M": M,
-                   "scheme": SCHEME,
-                   "matrices": "wq,wk,wv,wo 4096x4096; gate,up 11008x4096; down 4096x11008",
-                   "weights": "seeded N(0,0.02) drawn on device", "activations": "bf16 N(0,1)"},
-        "pct_of_hbm_peak": round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2),
-        "tok_per_s": round(M / (ms_step * 1e-3), 1),
-        "step_bytes": step_bytes,
-        "roofline": {"bound": "hbm",
-                     "kernel": "gemv_wave_kernel (gate+up, 2 x 11008x4096 sym4_g128, one launch)",
-                     "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": dom_bytes, "avg_launch_us": round(us_dom, 3)},
-    }
-    if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(layers[0], xs_host, M, a.cpu_seconds)
+    c = Ctx(a)
+    if a.workload in ("llama7b", "llama13b"):
+        out = run_llama(c, a, a.workload == "llama13b")
+    elif a.workload == "moe26b":
+        out = run_moe(c, a)
+    elif a.workload == "prefill":
+        out = run_prefill(c, a)
+    else:
+        out = run_gemv1024(c, a)
     print(json.dumps(out), flush=True)
 
 
