@@ -66,6 +66,63 @@ __device__ __forceinline__ float wave_sum_to_lane63(float v) {
 }
 
 // Workgroup = 4 row wavefronts + SW staging wavefronts (see the file comment).
+// D = sum over one 16-byte code vector of (BIAS_ELEM + u) * x, x given as the
+// staged bf16 pairs xp (XW dwords); 8-bit codes fold the high nibbles in as 16x.
+template <int S>
+__device__ __forceinline__ float dot_code_vector(const u32x4_t& c, const uint32_t* xp,
+                                                 uint32_t MASK, uint32_t MAGIC) {
+    using T = Traits<S>;
+    float D = 0.f, Dh = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t w = c[d];
+        if constexpr (T::BITS == 4) {
+            // sym: (nib & 0xF) ^ 0x..08 = 0x43 | (q + 8); affine: | 0x43 -> 128 + u
+            auto pair = [&](uint32_t s) {
+                return S == SYM4_G128 ? ((s & MASK) ^ MAGIC) : ((s & MASK) | MAGIC);
+            };
+            D = dot2_bf16(pair(w), xp[4 * d + 0], D);
+            D = dot2_bf16(pair(w >> 4), xp[4 * d + 1], D);
+            D = dot2_bf16(pair(w >> 8), xp[4 * d + 2], D);
+            D = dot2_bf16(pair(w >> 12), xp[4 * d + 3], D);
+        } else {
+            const uint32_t xa = xp[2 * d], xb = xp[2 * d + 1];
+            D = dot2_bf16((w & MASK) | MAGIC, xa, D);
+            D = dot2_bf16(((w >> 8) & MASK) | MAGIC, xb, D);
+            Dh = dot2_bf16(((w >> 4) & MASK) | MAGIC, xa, Dh);
+            Dh = dot2_bf16(((w >> 12) & MASK) | MAGIC, xb, Dh);
+        }
+    }
+    if constexpr (T::BITS == 8) D = fmaf(16.f, Dh, D);
+    return D;
+}
+
+// acc += s * D + (b - BIAS * s) * X   (affine)   or   s * D - BIAS * s * X   (sym)
+template <int S>
+__device__ __forceinline__ float apply_group(float acc, float D, float X, float s, float b) {
+    using T = Traits<S>;
+    const float corr = T::AFFINE ? fmaf(-T::BIAS, s, b) : -T::BIAS * s;
+    acc = fmaf(s, D, acc);
+    return fmaf(corr, X, acc);
+}
+
+template <int S>
+__device__ __forceinline__ uint32_t unpack_magic() {
+    return opaque(S == SYM4_G128 ? 0x43084308u : 0x43004300u);
+}
+
+// Staged activation pairs of vector v (XW dwords) from an LDS region.
+template <int S>
+__device__ __forceinline__ void read_pairs(const uint32_t* xs, int v,
+                                           uint32_t (&xp)[Traits<S>::BITS == 4 ? 16 : 8]) {
+    using L = XLayout<S, 1>;
+#pragma unroll
+    for (int p = 0; p < L::XW / 4; ++p) {
+        const uint4 q = *reinterpret_cast<const uint4*>(xs + L::piece(v, p));
+        xp[4 * p] = q.x; xp[4 * p + 1] = q.y; xp[4 * p + 2] = q.z; xp[4 * p + 3] = q.w;
+    }
+}
+
 template <int S, int NV, int R, int XV, int SW>
 __global__ __launch_bounds__(256 + 64 * SW) void gemv_wave_kernel(GemvGroupArgs a, int K,
                                                                   const uint16_t* __restrict__ x) {
@@ -127,7 +184,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void gemv_wave_kernel(GemvGroupArgs 
     __syncthreads();  // activations staged; weight loads still in flight
 
     const uint32_t MASK = opaque(0x000F000Fu);
-    const uint32_t MAGIC = opaque(S == SYM4_G128 ? 0x43084308u : 0x43004300u);
+    const uint32_t MAGIC = unpack_magic<S>();
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -136,41 +193,12 @@ __global__ __launch_bounds__(256 + 64 * SW) void gemv_wave_kernel(GemvGroupArgs 
         const int v = lane + 64 * j;
         if (v >= VR) break;
         uint32_t xp[XW];
-#pragma unroll
-        for (int p = 0; p < XW / 4; ++p) {
-            const uint4 q = *reinterpret_cast<const uint4*>(xs + L::piece(v, p));
-            xp[4 * p] = q.x; xp[4 * p + 1] = q.y; xp[4 * p + 2] = q.z; xp[4 * p + 3] = q.w;
-        }
+        read_pairs<S>(xs, v, xp);
         const float X = XS[v];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float D = 0.f, Dh = 0.f;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t w = c[r][j][d];
-                if constexpr (T::BITS == 4) {
-                    // sym: (nib & 0xF) ^ 0x..08 = 0x43 | (q + 8); affine: | 0x43 -> 128 + u
-                    auto pair = [&](uint32_t s) {
-                        return S == SYM4_G128 ? ((s & MASK) ^ MAGIC) : ((s & MASK) | MAGIC);
-                    };
-                    D = dot2_bf16(pair(w), xp[4 * d + 0], D);
-                    D = dot2_bf16(pair(w >> 4), xp[4 * d + 1], D);
-                    D = dot2_bf16(pair(w >> 8), xp[4 * d + 2], D);
-                    D = dot2_bf16(pair(w >> 12), xp[4 * d + 3], D);
-                } else {
-                    const uint32_t xa = xp[2 * d], xb = xp[2 * d + 1];
-                    D = dot2_bf16((w & MASK) | MAGIC, xa, D);
-                    D = dot2_bf16(((w >> 8) & MASK) | MAGIC, xb, D);
-                    Dh = dot2_bf16(((w >> 4) & MASK) | MAGIC, xa, Dh);
-                    Dh = dot2_bf16(((w >> 12) & MASK) | MAGIC, xb, Dh);
-                }
-            }
-            if constexpr (T::BITS == 8) D = fmaf(16.f, Dh, D);
-            const float s = sc[r][j];
-            const float corr = T::AFFINE ? fmaf(-T::BIAS, s, bi[r][j]) : -T::BIAS * s;
-            acc[r] = fmaf(s, D, acc[r]);
-            acc[r] = fmaf(corr, X, acc[r]);
-        }
+        for (int r = 0; r < R; ++r)
+            acc[r] = apply_group<S>(acc[r], dot_code_vector<S>(c[r][j], xp, MASK, MAGIC), X,
+                                    sc[r][j], T::AFFINE ? bi[r][j] : 0.f);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {

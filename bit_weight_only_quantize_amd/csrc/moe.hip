@@ -20,58 +20,42 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "skinny.hpp"
+#include "moe1.hpp"
 
 namespace w4 {
 
 // ---------------------------------------------------------------- routing
-// One wavefront per token. E <= 1024 (16 logits per lane), k <= 32.
+// One workgroup (64 threads) per token, E <= 1024. Every logit is ranked against
+// all E logits (staged in LDS): rank = #{j : l_j > l_e or (l_j == l_e and j < e)},
+// i.e. its position in a stable sort by logit descending. rank < k selects the
+// expert into slot `rank`. Softmax over all E raw logits; no renormalization.
 __global__ __launch_bounds__(64) void topk_softmax_kernel(const float* __restrict__ logits, int E,
                                                           int k, int32_t* __restrict__ ids,
                                                           float* __restrict__ wts) {
+    __shared__ float ls[1024];
     const int m = blockIdx.x, lane = threadIdx.x;
     const float* l = logits + (int64_t)m * E;
-    float v[16];
-    bool taken[16];
     float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? l[e] : -INFINITY;
-        taken[i] = e >= E;
-        mx = fmaxf(mx, v[i]);
+    for (int e = lane; e < E; e += 64) {
+        ls[e] = l[e];
+        mx = fmaxf(mx, ls[e]);
     }
     mx = wave_max(mx);
+    __syncthreads();
     float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-        if (lane + 64 * i < E) s += expf(v[i] - mx);
+    for (int e = lane; e < E; e += 64) s += expf(ls[e] - mx);
     for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);  // same order in every lane
     const float inv = 1.f / s;
-    for (int r = 0; r < k; ++r) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int e = lane + 64 * i;
-            if (!taken[i] && (v[i] > bv || (v[i] == bv && e < bi))) {
-                bv = v[i];
-                bi = e;
-            }
+    for (int e = lane; e < E; e += 64) {
+        const float v = ls[e];
+        int rank = 0;
+        for (int j = 0; j < E; ++j) {
+            const float u = ls[j];
+            rank += (u > v) | ((u == v) & (j < e));
         }
-        for (int o = 32; o >= 1; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, 64);
-            const int oi = __shfl_xor(bi, o, 64);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (lane + 64 * i == bi) taken[i] = true;
-        if (lane == 0) {
-            ids[(int64_t)m * k + r] = bi;
-            wts[(int64_t)m * k + r] = expf(bv - mx) * inv;
+        if (rank < k) {
+            ids[(int64_t)m * k + rank] = e;
+            wts[(int64_t)m * k + rank] = expf(v - mx) * inv;
         }
     }
 }
@@ -402,11 +386,86 @@ static hipError_t moe_passes(const MoeArgs& a0, int64_t Fs, hipStream_t st) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- M = 1 fast path
+static Moe1Mat m1m(const void* const* t, int64_t N, int64_t K, int scheme) {
+    const int64_t groups = K / (scheme == SYM4_G128 ? 128 : 64);
+    Moe1Mat m{};
+    m.codes = (const uint8_t*)t[0];
+    m.scale = (const uint8_t*)t[1];
+    m.bias = (const uint8_t*)t[2];
+    m.stride_c = N * K / 2;
+    m.stride_s = N * groups * (scheme == SYM4_G128 ? 4 : 2);
+    return m;
+}
+
+bool moe1_ok(int64_t M, int k, int64_t D, int64_t F, int64_t Fs) {
+    return M == 1 && k <= 8 && D >= 2048 && D <= 4096 && F >= 32 && F <= 1024 && Fs <= 4096 &&
+           (Fs == 0 || Fs >= 32);
+}
+
+template <int S, int NVD, int NVS>
+static void go_down1(const Moe1Args& a, int blocks, size_t lds, hipStream_t st) {
+    hipLaunchKernelGGL((moe1_down_kernel<S, NVD, NVS, 1, NVD + NVS>), dim3(blocks), dim3(320), lds,
+                       st, a);
+}
+
+template <int S, int NVD>
+static void pick_nvs(int nvs, const Moe1Args& a, int blocks, size_t lds, hipStream_t st) {
+    if (nvs == 0) go_down1<S, NVD, 0>(a, blocks, lds, st);
+    else if (nvs == 1) go_down1<S, NVD, 1>(a, blocks, lds, st);
+    else go_down1<S, NVD, 2>(a, blocks, lds, st);
+}
+
+template <int S>
+static hipError_t moe1_passes(Moe1Args a, hipStream_t st) {
+    constexpr int R = 2;
+    const int kv = Traits<S>::KV;
+    a.tiles_r = (a.F + 4 * R - 1) / (4 * R);
+    a.tiles_s = a.has_shared ? (a.Fs + 4 * R - 1) / (4 * R) : 0;
+    const int blocks = a.k * a.tiles_r + a.tiles_s;
+    const size_t lds = (size_t)(a.D / 2 + a.D / kv) * 4;
+    if (a.D / kv <= 64)
+        hipLaunchKernelGGL((moe1_gate_up_kernel<S, 1, R, 1>), dim3(blocks), dim3(320), lds, st, a);
+    else
+        hipLaunchKernelGGL((moe1_gate_up_kernel<S, 2, R, 2>), dim3(blocks), dim3(320), lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int VRF = a.F / kv, VRS = a.has_shared ? a.Fs / kv : 0;
+    const int nvd = (VRF + 7) / 8, nvs = (VRS + 63) / 64;
+    const size_t lds2 = (size_t)(8 * (a.F / 2 + VRF) + (a.has_shared ? a.Fs / 2 + VRS : 0)) * 4;
+    const int blocks2 = (a.D + 3) / 4;
+    switch (nvd) {
+        case 1: pick_nvs<S, 1>(nvs, a, blocks2, lds2, st); break;
+        case 2: pick_nvs<S, 2>(nvs, a, blocks2, lds2, st); break;
+        case 3: pick_nvs<S, 3>(nvs, a, blocks2, lds2, st); break;
+        default: pick_nvs<S, 4>(nvs, a, blocks2, lds2, st); break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_moe(int scheme, const MoeMats& W, const uint16_t* x, int64_t M, const int32_t* ids,
                       const float* wts, int k, void* ws, float* y, hipStream_t st) {
     const int64_t E = W.E, D = W.D, F = W.F, Fs = W.Fs;
     const MoeWorkspace L = moe_workspace_layout(M, k, E, D, F, Fs);
     uint8_t* base = (uint8_t*)ws;
+    if (moe1_ok(M, k, D, F, Fs)) {
+        Moe1Args a{};
+        a.gate = m1m(W.gate, F, D, scheme);
+        a.up = m1m(W.up, F, D, scheme);
+        a.down = m1m(W.down, D, F, scheme);
+        a.has_shared = Fs > 0;
+        if (Fs > 0) {
+            a.sgate = m1m(W.sgate, Fs, D, scheme);
+            a.sup = m1m(W.sup, Fs, D, scheme);
+            a.sdown = m1m(W.sdown, D, Fs, scheme);
+        }
+        a.k = k; a.E = (int)E; a.D = (int)D; a.F = (int)F; a.Fs = (int)Fs;
+        a.x = x; a.ids = ids; a.wts = wts;
+        a.h = (uint16_t*)(base + L.h);
+        a.hs = (uint16_t*)(base + L.hs);
+        a.y = y;
+        return scheme == SYM4_G128 ? moe1_passes<SYM4_G128>(a, st) : moe1_passes<AFF4_G64>(a, st);
+    }
     MoeArgs a{};
     a.gate = mm(W.gate[0], W.gate[1], W.gate[2], F, D, scheme);
     a.up = mm(W.up[0], W.up[1], W.up[2], F, D, scheme);

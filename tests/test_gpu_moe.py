@@ -144,3 +144,16 @@ def test_moe_rejects_bad_arguments():
     with pytest.raises(w4.W4Error) as ei:
         w4.moe_gemv(gate, up, down, x, ids, wts, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
     assert ei.value.code == -5
+
+
+@pytest.mark.parametrize("scheme", ["aff4_g64", "sym4_g128"])
+@pytest.mark.parametrize("k,ids_row,shared", [
+    (8, [5, 9, 5, -1, 31, 0, 200, 17], True),     # duplicate expert, invalid ids
+    (3, [2, 30, 7], True),                        # fewer than 8 slots
+    (8, [1, 2, 3, 4, 5, 6, 7, 8], False),         # no shared expert
+])
+def test_moe_single_token_fast_path_edges(scheme, k, ids_row, shared):
+    E, D, F, Fs = 32, 2048, 768, 2048
+    ids = np.array([ids_row], dtype=np.int32)
+    p = np.linspace(0.3, 0.05, k)[None, :]
+    _moe_case(1, E, D, F, Fs if shared else 0, k, scheme, 7, f"m1.{scheme}.{k}.{int(shared)}", ids=ids, p=p)
