@@ -252,9 +252,110 @@ hipError_t launch_gemv_wave(int scheme, int count, const void* const* codes,
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- 2 <= M <= 64, wave per row
+constexpr size_t kMaxLds = 160 * 1024;
+
+template <typename Kern>
+static void allow_lds(Kern k, size_t bytes) {
+    if (bytes > 64 * 1024)
+        (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)kMaxLds);
+}
+
+// Token tile: as many tokens as the LDS double buffer and the staging
+// wavefronts' registers (MT x XV activation vectors in flight) allow.
+static int mt_tile(int64_t M, int64_t K, int kv, int nv) {
+    int mt = M <= 2 ? 2 : (M <= 4 ? 4 : 8);
+    const int xv = (nv + 1) / 2;
+    while (mt > 2 && (mt * xv > 8 || (size_t)2 * mt * (K / 2 + K / kv) * 4 > kMaxLds)) mt /= 2;
+    return mt;
+}
+
+bool gemv_wave_mt_ok(int scheme, int64_t K, int64_t M) {
+    const int kv = scheme == AFF8_G64 ? 16 : 32;
+    const int64_t VR = K / kv;
+    if (M < 2 || M > 64 || VR < 64 || wave_nv(VR) == 0) return false;
+    if (scheme == AFF8_G64 && wave_nv(VR) > 2) return false;
+    return (size_t)2 * 2 * (K / 2 + VR) * 4 <= kMaxLds;
+}
+
+template <int S, int NV, int MT>
+static void go_mt(const GemvGroupArgs& a, int blocks, int K, int M, const uint16_t* x, size_t lds,
+                  hipStream_t st) {
+    constexpr int R = NV <= 3 ? 2 : 1;
+    constexpr int SW = 2, XV = (NV + 1) / 2;
+    auto kern = gemv_wave_mt_kernel<S, NV, R, MT, XV, SW>;
+    allow_lds(kern, lds);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256 + 64 * SW), lds, st, a, K, M, x);
+}
+
+template <int S, int NV>
+static void pick_mt_tile(int mt, const GemvGroupArgs& a, int blocks, int K, int M,
+                         const uint16_t* x, size_t lds, hipStream_t st) {
+    constexpr int XV = (NV + 1) / 2;
+    if constexpr (8 * XV <= 8)
+        if (mt == 8) return go_mt<S, NV, 8>(a, blocks, K, M, x, lds, st);
+    if constexpr (4 * XV <= 8)
+        if (mt >= 4) return go_mt<S, NV, 4>(a, blocks, K, M, x, lds, st);
+    go_mt<S, NV, 2>(a, blocks, K, M, x, lds, st);
+}
+
+template <int S>
+static void pick_nv_mt(int nv, int mt, const GemvGroupArgs& a, int blocks, int K, int M,
+                       const uint16_t* x, size_t lds, hipStream_t st) {
+    if constexpr (S == AFF8_G64) {
+        if (nv == 1) pick_mt_tile<S, 1>(mt, a, blocks, K, M, x, lds, st);
+        else pick_mt_tile<S, 2>(mt, a, blocks, K, M, x, lds, st);
+    } else {
+        switch (nv) {
+            case 1: pick_mt_tile<S, 1>(mt, a, blocks, K, M, x, lds, st); break;
+            case 2: pick_mt_tile<S, 2>(mt, a, blocks, K, M, x, lds, st); break;
+            case 3: pick_mt_tile<S, 3>(mt, a, blocks, K, M, x, lds, st); break;
+            case 4: pick_mt_tile<S, 4>(mt, a, blocks, K, M, x, lds, st); break;
+            case 6: pick_mt_tile<S, 6>(mt, a, blocks, K, M, x, lds, st); break;
+            case 7: pick_mt_tile<S, 7>(mt, a, blocks, K, M, x, lds, st); break;
+            default: pick_mt_tile<S, 8>(mt, a, blocks, K, M, x, lds, st); break;
+        }
+    }
+}
+
+hipError_t launch_gemv_wave_mt(int scheme, int count, const void* const* codes,
+                               const void* const* scale, const void* const* bias, const int64_t* N,
+                               int64_t K, const uint16_t* x, int64_t M, float* const* y,
+                               hipStream_t st) {
+    const int kv = scheme == AFF8_G64 ? 16 : 32;
+    const int64_t VR = K / kv;
+    const int nv = wave_nv(VR);
+    const int R = nv <= 3 ? 2 : 1;
+    const int mt = mt_tile(M, K, kv, nv);
+    GemvGroupArgs a{};
+    int blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        a.codes[i] = (const uint8_t*)codes[i];
+        a.scale[i] = (const uint8_t*)scale[i];
+        a.bias[i] = (const uint8_t*)bias[i];
+        a.y[i] = y[i];
+        a.N[i] = (int)N[i];
+        a.tile_start[i] = blocks;
+        blocks += (int)((N[i] + 4 * R - 1) / (4 * R));
+    }
+    a.tile_start[count] = blocks;
+    a.count = count;
+    if (blocks == 0) return hipSuccess;
+    const size_t lds = (size_t)2 * mt * (K / 2 + VR) * 4;
+    switch (scheme) {
+        case SYM4_G128: pick_nv_mt<SYM4_G128>(nv, mt, a, blocks, (int)K, (int)M, x, lds, st); break;
+        case AFF4_G64: pick_nv_mt<AFF4_G64>(nv, mt, a, blocks, (int)K, (int)M, x, lds, st); break;
+        default: pick_nv_mt<AFF8_G64>(nv, mt, a, blocks, (int)K, (int)M, x, lds, st); break;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv(int scheme, const void* codes, const void* scale, const void* bias,
                        int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                        hipStream_t st) {
+    if (gemv_wave_mt_ok(scheme, K, M))
+        return launch_gemv_wave_mt(scheme, 1, &codes, &scale, &bias, &N, K, x, M, &y, st);
     if (M == 1 && gemv_wave_ok(scheme, K))
         return launch_gemv_wave(scheme, 1, &codes, &scale, &bias, &N, K, x, &y, st);
     const GemvPlan p = plan_gemv(scheme, N, K, M);

@@ -208,3 +208,149 @@ __global__ __launch_bounds__(256 + 64 * SW) void gemv_wave_kernel(GemvGroupArgs 
 }
 
 }  // namespace w4
+
+namespace w4 {
+
+// Multi-token decode GEMV (2 <= M <= 64) on the same design: a row wavefront
+// loads its R rows' codes once (registers) and reuses them for every token;
+// the staging wavefronts stage MT tokens at a time into one of two LDS buffers
+// while the row wavefronts consume the other. Per token tile a row wavefront
+// unpacks each code vector once and issues 16 v_dot2 per token.
+// LDS: 2 * MT * (K/2 + K/KV) dwords (up to the 160 KiB of a gfx950 CU).
+template <int S, int NV, int R, int MT, int XV, int SW>
+__global__ __launch_bounds__(256 + 64 * SW) void gemv_wave_mt_kernel(GemvGroupArgs a, int K, int M,
+                                                                     const uint16_t* __restrict__ x) {
+    using T = Traits<S>;
+    using L = XLayout<S, 1>;
+    constexpr int XW = L::XW;
+    extern __shared__ __align__(16) uint32_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int VR = K / T::KV;
+    const int tokw = K / 2 + VR;             // dwords per staged token
+    const int tiles = (M + MT - 1) / MT;
+
+    const int t = blockIdx.x;
+    int i = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxGroup; ++q)
+        if (q < a.count && t >= a.tile_start[q]) i = q;
+    const int N = a.N[i];
+    const int row0 = (t - a.tile_start[i]) * (4 * R) + wave * R;
+
+    if (wave >= 4) {
+        // staging wavefronts: tile s -> buffer s % 2, one barrier per tile
+        const int sl = threadIdx.x - 256;
+        for (int s = 0; s < tiles; ++s) {
+            uint32_t* buf = smem + (s & 1) * MT * tokw;
+            XStage<S, XV, 64 * SW> st[MT];  // all loads of the tile first, then the LDS writes
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int tok = min(s * MT + m, M - 1);  // rows past M re-stage the last (unused)
+                st[m].fetch(x + (int64_t)tok * K, VR, sl);
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                st[m].commit(VR, buf + m * tokw, reinterpret_cast<float*>(buf + m * tokw + K / 2), sl);
+            __syncthreads();
+        }
+        return;
+    }
+
+    const int64_t rowbytes = (int64_t)K * T::BITS / 8;
+    const int64_t groups = K / T::GROUP;
+    constexpr int SB = T::AFFINE ? 2 : 4;
+    u32x4_t c[R][NV];
+    float sc[R][NV], bi[R][NV];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t n = row0 + r < N ? row0 + r : N - 1;
+        const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(a.codes[i] + n * rowbytes);
+        const uint8_t* sp = a.scale[i] + n * groups * SB;
+        const uint8_t* bp = T::AFFINE ? a.bias[i] + n * groups * 2 : nullptr;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int v = min(lane + 64 * j, VR - 1);
+            c[r][j] = __builtin_nontemporal_load(cp + v);
+            const int g = v / T::VPG;
+            if constexpr (T::AFFINE) {
+                sc[r][j] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(sp)[g]);
+                bi[r][j] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(bp)[g]);
+            } else {
+                sc[r][j] = reinterpret_cast<const float*>(sp)[g];
+                bi[r][j] = 0.f;
+            }
+        }
+    }
+    const uint32_t MASK = opaque(0x000F000Fu);
+    const uint32_t MAGIC = unpack_magic<S>();
+    for (int s = 0; s < tiles; ++s) {
+        __syncthreads();  // tile s staged
+        const uint32_t* buf = smem + (s & 1) * MT * tokw;
+        float acc[R][MT];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int v = lane + 64 * j;
+            if (v >= VR) break;
+            uint32_t w[R][16];  // unpacked bf16 pairs of each row's code vector
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t cw = c[r][j][d];
+                    if constexpr (T::BITS == 4) {
+#pragma unroll
+                        for (int h = 0; h < 4; ++h) {
+                            const uint32_t sft = cw >> (4 * h);
+                            w[r][4 * d + h] = S == SYM4_G128 ? ((sft & MASK) ^ MAGIC) : ((sft & MASK) | MAGIC);
+                        }
+                    } else {
+                        w[r][4 * d + 0] = (cw & MASK) | MAGIC;          // low nibbles, bytes 0/2
+                        w[r][4 * d + 1] = ((cw >> 8) & MASK) | MAGIC;   // low nibbles, bytes 1/3
+                        w[r][4 * d + 2] = ((cw >> 4) & MASK) | MAGIC;   // high nibbles, bytes 0/2
+                        w[r][4 * d + 3] = ((cw >> 12) & MASK) | MAGIC;  // high nibbles, bytes 1/3
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                uint32_t xp[XW];
+                read_pairs<S>(buf + m * tokw, v, xp);
+                const float X = reinterpret_cast<const float*>(buf + m * tokw + K / 2)[v];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float D = 0.f;
+                    if constexpr (T::BITS == 4) {
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) D = dot2_bf16(w[r][q], xp[q], D);
+                    } else {
+                        float Dh = 0.f;
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            D = dot2_bf16(w[r][4 * d + 0], xp[2 * d], D);
+                            D = dot2_bf16(w[r][4 * d + 1], xp[2 * d + 1], D);
+                            Dh = dot2_bf16(w[r][4 * d + 2], xp[2 * d], Dh);
+                            Dh = dot2_bf16(w[r][4 * d + 3], xp[2 * d + 1], Dh);
+                        }
+                        D = fmaf(16.f, Dh, D);
+                    }
+                    acc[r][m] = apply_group<S>(acc[r][m], D, X, sc[r][j], bi[r][j]);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float tot = wave_sum_to_lane63(acc[r][m]);
+                const int tok = s * MT + m;
+                if (lane == 63 && row0 + r < N && tok < M) a.y[i][(int64_t)tok * N + row0 + r] = tot;
+            }
+    }
+}
+
+}  // namespace w4
