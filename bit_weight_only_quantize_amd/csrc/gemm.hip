@@ -5,31 +5,34 @@
 // weights are converted right after they are loaded instead of materializing a
 // dequantized copy in HBM.
 //
-// Tiling for gfx950 (256 CUs in 8 XCDs, 160 KiB LDS, bf16 MFMA 32x32x16):
-//   * a workgroup computes a 256 (M) x 128 (N) tile with 4 wavefronts, each a
-//     128 x 64 sub-tile of 4 x 2 MFMA blocks (fp32 accumulators);
-//   * per 32-wide k step the X tile (bf16, 16 KiB) is copied and the W tile's
-//     codes (2 KiB) are dequantized to bf16 -- w = s*q (sym) or s*u + b (affine),
-//     computed in fp32 and rounded to nearest even -- into a double-buffered LDS
-//     stage (48 KiB), 16-byte chunks XOR-swizzled so the MFMA operand reads are
-//     free of bank conflicts; the next step's global loads are in flight while
-//     the current step's MFMAs run;
-//   * tiles are ordered so that consecutive tiles land on one XCD and share an
-//     X row block (workgroups are dispatched round-robin over the 8 XCDs), which
-//     keeps the X block resident in that XCD's L2;
+// Design for gfx950 (256 CUs in 8 XCDs, 160 KiB LDS, bf16 MFMA 32x32x16):
+//   * a workgroup computes a 256 (M) x 128 (N) tile with 8 wavefronts: 4 MFMA
+//     wavefronts (a 2 x 2 grid of 128 x 64 sub-tiles, fp32 accumulators) and 4
+//     producer wavefronts, one of each per SIMD, so the dequantization VALU work
+//     of the producer issues in the shadow of the consumer's MFMAs;
+//   * producers stream 64-wide k steps: the X tile (bf16, 32 KiB) is copied and
+//     the W tile's codes (4 KiB) are dequantized -- w = s*q (sym) or s*u + b
+//     (affine), in fp32, rounded to nearest even bf16 -- into a 3-stage LDS ring
+//     (144 KiB); global loads run two steps ahead of their LDS stores;
+//   * 16-byte chunks are XOR-swizzled by row so MFMA operand reads from LDS are
+//     free of bank conflicts; one barrier per k step separates the ring stages;
+//   * tiles are ordered so consecutive tiles land on one XCD and share an X row
+//     block (workgroups are dispatched round-robin over the 8 XCDs), keeping
+//     that block resident in the XCD's L2;
 //   * the epilogue rounds the fp32 accumulators to bf16 (nearest even).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace w4 {
 
-constexpr int GBM = 256, GBN = 128, GBK = 32;
+constexpr int GBM = 256, GBN = 128, GBK = 64, GSTAGES = 3;
+constexpr int GCH = GBK / 8;  // 16-byte chunks per LDS row
 
-// 16-byte chunk c (0..3) of LDS row `row` (64 bytes per row)
-__device__ __forceinline__ int gchunk(int row, int c) { return row * 4 + (c ^ ((row >> 1) & 3)); }
+// LDS chunk index of chunk c (0..7) of row `row`
+__device__ __forceinline__ int gchunk(int row, int c) { return row * GCH + (c ^ (row & 7)); }
 
 template <int S>
-__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(512) void gemm_kernel(const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ scale,
                                                    const uint8_t* __restrict__ bias, int M, int N,
                                                    int K, const uint16_t* __restrict__ X,
@@ -37,10 +40,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
                                                    int tiles_n) {
     using T = Traits<S>;
     extern __shared__ __align__(16) uint4 gsm[];
-    uint4* As = gsm;                      // [2][GBM * 4]
-    uint4* Bs = gsm + 2 * GBM * 4;        // [2][GBN * 4]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    constexpr int STAGE = (GBM + GBN) * GCH;  // chunks per ring stage
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     // XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a
     // contiguous range of tiles, N-fastest, so an XCD's workgroups share X rows.
@@ -49,69 +51,97 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
     const int L = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
     if (L >= ntiles) return;
     const int m0 = (L / tiles_n) * GBM, n0 = (L % tiles_n) * GBN;
+    const int ksteps = K / GBK;
 
-    // ---- per-thread load assignment
-    // X: 4 chunks of 16 bytes: rows tid/4 + 64 i, chunk tid % 4
-    const int ac = tid & 3;
-    const uint16_t* xrow[4];
+    if (wave >= 4) {
+        // ---------------- producers: 256 threads
+        const int p = tid - 256;
+        const uint16_t* xrow[8];
+        int arow[8], ac[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = min(m0 + (tid >> 2) + 64 * i, M - 1);
-        xrow[i] = X + (int64_t)r * K + ac * 8;
-    }
-    // W: row tid/2, 16 weights (8 bytes of codes) at k offset 16 * (tid % 2)
-    const int brow = tid >> 1, bh = tid & 1;
-    const int bn = min(n0 + brow, N - 1);
-    const uint8_t* crow = codes + (int64_t)bn * (K / 2) + bh * 8;
-    const int64_t groups = K / T::GROUP;
-    constexpr int SB = T::AFFINE ? 2 : 4;
-    const uint8_t* srow = scale + (int64_t)bn * groups * SB;
-    const uint8_t* bro = T::AFFINE ? bias + (int64_t)bn * groups * 2 : nullptr;
+        for (int i = 0; i < 8; ++i) {
+            const int q = p + 256 * i;
+            arow[i] = q >> 3;
+            ac[i] = q & 7;
+            const int r = min(m0 + arow[i], M - 1);
+            xrow[i] = X + (int64_t)r * K + ac[i] * 8;
+        }
+        const int brow = p >> 1, bh = p & 1;
+        const int bn = min(n0 + brow, N - 1);
+        const uint8_t* crow = codes + (int64_t)bn * (K / 2) + bh * 16;
+        const int64_t groups = K / T::GROUP;
+        constexpr int SB = T::AFFINE ? 2 : 4;
+        const uint8_t* srow = scale + (int64_t)bn * groups * SB;
+        const uint8_t* bro = T::AFFINE ? bias + (int64_t)bn * groups * 2 : nullptr;
 
-    u32x4_t xa[4];
-    uint2 wc;
-    float ws, wb;
-    auto gload = [&](int k0) {
+        struct Regs {
+            u32x4_t xa[8];
+            u32x4_t wc;
+            float ws, wb;
+        };
+        auto gload = [&](Regs& R, int s) {
+            const int k0 = s * GBK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xa[i] = *reinterpret_cast<const u32x4_t*>(xrow[i] + k0);
-        wc = *reinterpret_cast<const uint2*>(crow + k0 / 2);
-        const int g = (k0 + bh * 16) / T::GROUP;
-        if constexpr (T::AFFINE) {
-            ws = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(srow)[g]);
-            wb = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(bro)[g]);
-        } else {
-            ws = reinterpret_cast<const float*>(srow)[g];
-            wb = -8.f * ws;  // q = u - 8 after the xor below
-        }
-    };
-    auto lstore = [&](int stage) {
-        uint4* A = As + stage * GBM * 4;
+            for (int i = 0; i < 8; ++i) R.xa[i] = *reinterpret_cast<const u32x4_t*>(xrow[i] + k0);
+            R.wc = *reinterpret_cast<const u32x4_t*>(crow + k0 / 2);
+            const int g = k0 / T::GROUP;
+            if constexpr (T::AFFINE) {
+                R.ws = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(srow)[g]);
+                R.wb = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(bro)[g]);
+            } else {
+                R.ws = reinterpret_cast<const float*>(srow)[g];
+                R.wb = -8.f * R.ws;  // q = u - 8 after the xor below
+            }
+        };
+        auto lstore = [&](const Regs& R, int s) {
+            uint4* A = gsm + (s % GSTAGES) * STAGE;
+            uint4* B = A + GBM * GCH;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4_t v = xa[i];
-            A[gchunk((tid >> 2) + 64 * i, ac)] = make_uint4(v[0], v[1], v[2], v[3]);
-        }
-        // dequantize 16 weights -> 8 bf16 pairs (natural k order)
-        uint32_t out[8];
+            for (int i = 0; i < 8; ++i)
+                A[gchunk(arow[i], ac[i])] = make_uint4(R.xa[i][0], R.xa[i][1], R.xa[i][2], R.xa[i][3]);
+            // 32 weights (4 code dwords) -> 4 chunks of 8 bf16 in natural k order
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-            uint32_t c = d ? wc.y : wc.x;
-            if constexpr (S == SYM4_G128) c ^= 0x88888888u;  // two's complement -> q + 8
-            const uint32_t lo = c & 0x0F0F0F0Fu;             // elements 0, 2, 4, 6
-            const uint32_t hi = (c >> 4) & 0x0F0F0F0Fu;      // elements 1, 3, 5, 7
+            for (int d = 0; d < 4; ++d) {
+                uint32_t c = R.wc[d];
+                if constexpr (S == SYM4_G128) c ^= 0x88888888u;  // two's complement -> q + 8
+                const uint32_t lo = c & 0x0F0F0F0Fu;             // elements 0, 2, 4, 6
+                const uint32_t hi = (c >> 4) & 0x0F0F0F0Fu;      // elements 1, 3, 5, 7
+                uint32_t o[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float e0 = (float)((lo >> (8 * b)) & 0xFFu);
-                const float e1 = (float)((hi >> (8 * b)) & 0xFFu);
-                const bf16x2_t p = {(__bf16)fmaf(e0, ws, wb), (__bf16)fmaf(e1, ws, wb)};
-                out[4 * d + b] = __builtin_bit_cast(uint32_t, p);
+                for (int b = 0; b < 4; ++b) {
+                    const float e0 = (float)((lo >> (8 * b)) & 0xFFu);
+                    const float e1 = (float)((hi >> (8 * b)) & 0xFFu);
+                    const bf16x2_t pr = {(__bf16)fmaf(e0, R.ws, R.wb), (__bf16)fmaf(e1, R.ws, R.wb)};
+                    o[b] = __builtin_bit_cast(uint32_t, pr);
+                }
+                B[gchunk(brow, 4 * bh + d)] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        };
+        // prologue: stages 0 and 1 stored, step 2 in registers
+        Regs ra, rb;
+        gload(ra, 0);
+        if (ksteps > 1) gload(rb, 1);
+        lstore(ra, 0);
+        if (ksteps > 2) gload(ra, 2);
+        if (ksteps > 1) lstore(rb, 1);
+        if (ksteps > 3) gload(rb, 3);
+        __syncthreads();
+        // iteration s: store step s+2 (loaded earlier), load step s+4
+        for (int s = 0; s < ksteps; s += 2) {
+            if (s + 2 < ksteps) lstore(ra, s + 2);
+            if (s + 4 < ksteps) gload(ra, s + 4);
+            __syncthreads();
+            if (s + 1 < ksteps) {
+                if (s + 3 < ksteps) lstore(rb, s + 3);
+                if (s + 5 < ksteps) gload(rb, s + 5);
+                __syncthreads();
             }
         }
-        uint4* B = Bs + stage * GBN * 4;
-        B[gchunk(brow, 2 * bh)] = make_uint4(out[0], out[1], out[2], out[3]);
-        B[gchunk(brow, 2 * bh + 1)] = make_uint4(out[4], out[5], out[6], out[7]);
-    };
+        return;
+    }
 
+    // ---------------- MFMA consumers: 4 wavefronts, 128 x 64 each
+    const int wm = wave >> 1, wn = wave & 1;
     f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -119,19 +149,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    const int ksteps = K / GBK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
     const int arow = wm * 128 + (lane & 31), brw = wn * 64 + (lane & 31), half = lane >> 5;
+    __syncthreads();  // prologue stages ready
     for (int s = 0; s < ksteps; ++s) {
-        const int st = s & 1;
-        if (s + 1 < ksteps) gload((s + 1) * GBK);
-        const uint4* A = As + st * GBM * 4;
-        const uint4* B = Bs + st * GBN * 4;
+        const uint4* A = gsm + (s % GSTAGES) * STAGE;
+        const uint4* B = A + GBM * GCH;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < GBK / 16; ++kk) {
             bf16x8_t af[4], bf[2];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -145,7 +169,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
-        if (s + 1 < ksteps) lstore(st ^ 1);
         __syncthreads();
     }
 
@@ -161,8 +184,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
                 if (m < M) {
-                    const bf16x2_t p = {(__bf16)acc[i][j][r], (__bf16)0.f};
-                    Y[(int64_t)m * N + n] = (uint16_t)__builtin_bit_cast(uint32_t, p);
+                    const bf16x2_t pr = {(__bf16)acc[i][j][r], (__bf16)0.f};
+                    Y[(int64_t)m * N + n] = (uint16_t)__builtin_bit_cast(uint32_t, pr);
                 }
             }
         }
@@ -173,15 +196,12 @@ hipError_t launch_gemm(int scheme, const void* codes, const void* scale, const v
                        hipStream_t st) {
     const int tm = (int)((M + GBM - 1) / GBM), tn = (int)((N + GBN - 1) / GBN);
     const int per = (tm * tn + 7) / 8;
-    const size_t lds = 2 * (GBM + GBN) * 64;
-    if (scheme == SYM4_G128)
-        hipLaunchKernelGGL(gemm_kernel<SYM4_G128>, dim3(8 * per), dim3(256), lds, st,
-                           (const uint8_t*)codes, (const uint8_t*)scale, (const uint8_t*)bias,
-                           (int)M, (int)N, (int)K, X, Y, tm, tn);
-    else
-        hipLaunchKernelGGL(gemm_kernel<AFF4_G64>, dim3(8 * per), dim3(256), lds, st,
-                           (const uint8_t*)codes, (const uint8_t*)scale, (const uint8_t*)bias,
-                           (int)M, (int)N, (int)K, X, Y, tm, tn);
+    const size_t lds = (size_t)GSTAGES * (GBM + GBN) * GCH * 16;
+    auto kern = scheme == SYM4_G128 ? gemm_kernel<SYM4_G128> : gemm_kernel<AFF4_G64>;
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(kern, dim3(8 * per), dim3(512), lds, st, (const uint8_t*)codes,
+                       (const uint8_t*)scale, (const uint8_t*)bias, (int)M, (int)N, (int)K, X, Y,
+                       tm, tn);
     return hipGetLastError();
 }
 
