@@ -74,10 +74,13 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint8_t* __restrict__ c
         const uint8_t* srow = scale + (int64_t)bn * groups * SB;
         const uint8_t* bro = T::AFFINE ? bias + (int64_t)bn * groups * 2 : nullptr;
 
+        // Loaded values are kept raw until lstore: converting a scale right after
+        // its load would make the wavefront wait (vmcnt retires in order) for the
+        // whole load batch issued before it, defeating the prefetch.
         struct Regs {
             u32x4_t xa[8];
             u32x4_t wc;
-            float ws, wb;
+            uint32_t ws, wb;  // raw scale / bias bits
         };
         auto gload = [&](Regs& R, int s) {
             const int k0 = s * GBK;
@@ -86,14 +89,15 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint8_t* __restrict__ c
             R.wc = *reinterpret_cast<const u32x4_t*>(crow + k0 / 2);
             const int g = k0 / T::GROUP;
             if constexpr (T::AFFINE) {
-                R.ws = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(srow)[g]);
-                R.wb = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(bro)[g]);
+                R.ws = reinterpret_cast<const uint16_t*>(srow)[g];
+                R.wb = reinterpret_cast<const uint16_t*>(bro)[g];
             } else {
-                R.ws = reinterpret_cast<const float*>(srow)[g];
-                R.wb = -8.f * R.ws;  // q = u - 8 after the xor below
+                R.ws = reinterpret_cast<const uint32_t*>(srow)[g];
             }
         };
         auto lstore = [&](const Regs& R, int s) {
+            const float ws = T::AFFINE ? bf16_bits_to_f32(R.ws) : __uint_as_float(R.ws);
+            const float wb = T::AFFINE ? bf16_bits_to_f32(R.wb) : -8.f * ws;  // sym: q = u - 8
             uint4* A = gsm + (s % GSTAGES) * STAGE;
             uint4* B = A + GBM * GCH;
 #pragma unroll
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint8_t* __restrict__ c
                 for (int b = 0; b < 4; ++b) {
                     const float e0 = (float)((lo >> (8 * b)) & 0xFFu);
                     const float e1 = (float)((hi >> (8 * b)) & 0xFFu);
-                    const bf16x2_t pr = {(__bf16)fmaf(e0, R.ws, R.wb), (__bf16)fmaf(e1, R.ws, R.wb)};
+                    const bf16x2_t pr = {(__bf16)fmaf(e0, ws, wb), (__bf16)fmaf(e1, ws, wb)};
                     o[b] = __builtin_bit_cast(uint32_t, pr);
                 }
                 B[gchunk(brow, 4 * bh + d)] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -150,25 +154,39 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint8_t* __restrict__ c
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     const int arow = wm * 128 + (lane & 31), brw = wn * 64 + (lane & 31), half = lane >> 5;
-    __syncthreads();  // prologue stages ready
-    for (int s = 0; s < ksteps; ++s) {
+    // Fragments are double-buffered across (step, kk): the reads for the next
+    // k slice are in flight while this slice's MFMAs issue. Stage s+1 is already
+    // complete during step s (the ring is 3 deep), so the pipeline runs across
+    // step boundaries; the barrier only has to follow the last read of stage s.
+    bf16x8_t af[2][4], bf[2][2];
+    auto frags = [&](int buf, int s, int kk) {
         const uint4* A = gsm + (s % GSTAGES) * STAGE;
         const uint4* B = A + GBM * GCH;
 #pragma unroll
-        for (int kk = 0; kk < GBK / 16; ++kk) {
-            bf16x8_t af[4], bf[2];
+        for (int i = 0; i < 4; ++i)
+            af[buf][i] = __builtin_bit_cast(bf16x8_t, A[gchunk(arow + 32 * i, 2 * kk + half)]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = __builtin_bit_cast(bf16x8_t, A[gchunk(arow + 32 * i, 2 * kk + half)]);
+        for (int j = 0; j < 2; ++j)
+            bf[buf][j] = __builtin_bit_cast(bf16x8_t, B[gchunk(brw + 32 * j, 2 * kk + half)]);
+    };
+    auto mfmas = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                bf[j] = __builtin_bit_cast(bf16x8_t, B[gchunk(brw + 32 * j, 2 * kk + half)]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bf[buf][j], acc[i][j], 0, 0, 0);
+    };
+    __syncthreads();  // prologue stages ready
+    frags(0, 0, 0);
+    for (int s = 0; s < ksteps; ++s) {
+        frags(1, s, 1);
+        mfmas(0);
+        frags(0, s, 2);
+        mfmas(1);
+        frags(1, s, 3);
+        mfmas(0);
+        if (s + 1 < ksteps) frags(0, s + 1, 0);
+        mfmas(1);
         __syncthreads();
     }
 
