@@ -37,6 +37,9 @@ LLAMA13B = [("wq", 5120, 5120), ("wk", 5120, 5120), ("wv", 5120, 5120), ("wo", 5
             ("gate", 13824, 5120), ("up", 13824, 5120), ("down", 5120, 13824)]
 
 
+GEMV_WAVE_SOURCES = ("common.hpp", "launch.hpp", "skinny.hpp", "gemv_wave.hpp", "gemv.hip")
+
+
 def weight_bytes(scheme: str, N: int, K: int) -> int:
     """Stored bytes of one quantized N x K matrix (codes + scales + biases)."""
     if scheme == "sym4_g128":
@@ -128,11 +131,51 @@ def base_line(a, metric, value, unit, ms, config, dtype="bf16"):
             "config": config}
 
 
-def hbm_roofline(kernel, nbytes, us):
+def hbm_roofline(kernel, nbytes, us, traffic=None):
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "bytes_per_launch": nbytes, "avg_launch_us": round(us, 3)}
+
+
+def calibration_copy(c, nbytes=1 << 30):
+    """A plain elementwise copy of known size (reads and writes nbytes once each),
+    run in the counter-collection mode so FETCH_SIZE / WRITE_SIZE can be scaled
+    by what they read for it."""
+    torch = c.torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=c.dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    return nbytes
+
+
+def kernel_sources_digest(files):
+    """sha256 over the sources a kernel is built from; a counter measurement is
+    only reported while the kernel is unchanged since it was taken."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "bit_weight_only_quantize_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(profile, files):
+    """HBM bytes per launch from a committed counter summary (a line
+    `traffic_bytes_per_launch: <int> sources_sha256: <hex>`), or None when the
+    summary is missing or the kernel has changed since."""
+    path = os.path.join(ROOT, "profiles", profile)
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m = __import__("re").search(r"traffic_bytes_per_launch:\s*(\d+)\s+sources_sha256:\s*([0-9a-f]{64})", text)
+    if not m or m.group(2) != kernel_sources_digest(files):
+        return None
+    return int(m.group(1))
 
 
 # ---------------------------------------------------------------- dense decode stacks
@@ -209,10 +252,12 @@ def run_llama(c: Ctx, a, big: bool):
     mats, xh, step, dominant, step_bytes, dom_bytes = decode_stack(c, shapes, scheme, layers, M, head)
     g_dom = c.graph(dominant)
     if a.dominant_only:
+        copy_bytes = calibration_copy(c)
         for _ in range(a.warmup + a.steps):
             g_dom.replay()
         c.torch.cuda.synchronize()
-        return {"dominant_only": True, "launches": layers * (a.warmup + a.steps)}
+        return {"dominant_only": True, "launches": layers * (a.warmup + a.steps),
+                "calibration_copy_bytes": copy_bytes}
     g_step = c.graph(step)
     ms = c.time_graph(g_step, a.steps, a.warmup)
     us_dom = c.time_graph(g_dom, max(4, a.steps // 2), 2) * 1e3 / layers
@@ -227,8 +272,11 @@ def run_llama(c: Ctx, a, big: bool):
     out["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
     out["tok_per_s"] = round(M / (ms * 1e-3), 1)
     out["step_bytes"] = step_bytes
+    traffic = None
+    if not big and M == 1 and layers == 32:
+        traffic = measured_traffic("gemv_wave_gate_up_llama7b_counters.md", GEMV_WAVE_SOURCES)
     out["roofline"] = hbm_roofline(f"gemv_wave_kernel (gate+up, 2 x {f}x{d} {scheme}, one launch)",
-                                   dom_bytes, us_dom)
+                                   dom_bytes, us_dom, traffic)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(mats[0], {K: v[0] for K, v in xh.items()}, M,
                                            a.cpu_seconds, shapes, scheme, layers)

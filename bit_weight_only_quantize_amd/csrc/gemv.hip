@@ -187,27 +187,38 @@ bool gemv_wave_ok(int scheme, int64_t K) {
     return VR >= 64 && wave_nv(VR) > 0;
 }
 
-template <int S, int NV, int R>
+// Row wavefronts stage the activations themselves (no staging wavefronts): a
+// workgroup is RW row wavefronts, each issuing its share of the activation
+// loads before its weight loads.
+template <int S, int NV, int R, int RW>
 static void go_wave(const GemvGroupArgs& a, int blocks, int K, const uint16_t* x, size_t lds,
                     hipStream_t st) {
-    constexpr int SW = 2;                 // staging wavefronts per workgroup
-    constexpr int XV = (NV + 1) / 2;      // activation vectors per staging lane
-    hipLaunchKernelGGL((gemv_wave_kernel<S, NV, R, XV, SW>), dim3(blocks), dim3(256 + 64 * SW), lds,
-                       st, a, K, x);
+    constexpr int XV = (NV + RW - 1) / RW;  // activation vectors per lane
+    hipLaunchKernelGGL((gemv_wave_kernel<S, NV, R, XV, RW>), dim3(blocks), dim3(64 * RW), lds, st,
+                       a, K, x);
 }
 
-template <int S, int R>
+template <int S, int R, int RW>
 static void pick_nv(int nv, const GemvGroupArgs& a, int blocks, int K, const uint16_t* x,
                     size_t lds, hipStream_t st) {
     switch (nv) {
-        case 1: go_wave<S, 1, R>(a, blocks, K, x, lds, st); break;
-        case 2: go_wave<S, 2, R>(a, blocks, K, x, lds, st); break;
-        case 3: go_wave<S, 3, R>(a, blocks, K, x, lds, st); break;
-        case 4: go_wave<S, 4, R>(a, blocks, K, x, lds, st); break;
-        case 6: go_wave<S, 6, R>(a, blocks, K, x, lds, st); break;
-        case 7: go_wave<S, 7, R>(a, blocks, K, x, lds, st); break;
-        default: go_wave<S, 8, R>(a, blocks, K, x, lds, st); break;
+        case 1: go_wave<S, 1, R, RW>(a, blocks, K, x, lds, st); break;
+        case 2: go_wave<S, 2, R, RW>(a, blocks, K, x, lds, st); break;
+        case 3: go_wave<S, 3, R, RW>(a, blocks, K, x, lds, st); break;
+        case 4: go_wave<S, 4, R, RW>(a, blocks, K, x, lds, st); break;
+        case 6: go_wave<S, 6, R, RW>(a, blocks, K, x, lds, st); break;
+        case 7: go_wave<S, 7, R, RW>(a, blocks, K, x, lds, st); break;
+        default: go_wave<S, 8, R, RW>(a, blocks, K, x, lds, st); break;
     }
+}
+
+template <int S>
+static void pick_shape(int R, int RW, int nv, const GemvGroupArgs& a, int blocks, int K,
+                       const uint16_t* x, size_t lds, hipStream_t st) {
+    if (R == 2 && RW == 4) pick_nv<S, 2, 4>(nv, a, blocks, K, x, lds, st);
+    else if (R == 2) pick_nv<S, 2, 8>(nv, a, blocks, K, x, lds, st);
+    else if (RW == 4) pick_nv<S, 1, 4>(nv, a, blocks, K, x, lds, st);
+    else pick_nv<S, 1, 8>(nv, a, blocks, K, x, lds, st);
 }
 
 hipError_t launch_gemv_wave(int scheme, int count, const void* const* codes,
@@ -218,8 +229,12 @@ hipError_t launch_gemv_wave(int scheme, int count, const void* const* codes,
     const int nv = wave_nv(VR);
     int64_t total_rows = 0;
     for (int i = 0; i < count; ++i) total_rows += N[i];
-    // 4 rows per wavefront once there are enough rows to keep every CU busy
-    const int R = total_rows >= 8192 ? 4 : 2;
+    // Measured on the decode shapes: two rows per wavefront pay off once a
+    // launch has enough rows to fill every CU several times over and rows are
+    // short; otherwise one. Small launches keep 4-wavefront workgroups so that
+    // more CUs get work.
+    const int R = (total_rows >= 12288 && nv <= 4) ? 2 : 1;
+    const int RW = ((R == 2 && nv <= 2) || total_rows < 4096) ? 4 : 8;
     GemvGroupArgs a{};
     int blocks = 0;
     for (int i = 0; i < count; ++i) {
@@ -229,25 +244,16 @@ hipError_t launch_gemv_wave(int scheme, int count, const void* const* codes,
         a.y[i] = y[i];
         a.N[i] = (int)N[i];
         a.tile_start[i] = blocks;
-        blocks += (int)((N[i] + 4 * R - 1) / (4 * R));
+        blocks += (int)((N[i] + RW * R - 1) / (RW * R));
     }
     a.tile_start[count] = blocks;
     a.count = count;
     if (blocks == 0) return hipSuccess;
     const size_t lds = (size_t)(K / 2 + VR) * 4;
     switch (scheme) {
-        case SYM4_G128:
-            if (R == 4) pick_nv<SYM4_G128, 4>(nv, a, blocks, (int)K, x, lds, st);
-            else pick_nv<SYM4_G128, 2>(nv, a, blocks, (int)K, x, lds, st);
-            break;
-        case AFF4_G64:
-            if (R == 4) pick_nv<AFF4_G64, 4>(nv, a, blocks, (int)K, x, lds, st);
-            else pick_nv<AFF4_G64, 2>(nv, a, blocks, (int)K, x, lds, st);
-            break;
-        default:
-            if (R == 4) pick_nv<AFF8_G64, 4>(nv, a, blocks, (int)K, x, lds, st);
-            else pick_nv<AFF8_G64, 2>(nv, a, blocks, (int)K, x, lds, st);
-            break;
+        case SYM4_G128: pick_shape<SYM4_G128>(R, RW, nv, a, blocks, (int)K, x, lds, st); break;
+        case AFF4_G64: pick_shape<AFF4_G64>(R, RW, nv, a, blocks, (int)K, x, lds, st); break;
+        default: pick_shape<AFF8_G64>(R, RW, nv, a, blocks, (int)K, x, lds, st); break;
     }
     return hipGetLastError();
 }

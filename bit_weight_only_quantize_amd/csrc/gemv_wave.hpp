@@ -5,15 +5,20 @@
 //   * a wavefront owns R whole rows, so row addresses are wave-uniform (SGPRs)
 //     and lane l reads 16-byte code vectors l, l+64, ... of each row: every load
 //     instruction moves 1 KiB of contiguous codes;
-//   * all code and scale loads of a lane are issued before anything else
-//     (single shot), so the whole matrix is in flight at once;
+//   * all code and scale loads of a lane are issued up front (single shot),
+//     right behind its share of the activations, so the whole matrix is in
+//     flight at once;
 //   * the activation vector is staged once per workgroup in LDS as bf16 pairs
-//     matching the unpack order, with per-vector sums for the offset removal,
-//     by dedicated staging wavefronts: vmcnt retires a wavefront's loads in
-//     order, so a row wavefront that also loaded activations would have to wait
-//     for all of its weight bytes before staging them. Row wavefronts issue only
-//     weight loads, meet the staging wavefronts at the barrier (no memory wait)
-//     and consume code vector j as soon as its own loads have retired;
+//     matching the unpack order, with per-vector sums for the offset removal.
+//     Every row wavefront stages a share of it and issues those loads before
+//     its weight loads: vmcnt retires a wavefront's loads in order, so waiting
+//     for the activations then does not wait for the weights, and the weight
+//     bytes stay in flight across the staging barrier. (Dedicated staging
+//     wavefronts were measured slower: their loads queue behind the row
+//     wavefronts' weight traffic and they take wave slots from row waves, so
+//     fewer workgroups fit on a CU at once.)
+//   * a code vector is consumed as soon as the wavefront's own loads for it
+//     have retired;
 //   * one v_and_or_b32 (affine) or v_bitop3_b32 (sym: and + xor with 0x43084308,
 //     which also moves the two's-complement code to q + 8) turns a nibble pair
 //     into a bf16 pair (128 + u); v_dot2_f32_bf16 accumulates in fp32;
@@ -65,7 +70,6 @@ __device__ __forceinline__ float wave_sum_to_lane63(float v) {
     return v;
 }
 
-// Workgroup = 4 row wavefronts + SW staging wavefronts (see the file comment).
 // D = sum over one 16-byte code vector of (BIAS_ELEM + u) * x, x given as the
 // staged bf16 pairs xp (XW dwords); 8-bit codes fold the high nibbles in as 16x.
 template <int S>
@@ -123,9 +127,13 @@ __device__ __forceinline__ void read_pairs(const uint32_t* xs, int v,
     }
 }
 
-template <int S, int NV, int R, int XV, int SW>
-__global__ __launch_bounds__(256 + 64 * SW) void gemv_wave_kernel(GemvGroupArgs a, int K,
-                                                                  const uint16_t* __restrict__ x) {
+// x is deliberately not __restrict__: loads from a read-only no-alias kernel
+// argument count as constant memory, which the compiler may schedule after the
+// weight loads regardless of any fence, and then the activation wait would
+// also wait for every weight byte.
+template <int S, int NV, int R, int XV, int RW>
+__global__ __launch_bounds__(64 * RW) void gemv_wave_kernel(GemvGroupArgs a, int K,
+                                                            const uint16_t* x) {
     using T = Traits<S>;
     using L = XLayout<S, 1>;
     constexpr int XW = L::XW;
@@ -141,21 +149,17 @@ __global__ __launch_bounds__(256 + 64 * SW) void gemv_wave_kernel(GemvGroupArgs 
     for (int q = 1; q < kMaxGroup; ++q)
         if (q < a.count && t >= a.tile_start[q]) i = q;
     const int N = a.N[i];
-    const int row0 = (t - a.tile_start[i]) * (4 * R) + wave * R;
+    const int row0 = (t - a.tile_start[i]) * (RW * R) + wave * R;
     const int64_t rowbytes = (int64_t)K * T::BITS / 8;
     const int64_t groups = K / T::GROUP;
     constexpr int SB = T::AFFINE ? 2 : 4;
 
     uint32_t* xs = smem;
     float* XS = reinterpret_cast<float*>(smem + K / 2);
-    if (wave >= 4) {
-        // staging wavefront(s): activations -> LDS, then done
-        XStage<S, XV, 64 * SW> xstage;
-        xstage.fetch(x, VR, threadIdx.x - 256);
-        xstage.commit(VR, xs, XS, threadIdx.x - 256);
-        __syncthreads();
-        return;
-    }
+    // this wavefront's share of the activations, loaded before any weight byte
+    XStage<S, XV, 64 * RW> xstage;
+    xstage.fetch(x, VR, threadIdx.x);
+    asm volatile("" ::: "memory");  // keep the weight loads behind these
 
     u32x4_t c[R][NV];
     float sc[R][NV], bi[R][NV];
@@ -181,6 +185,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void gemv_wave_kernel(GemvGroupArgs 
         }
     }
 
+    xstage.commit(VR, xs, XS, threadIdx.x);  // waits for the activations only
     __syncthreads();  // activations staged; weight loads still in flight
 
     const uint32_t MASK = opaque(0x000F000Fu);
