@@ -132,40 +132,30 @@ int w4a16_gemv_multi(const w4_matrix* const* Ws, int count, const uint16_t* x, i
     if (!x) return fail(W4_EINVAL, "null x");
     if (!aligned16(x)) return fail(W4_EALIGN, "x must be 16-byte aligned");
     hipStream_t st = (hipStream_t)stream;
-    if (M == 1 && w4::gemv_wave_ok(Ws[0]->scheme, K)) {
-        const void* c[4];
-        const void* sc[4];
-        const void* b[4];
-        int64_t N[4];
-        float* y[4];
-        int n = 0;
-        for (int i = 0; i < count; ++i) {
-            if (Ws[i]->N == 0) continue;
-            c[n] = Ws[i]->codes; sc[n] = Ws[i]->scale; b[n] = Ws[i]->bias; N[n] = Ws[i]->N;
-            y[n] = ys[i];
-            ++n;
-        }
-        if (n == 0) return ok();
-        return hip_status(w4::launch_gemv_wave(Ws[0]->scheme, n, c, sc, b, N, K, x, y, st),
-                          "gemv_multi launch");
+    // the non-empty members, for the kernels that serve several matrices per launch
+    const void* c[4];
+    const void* sc[4];
+    const void* b[4];
+    int64_t N[4];
+    float* y[4];
+    int n = 0;
+    for (int i = 0; i < count; ++i) {
+        if (Ws[i]->N == 0) continue;
+        c[n] = Ws[i]->codes; sc[n] = Ws[i]->scale; b[n] = Ws[i]->bias; N[n] = Ws[i]->N;
+        y[n] = ys[i];
+        ++n;
     }
-    if (w4::gemv_wave_mt_ok(Ws[0]->scheme, K, M)) {
-        const void* c[4];
-        const void* sc[4];
-        const void* b[4];
-        int64_t N[4];
-        float* y[4];
-        int n = 0;
-        for (int i = 0; i < count; ++i) {
-            if (Ws[i]->N == 0) continue;
-            c[n] = Ws[i]->codes; sc[n] = Ws[i]->scale; b[n] = Ws[i]->bias; N[n] = Ws[i]->N;
-            y[n] = ys[i];
-            ++n;
-        }
-        if (n == 0) return ok();
-        return hip_status(w4::launch_gemv_wave_mt(Ws[0]->scheme, n, c, sc, b, N, K, x, M, y, st),
+    if (n == 0) return ok();
+    const int scheme = Ws[0]->scheme;
+    if (M == 1 && w4::gemv_wave_ok(scheme, K))
+        return hip_status(w4::launch_gemv_wave(scheme, n, c, sc, b, N, K, x, y, st),
                           "gemv_multi launch");
-    }
+    if (w4::gemv_mfma_ok(scheme, K, M))
+        return hip_status(w4::launch_gemv_mfma(scheme, n, c, sc, b, N, K, x, M, y, st),
+                          "gemv_multi launch");
+    if (w4::gemv_wave_mt_ok(scheme, K, M))
+        return hip_status(w4::launch_gemv_wave_mt(scheme, n, c, sc, b, N, K, x, M, y, st),
+                          "gemv_multi launch");
     for (int i = 0; i < count; ++i) {
         if (Ws[i]->N == 0) continue;
         hipError_t e = w4::launch_gemv(Ws[i]->scheme, Ws[i]->codes, Ws[i]->scale, Ws[i]->bias,

@@ -360,10 +360,12 @@ hipError_t launch_gemv_wave_mt(int scheme, int count, const void* const* codes,
 hipError_t launch_gemv(int scheme, const void* codes, const void* scale, const void* bias,
                        int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                        hipStream_t st) {
-    if (gemv_wave_mt_ok(scheme, K, M))
-        return launch_gemv_wave_mt(scheme, 1, &codes, &scale, &bias, &N, K, x, M, &y, st);
     if (M == 1 && gemv_wave_ok(scheme, K))
         return launch_gemv_wave(scheme, 1, &codes, &scale, &bias, &N, K, x, &y, st);
+    if (gemv_mfma_ok(scheme, K, M))
+        return launch_gemv_mfma(scheme, 1, &codes, &scale, &bias, &N, K, x, M, &y, st);
+    if (gemv_wave_mt_ok(scheme, K, M))
+        return launch_gemv_wave_mt(scheme, 1, &codes, &scale, &bias, &N, K, x, M, &y, st);
     const GemvPlan p = plan_gemv(scheme, N, K, M);
     switch (scheme) {
         case SYM4_G128: return pick_mt<SYM4_G128>(p, codes, scale, bias, N, K, x, M, y, st);

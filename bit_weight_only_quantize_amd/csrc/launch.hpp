@@ -26,6 +26,13 @@ hipError_t launch_gemv_wave(int scheme, int count, const void* const* codes,
                             const void* const* scale, const void* const* bias, const int64_t* N,
                             int64_t K, const uint16_t* x, float* const* y, hipStream_t st);
 
+// 2 <= M <= 16, 4-bit schemes: unpacked codes feed bf16 MFMA from registers.
+bool gemv_mfma_ok(int scheme, int64_t K, int64_t M);
+hipError_t launch_gemv_mfma(int scheme, int count, const void* const* codes,
+                            const void* const* scale, const void* const* bias, const int64_t* N,
+                            int64_t K, const uint16_t* x, int64_t M, float* const* y,
+                            hipStream_t st);
+
 // 2 <= M <= 64, same design with token tiles staged in LDS.
 bool gemv_wave_mt_ok(int scheme, int64_t K, int64_t M);
 hipError_t launch_gemv_wave_mt(int scheme, int count, const void* const* codes,

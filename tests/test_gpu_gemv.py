@@ -45,6 +45,10 @@ def _run(scheme, N, K, M, name, rows=None, quantize_on_gpu=True):
     ("aff4_g64", 7, 192, 2),
     ("sym4_g128", 1, 128, 1),
     ("aff4_g64", 520, 13824, 2),
+    ("sym4_g128", 1000, 4096, 16),    # skinny MFMA path: full token tile, ragged rows
+    ("aff4_g64", 333, 768, 13),
+    ("aff4_g64", 17, 64, 6),          # one k step: most split-K wavefronts get none
+    ("sym4_g128", 31, 128, 11),
 ])
 def test_gemv_matches_oracle(scheme, N, K, M):
     _run(scheme, N, K, M, f"small.{scheme}.{N}x{K}")
