@@ -6,17 +6,19 @@ namespace w4 {
 
 bool gemv_mfma_ok(int scheme, int64_t K, int64_t M) {
     if (scheme != SYM4_G128 && scheme != AFF4_G64) return false;
-    const int kstep = scheme == SYM4_G128 ? MfmaStep<SYM4_G128>::KSTEP : MfmaStep<AFF4_G64>::KSTEP;
     const int group = scheme == SYM4_G128 ? 128 : 64;
-    return M >= 2 && M <= 16 && K >= kstep && K % kstep == 0 && K / group <= kMfmaMaxGroups;
+    return M >= 2 && M <= 16 && K >= group && K / group <= kMfmaMaxGroups;
 }
 
 template <int S, int RT, int WK>
 static void go_mfma(const GemvGroupArgs& a, int blocks, int K, int M, const uint16_t* x,
                     hipStream_t st) {
     const size_t lds = gemv_mfma_lds_bytes<S, RT, WK>(K);
-    hipLaunchKernelGGL((gemv_mfma_kernel<S, RT, WK, 2>), dim3(blocks), dim3(64 * WK), lds, st, a, K,
-                       M, x);
+    switch (mfma_slices(K / Traits<S>::GROUP)) {
+        case 1: hipLaunchKernelGGL((gemv_mfma_kernel<S, RT, WK, 2, 1>), dim3(blocks), dim3(64 * WK), lds, st, a, K, M, x); break;
+        case 2: hipLaunchKernelGGL((gemv_mfma_kernel<S, RT, WK, 2, 2>), dim3(blocks), dim3(64 * WK), lds, st, a, K, M, x); break;
+        default: hipLaunchKernelGGL((gemv_mfma_kernel<S, RT, WK, 2, 4>), dim3(blocks), dim3(64 * WK), lds, st, a, K, M, x); break;
+    }
 }
 
 template <int S>
@@ -24,12 +26,10 @@ static void pick_mfma(int RT, int WK, const GemvGroupArgs& a, int blocks, int K,
                       const uint16_t* x, hipStream_t st) {
     if (RT == 2) {
         if (WK == 8) go_mfma<S, 2, 8>(a, blocks, K, M, x, st);
-        else if (WK == 4) go_mfma<S, 2, 4>(a, blocks, K, M, x, st);
-        else go_mfma<S, 2, 2>(a, blocks, K, M, x, st);
+        else go_mfma<S, 2, 4>(a, blocks, K, M, x, st);
     } else {
         if (WK == 8) go_mfma<S, 1, 8>(a, blocks, K, M, x, st);
-        else if (WK == 4) go_mfma<S, 1, 4>(a, blocks, K, M, x, st);
-        else go_mfma<S, 1, 2>(a, blocks, K, M, x, st);
+        else go_mfma<S, 1, 4>(a, blocks, K, M, x, st);
     }
 }
 

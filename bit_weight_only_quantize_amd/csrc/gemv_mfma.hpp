@@ -10,10 +10,11 @@
 //     activations, B the 32 k x 16 weight rows; lane l holds weight row l % 16
 //     and k = 8 (l / 16) + 0..7 of B, and rows 4 (l / 16) + 0..3 (tokens) of D,
 //     so a lane's outputs all belong to one weight row and one group scale;
-//   * a step is one quantization group: 16 bytes of codes per lane (sym, 128
-//     weights x 16 rows per wavefront load) or 8 bytes (affine, 64 weights) --
-//     an MFMA's 32 k must not straddle two groups, and with four lanes per row
-//     an affine group of 64 only fits 8-byte lane loads;
+//   * a step is 128 weights of 16 rows: 16 bytes of codes per lane, one group
+//     (sym) or two (affine). An MFMA's 32 k must not straddle two groups: for
+//     affine, lanes 0-31 hold group A's words and lanes 32-63 group B's, so two
+//     v_permlane32_swap per lane regroup them into operand registers of a
+//     single group (the activation pieces are loaded in the matching k order);
 //   * a code word (8 nibbles) unpacks with the magic-exponent trick into four
 //     bf16 pairs (k, k+4) = 128 + u, so the activations are permuted the same
 //     way (v_perm_b32) and the offset is removed per group with the group's
@@ -23,9 +24,10 @@
 //     loads issued before the step's code loads) and are reused by the RT row
 //     tiles of a wavefront; the block's group scales are staged once in LDS
 //     (one coalesced pass instead of a scattered 2-4 byte load per step);
-//   * the WK wavefronts of a workgroup take contiguous step ranges of the same
-//     rows (split K, DEPTH steps in flight per wavefront) and their partial sums
-//     are added through LDS in a fixed order, so results are deterministic.
+//   * the WK wavefronts of a workgroup split K over the same rows, taking
+//     interleaved steps (the workgroup reads WK consecutive 64-byte pieces of
+//     every row at a time), DEPTH steps in flight each; their partial sums are
+//     added through LDS in a fixed order, so results are deterministic.
 #pragma once
 
 #include "common.hpp"
@@ -37,11 +39,25 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 template <int S>
 struct MfmaStep {
-    static constexpr int LB = S == SYM4_G128 ? 16 : 8;  // code bytes per lane per step
-    static constexpr int WPL = LB / 4;                  // code words per lane per step
-    static constexpr int KSTEP = 8 * LB;                // k per step (one group)
-    using code_t = typename std::conditional<LB == 16, u32x4_t, u32x2_t>::type;
+    static constexpr int GPS = S == SYM4_G128 ? 1 : 2;  // groups per 128-weight step
+    // k offset of activation piece d (8 weights, A operand of word d after the
+    // regrouping) for lane group g, relative to the step's first k
+    __device__ __forceinline__ static int xpiece(int g, int d) {
+        if constexpr (GPS == 1) return 32 * g + 8 * d;
+        // group A: own words of lanes 0-31, lanes 32-63 take lanes 0-31's third
+        // and fourth words; group B symmetric
+        return 32 * (g & 1) + 16 * (g >> 1) + 8 * (d & 1) + 64 * (d >> 1);
+    }
 };
+
+// Global-address-space view of a pointer: loads through it are global_load,
+// never flat_load (a flat load also counts against the LDS counter and makes
+// the compiler wait for every outstanding memory operation). Pointers picked
+// from a struct array with a runtime index lose the address space otherwise.
+template <typename V>
+__device__ __forceinline__ const __attribute__((address_space(1))) V* gmem(const void* p) {
+    return (const __attribute__((address_space(1))) V*)p;
+}
 
 // bf16x8 from four packed bf16 pairs
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -49,104 +65,137 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// At most kMfmaMaxGroups groups per row (the staging registers hold four
+// At most kMfmaMaxGroups groups per row (scales are staged in at most four
 // 64-group slices).
 constexpr int kMfmaMaxGroups = 256;
 
+// 64-group slices to stage per row: 1, 2 or 4.
+inline int mfma_slices(int64_t groups) { return groups <= 64 ? 1 : (groups <= 128 ? 2 : 4); }
+
+// One row tile of 16 weight rows: rows row0 .. row0+15 of an N x K matrix
+// (rows past N are read clamped and their outputs dropped by the caller).
+struct MfmaTile {
+    const uint8_t* codes;
+    const uint8_t* scale;
+    const uint8_t* bias;
+    int row0, N;
+};
+
 // LDS: the workgroup's scales as [group][row] words (affine: bf16 scale in the
 // low half, bf16 bias in the high half), later reused for the split-K sums.
-template <int S, int RT, int WK>
+template <int S, int RT, int WK, int WR = 1>
 size_t gemv_mfma_lds_bytes(int64_t K) {
-    const size_t scales = (size_t)(K / Traits<S>::GROUP) * 16 * RT * 4;
-    const size_t red = (size_t)(WK > 1 ? WK - 1 : 1) * RT * 4 * 64 * 4;
+    const size_t scales = ((size_t)(K / Traits<S>::GROUP) * 16 * RT * WR + 1) * 4;  // + trash word
+    const size_t red = (size_t)(WK > 1 ? WK - 1 : 1) * WR * RT * 4 * 64 * 4;
     return scales > red ? scales : red;
 }
 
-template <int S, int RT, int WK, int DEPTH>
-__global__ __launch_bounds__(64 * WK) void gemv_mfma_kernel(GemvGroupArgs a, int K, int M,
-                                                            const uint16_t* x) {
+// The workgroup's product of WR x RT row tiles with up to 16 activation rows
+// over the whole K. Wavefront w works on tiles tl[(w % WR) * RT ..] over the
+// w / WR-th of WK contiguous step ranges. Every wavefront must call it (it
+// synchronizes); the split-K sums end up in the acc of the wavefronts with
+// w < WR (the others hold partial sums). Lane l's activation row starts at
+// element xoff of the wave-uniform xbase (tokens past the valid ones point at a
+// valid row; the caller drops their outputs).
+template <int S, int RT, int WK, int DEPTH, int WR, int SL, bool IL = true>
+__device__ __forceinline__ void mfma_tiles(const MfmaTile (&tl)[WR * RT], int K,
+                                           const uint16_t* xbase, uint32_t xoff, uint32_t* lds,
+                                           f32x4_t (&acc)[RT]) {
     using T = Traits<S>;
     using P = MfmaStep<S>;
-    using code_t = typename P::code_t;
-    constexpr int WPL = P::WPL;
-    constexpr int ROWS = 16 * RT;
-    extern __shared__ __align__(16) uint32_t lds[];
+    constexpr int GPS = P::GPS;
+    constexpr int NW = WR * WK;       // wavefronts
+    constexpr int ROWS = 16 * RT * WR;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = wave % WR, wk = wave / WR;
     const int g = lane >> 4, c16 = lane & 15;
+    const int groups = K / T::GROUP;
+    const int steps = (groups + GPS - 1) / GPS;  // an odd affine count ends with a half step
+    const bool odd = GPS == 2 && (groups & 1);
+    // wavefront wk's steps: wk, wk + WK, ... (interleaved, so that the
+    // workgroup reads WK consecutive 64-byte pieces of every row at a time) or
+    // one contiguous range
+    const int J = (steps + WK - 1) / WK;
+    const int nj = IL ? (wk < steps ? (steps - 1 - wk) / WK + 1 : 0) : max(0, min(J, steps - wk * J));
+    auto step_of = [&](int j) {  // clamped: loads past the last step re-load it
+        const int jj = min(j, max(nj - 1, 0));
+        return min(IL ? wk + jj * WK : wk * J + jj, steps - 1);
+    };
 
-    const int t = blockIdx.x;
-    int i = 0;
-#pragma unroll
-    for (int q = 1; q < kMaxGroup; ++q)
-        if (q < a.count && t >= a.tile_start[q]) i = q;
-    const int N = a.N[i];
-    const int row0 = (t - a.tile_start[i]) * ROWS;
-    const int groups = K / T::GROUP;  // == steps
-    const int J = (groups + WK - 1) / WK;
-    const int s0 = wave * J;
-    const int s1 = min(s0 + J, groups);
-
-    // 1. the block's scales (and biases) -> LDS, loads issued first
-    constexpr int SR = (ROWS + WK - 1) / WK;  // rows staged per wavefront
-    const int sgl = (groups + 63) / 64;       // group slices per row
-    uint32_t sv[SR][4];
+    // 1. the tiles' scales (and biases) -> LDS, loads issued first; SL slices
+    //    of 64 groups per row (SL * 64 >= groups): one coalesced pass instead of
+    //    scattered 2-4 byte loads every step. Every load is unconditional
+    //    (indices clamped) so that no branch makes the compiler's wait counts
+    //    conservative.
+    constexpr int SR = (ROWS + NW - 1) / NW;  // rows staged per wavefront
+    uint32_t sv[SR][SL];
 #pragma unroll
     for (int k = 0; k < SR; ++k) {
-        const int r = wave + WK * k;
-        const int n = min(row0 + min(r, ROWS - 1), N - 1);
+        const int r = min(wave + NW * k, ROWS - 1);
+        const MfmaTile& tt = tl[r / 16];
+        const int n = min(tt.row0 + r % 16, tt.N - 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j >= sgl) break;  // uniform
+        for (int j = 0; j < SL; ++j) {
             const int gi = min(lane + 64 * j, groups - 1);
             const uint32_t e = (uint32_t)n * (uint32_t)groups + (uint32_t)gi;
             if constexpr (T::AFFINE)
-                sv[k][j] = (uint32_t)reinterpret_cast<const uint16_t*>(a.scale[i])[e] |
-                           ((uint32_t)reinterpret_cast<const uint16_t*>(a.bias[i])[e] << 16);
+                sv[k][j] = (uint32_t)gmem<uint16_t>(tt.scale)[e] |
+                           ((uint32_t)gmem<uint16_t>(tt.bias)[e] << 16);
             else
-                sv[k][j] = reinterpret_cast<const uint32_t*>(a.scale[i])[e];
+                sv[k][j] = gmem<uint32_t>(tt.scale)[e];
         }
     }
     asm volatile("" ::: "memory");  // keep the step loads behind these
 
-    // 2. per-lane bases: 32-bit offsets from wave-uniform pointers
-    const uint8_t* cbase = a.codes[i];
+    // 2. per-lane code offsets from this wavefront's tiles' (uniform) bases
+    const uint8_t* cb[RT];
     uint32_t coff[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const int n = min(row0 + 16 * rt + c16, N - 1);
-        coff[rt] = (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(g * P::LB);
+        const MfmaTile& tt = tl[wr * RT + rt];
+        const int n = min(tt.row0 + c16, tt.N - 1);
+        cb[rt] = tt.codes;
+        coff[rt] = (uint32_t)n * (uint32_t)(K / 2);
     }
-    // tokens past M re-read row M-1; their outputs are never stored
-    const uint32_t xoff = (uint32_t)min(c16, M - 1) * (uint32_t)K + (uint32_t)(g * 2 * P::LB);
 
     struct Buf {
-        u32x4_t xv[WPL];
-        code_t c[RT];
+        u32x4_t xv[4];
+        u32x4_t c[RT];
     };
     auto load = [&](Buf& B, int s) {
+        // a half step (odd affine group count, last step) has no group B: its
+        // loads are redirected into group A (results unused), never past a row
+        const bool half = odd && s == steps - 1;
+        const int gl = half ? (g & 1) : g;
         // activations first: in-order vmcnt then never waits for code bytes
 #pragma unroll
-        for (int d = 0; d < WPL; ++d)
-            B.xv[d] = *reinterpret_cast<const u32x4_t*>(x + xoff + (uint32_t)s * P::KSTEP + 8 * d);
+        for (int d = 0; d < 4; ++d)
+            B.xv[d] = *gmem<u32x4_t>(xbase + (xoff + (uint32_t)s * 128 +
+                                              (uint32_t)P::xpiece(g, half ? (d & 1) : d)));
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-            B.c[rt] = *reinterpret_cast<const code_t*>(cbase + coff[rt] + (uint32_t)s * (P::KSTEP / 2));
+        for (int rt = 0; rt < RT; ++rt) {
+            B.c[rt] = *gmem<u32x4_t>(cb[rt] + coff[rt] + (uint32_t)s * 64 + 16 * gl);
+        }
     };
 
+    // DEPTH steps in flight. Loads are unconditional (a wavefront past its
+    // last step re-loads that step, results unused): a load under a branch
+    // would make the compiler wait for every outstanding load, prefetched
+    // steps included.
     Buf buf[DEPTH];
 #pragma unroll
-    for (int p = 0; p < DEPTH - 1; ++p)
-        if (s0 + p < s1) load(buf[p], s0 + p);
+    for (int p = 0; p < DEPTH - 1; ++p) load(buf[p], step_of(p));
 
-    // scales land in LDS while the first steps' bytes are in flight
+    // scales land in LDS while the first steps' bytes are in flight; staged
+    // values past the rows or groups go to a trash word (no branch, see above)
 #pragma unroll
     for (int k = 0; k < SR; ++k) {
-        const int r = wave + WK * k;
-        if (r < ROWS) {
+        const int r = wave + NW * k;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (j < sgl && lane + 64 * j < groups) lds[(lane + 64 * j) * ROWS + r] = sv[k][j];
+        for (int j = 0; j < SL; ++j) {
+            const int gi = lane + 64 * j;
+            lds[r < ROWS && gi < groups ? gi * ROWS + r : groups * ROWS] = sv[k][j];
         }
     }
     __syncthreads();
@@ -155,83 +204,139 @@ __global__ __launch_bounds__(64 * WK) void gemv_mfma_kernel(GemvGroupArgs a, int
     const uint32_t MAGIC = unpack_magic<S>();
     const uint32_t ONE2 = 0x3F803F80u;  // bf16 pair (1, 1)
     const bf16x8_t ONES = as_bf16x8(ONE2, ONE2, ONE2, ONE2);
-    f32x4_t acc[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    auto unpack = [&](uint32_t w) {
+        auto pair = [&](uint32_t v) {
+            return S == SYM4_G128 ? ((v & MASK) ^ MAGIC) : ((v & MASK) | MAGIC);
+        };
+        return as_bf16x8(pair(w), pair(w >> 4), pair(w >> 8), pair(w >> 12));
+    };
     auto compute = [&](const Buf& B, int s) {
-        uint32_t sw[RT];
+        const bool half = odd && s == steps - 1;
+        uint32_t sw[RT][GPS];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) sw[rt] = lds[s * ROWS + 16 * rt + c16];
-        bf16x8_t A[WPL];
-        f32x4_t DX = {0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int d = 0; d < WPL; ++d) {
+            for (int q = 0; q < GPS; ++q)
+                sw[rt][q] = lds[min(GPS * s + q, groups - 1) * ROWS + 16 * (wr * RT + rt) + c16];
+        bf16x8_t A[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
             const u32x4_t e = B.xv[d];  // (x0,x1) (x2,x3) (x4,x5) (x6,x7) -> (x0,x4) (x1,x5) ...
             A[d] = as_bf16x8(__builtin_amdgcn_perm(e[2], e[0], 0x05040100u),
                              __builtin_amdgcn_perm(e[2], e[0], 0x07060302u),
                              __builtin_amdgcn_perm(e[3], e[1], 0x05040100u),
                              __builtin_amdgcn_perm(e[3], e[1], 0x07060302u));
-            DX = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[d], ONES, DX, 0, 0, 0);
+        }
+        // group activation sums, one per group of the step, in the D layout
+        f32x4_t DX[GPS];
+#pragma unroll
+        for (int q = 0; q < GPS; ++q) {
+            DX[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (q == 1 && half) continue;
+#pragma unroll
+            for (int d = 4 / GPS * q; d < 4 / GPS * (q + 1); ++d)
+                DX[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[d], ONES, DX[q], 0, 0, 0);
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            f32x4_t D = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int d = 0; d < WPL; ++d) {
-                const uint32_t w = B.c[rt][d];
-                auto pair = [&](uint32_t v) {
-                    return S == SYM4_G128 ? ((v & MASK) ^ MAGIC) : ((v & MASK) | MAGIC);
-                };
-                const bf16x8_t Bw = as_bf16x8(pair(w), pair(w >> 4), pair(w >> 8), pair(w >> 12));
-                D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[d], Bw, D, 0, 0, 0);
-            }
-            float sc, corr;
-            if constexpr (T::AFFINE) {
-                sc = __uint_as_float(sw[rt] << 16);
-                corr = fmaf(-T::BIAS, sc, __uint_as_float(sw[rt] & 0xFFFF0000u));
-            } else {
-                sc = __uint_as_float(sw[rt]);
-                corr = -T::BIAS * sc;
+            uint32_t w[4] = {B.c[rt][0], B.c[rt][1], B.c[rt][2], B.c[rt][3]};
+            if constexpr (GPS == 2) {
+                // lanes 0-31 hold group A, lanes 32-63 group B: swap the upper
+                // half of words 0/1 with the lower half of words 2/3
+                const auto p02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+                const auto p13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+                w[0] = p02[0]; w[2] = p02[1];
+                w[1] = p13[0]; w[3] = p13[1];
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[rt][r] = fmaf(corr, DX[r], fmaf(sc, D[r], acc[rt][r]));
+            for (int q = 0; q < GPS; ++q) {
+                if (q == 1 && half) continue;
+                f32x4_t D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int d = 4 / GPS * q; d < 4 / GPS * (q + 1); ++d)
+                    D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[d], unpack(w[d]), D, 0, 0, 0);
+                float sc, corr;
+                if constexpr (T::AFFINE) {
+                    sc = __uint_as_float(sw[rt][q] << 16);
+                    corr = fmaf(-T::BIAS, sc, __uint_as_float(sw[rt][q] & 0xFFFF0000u));
+                } else {
+                    sc = __uint_as_float(sw[rt][q]);
+                    corr = -T::BIAS * sc;
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[rt][r] = fmaf(corr, DX[q][r], fmaf(sc, D[r], acc[rt][r]));
+            }
         }
     };
 
-    // DEPTH steps in flight: step s + DEPTH - 1 is loaded while step s is
-    // computed; the ring is unrolled so every buffer index is static
-    for (int s = s0; s < s1; s += DEPTH) {
+    // step s + DEPTH - 1 is loaded while step s is computed; the ring is
+    // unrolled so every buffer index is static
+    for (int j0 = 0; j0 < nj; j0 += DEPTH) {
 #pragma unroll
         for (int u = 0; u < DEPTH; ++u) {
-            const int step = s + u;
-            if (step < s1) {
-                if (step + DEPTH - 1 < s1) load(buf[(u + DEPTH - 1) % DEPTH], step + DEPTH - 1);
-                compute(buf[u], step);
-            }
+            const int j = j0 + u;
+            load(buf[(u + DEPTH - 1) % DEPTH], step_of(j + DEPTH - 1));
+            // keep the prefetch ahead of this step's compute: left alone, the
+            // scheduler sinks the loads below the MFMAs and the loop degenerates
+            // into load, wait, compute
+            __builtin_amdgcn_sched_barrier(0);
+            if (j < nj) compute(buf[u], step_of(j));
         }
     }
 
-    // split-K partial sums: waves 1.. hand theirs to wave 0 through LDS (the
-    // scale area, free once every wavefront is past its last step)
+    // split-K partial sums: wavefronts wk > 0 hand theirs to wavefront wr
+    // through LDS (the scale area, free once every wavefront is past its last
+    // step), added in a fixed order
     if constexpr (WK > 1) {
         __syncthreads();
         float* red = reinterpret_cast<float*>(lds);
-        if (wave > 0) {
+        if (wk > 0) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) red[(((wave - 1) * RT + rt) * 4 + r) * 64 + lane] = acc[rt][r];
+                for (int r = 0; r < 4; ++r)
+                    red[((((wk - 1) * WR + wr) * RT + rt) * 4 + r) * 64 + lane] = acc[rt][r];
         }
         __syncthreads();
-        if (wave > 0) return;
+        if (wk == 0) {
 #pragma unroll
-        for (int w = 0; w < WK - 1; ++w)
+            for (int w = 0; w < WK - 1; ++w)
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+                for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[rt][r] += red[((w * RT + rt) * 4 + r) * 64 + lane];
+                    for (int r = 0; r < 4; ++r)
+                        acc[rt][r] += red[(((w * WR + wr) * RT + rt) * 4 + r) * 64 + lane];
+        }
     }
+}
+
+// Dense decode GEMM: RT row tiles of one matrix of the group per workgroup.
+template <int S, int RT, int WK, int DEPTH, int SL>
+__global__ __launch_bounds__(64 * WK) void gemv_mfma_kernel(GemvGroupArgs a, int K, int M,
+                                                            const uint16_t* x) {
+    extern __shared__ __align__(16) uint32_t lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, c16 = lane & 15;
+    const int t = blockIdx.x;
+    int i = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxGroup; ++q)
+        if (q < a.count && t >= a.tile_start[q]) i = q;
+    const int N = a.N[i];
+    const int row0 = (t - a.tile_start[i]) * (16 * RT);
+    MfmaTile tl[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) tl[rt] = MfmaTile{a.codes[i], a.scale[i], a.bias[i], row0 + 16 * rt, N};
+    // tokens past M re-read row M-1; their outputs are never stored
+    const uint32_t xoff = (uint32_t)min(c16, M - 1) * (uint32_t)K;
+    f32x4_t acc[RT];
+    mfma_tiles<S, RT, WK, DEPTH, 1, SL>(tl, K, x, xoff, lds, acc);
+    if (wave != 0) return;
     float* y = a.y[i];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {

@@ -60,8 +60,11 @@ struct MoeMats {
     const void* sdown[3];
 };
 
+// Routed (token, slot) pairs per call: M <= 256 tokens times top_k <= 32.
+constexpr int kMoeMaxPairs = 256 * 32;
+
 struct MoeWorkspace {  // byte offsets inside the caller's workspace
-    size_t offsets, active, n_active, pairs, h, hs, part, sout, total;
+    size_t work, pairs, h, hs, part, sout, total;
 };
 MoeWorkspace moe_workspace_layout(int64_t M, int k, int64_t E, int64_t D, int64_t F, int64_t Fs);
 

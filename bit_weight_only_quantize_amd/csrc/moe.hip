@@ -9,8 +9,10 @@
 // Route:  router GEMV (fp32 logits) -> one wavefront per token: softmax over all
 //         E raw logits, top-k by logit (ties to the lower index), weights = the
 //         selected probabilities (not renormalized).
-// Experts: bucket (token, slot) pairs by expert (stable, deterministic) ->
-//         gate/up pass (both rows of an n in one lane; epilogue
+// Experts: one token: a two-launch fast path (moe1.hpp). Several tokens:
+//         bucket (token, slot) pairs by expert (stable, deterministic) ->
+//         gate/up pass on the matrix cores (a gate tile and an up tile of the
+//         same rows, so a lane holds g and u of one (token, f); epilogue
 //         h = bf16(gelu_tanh(g) * u)) over active experts + the shared expert ->
 //         down pass into per-pair partial rows + the shared output ->
 //         combine y = shared + sum_j w_j * partial_j in a fixed order.
@@ -19,6 +21,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "gemv_mfma.hpp"
 #include "skinny.hpp"
 #include "moe1.hpp"
 
@@ -71,43 +74,63 @@ hipError_t launch_route(int scheme, const void* codes, const void* scale, const 
 }
 
 // ---------------------------------------------------------------- bucketing
-// Single workgroup. Pair p = m * k + j (token m, slot j). For every expert e, the
-// pairs routed to it in increasing p; experts with at least one pair listed in
-// increasing e. Ids outside [0, E) are ignored.
+// Single workgroup. Pair p = m * k + j (token m, slot j), P <= kMoeMaxPairs.
+// For every expert e, the pairs routed to it in increasing p; the experts with
+// at least one pair get work descriptors {e, first pair index, pair count} in
+// increasing e, the remaining descriptors up to `slots` are {-1, 0, 0}. Ids
+// outside [0, E) are ignored. Counts use LDS integer atomics (exact in any
+// order); the placement is sequential per expert, so the output is
+// deterministic.
 __global__ __launch_bounds__(1024) void moe_bucket_kernel(const int32_t* __restrict__ ids, int P,
-                                                          int E, int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ active,
-                                                          int32_t* __restrict__ n_active,
+                                                          int E, int slots, int4* __restrict__ work,
                                                           int32_t* __restrict__ pairs) {
-    __shared__ int cnt[1024];
-    __shared__ int off[1025];
-    __shared__ int act[1025];
+    __shared__ int sid[kMoeMaxPairs];
+    __shared__ int cnt[1024], off[1024], act[1024];
+    __shared__ int n_act;
     const int t = threadIdx.x;
-    for (int e = t; e < E; e += blockDim.x) {
-        int c = 0;
-        for (int p = 0; p < P; ++p) c += ids[p] == e;
-        cnt[e] = c;
+    for (int p = t; p < P; p += blockDim.x) {
+        const int v = ids[p];
+        sid[p] = v >= 0 && v < E ? v : -1;
     }
+    for (int e = t; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
-    if (t == 0) {  // exclusive scans (E <= 1024: a single pass is cheap)
-        int o = 0, a = 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = o;
-            o += cnt[e];
-            if (cnt[e]) act[a++] = e;
+    for (int p = t; p < P; p += blockDim.x)
+        if (sid[p] >= 0) atomicAdd(&cnt[sid[p]], 1);
+    __syncthreads();
+    if (t < 64) {  // exclusive scans of counts and of active flags: 16 experts per lane
+        int c[16], loc = 0, la = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int e = 16 * t + i;
+            c[i] = e < E ? cnt[e] : 0;
+            loc += c[i];
+            la += c[i] > 0;
         }
-        off[E] = o;
-        act[E] = a;
+        int incl = loc, inca = la;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d), oa = __shfl_up(inca, d);
+            if (t >= d) { incl += o; inca += oa; }
+        }
+        int o = incl - loc, oa = inca - la;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int e = 16 * t + i;
+            if (e < E) { off[e] = o; act[e] = c[i] > 0 ? oa : -1; }
+            o += c[i];
+            oa += c[i] > 0;
+        }
+        if (t == 63) n_act = inca;
     }
     __syncthreads();
-    for (int e = t; e <= E; e += blockDim.x) offsets[e] = off[e];
-    for (int i = t; i < E; i += blockDim.x) active[i] = i < act[E] ? act[i] : -1;
-    if (t == 0) *n_active = act[E];
     for (int e = t; e < E; e += blockDim.x) {
+        if (act[e] < 0) continue;
+        work[act[e]] = make_int4(e, off[e], cnt[e], 0);
         int w = off[e];
         for (int p = 0; p < P; ++p)
-            if (ids[p] == e) pairs[w++] = p;
+            if (sid[p] == e) pairs[w++] = p;
     }
+    for (int s = n_act + t; s < slots; s += blockDim.x) work[s] = make_int4(-1, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- expert passes
@@ -124,9 +147,7 @@ struct MoeArgs {
     int has_shared;
     int M, k, E;
     const uint16_t* x;        // [M][D]
-    const int32_t* offsets;   // [E+1]
-    const int32_t* active;    // [E]
-    const int32_t* n_active;  // [1]
+    const int4* work;         // [amax] {expert, first pair, pair count} or {-1, ..}
     const int32_t* pairs;     // [M*k]
     uint16_t* h;              // [M*k][F] bf16
     uint16_t* hs;             // [M][Fs] bf16
@@ -136,167 +157,118 @@ struct MoeArgs {
     int tiles_r, tiles_s;     // row tiles per routed slot / for the shared expert
 };
 
+// Expert passes for M > 1 on the skinny MFMA core: a workgroup owns 16 * WR
+// (gate, up) rows or 32 * WR down rows of one active expert (or of the shared
+// expert, whose "bucket" is every token), WR wavefronts across its rows times
+// WK splitting K, and takes the expert's tokens 16 at a time as the activation
+// rows, so each expert's weights are read once per token tile.
+
 template <int S>
-__device__ __forceinline__ void row_ptrs(const MoeMat& W, int e, int n, const uint8_t*& c,
-                                         const uint8_t*& s, const uint8_t*& b) {
-    using T = Traits<S>;
-    const int64_t groups = W.K / T::GROUP;
-    constexpr int SB = T::AFFINE ? 2 : 4;
-    c = W.codes + e * W.stride_c + (int64_t)n * W.K * T::BITS / 8;
-    s = W.scale + e * W.stride_s + (int64_t)n * groups * SB;
-    b = T::AFFINE ? W.bias + e * W.stride_s + (int64_t)n * groups * 2 : nullptr;
+__device__ __forceinline__ MfmaTile expert_tile(const MoeMat& W, int e, int row0) {
+    return MfmaTile{W.codes + e * W.stride_c, W.scale + e * W.stride_s,
+                    Traits<S>::AFFINE ? W.bias + e * W.stride_s : nullptr, row0, W.N};
 }
 
-// gate/up pass: one lane slot owns (gate row n, up row n); block = 4 * (64/LPR) n.
-template <int S, int MT, int LPR, int V>
-__global__ __launch_bounds__(256) void moe_gate_up_kernel(MoeArgs a) {
-    using Core = SkinnyCore<S, MT, LPR, V, 2>;
-    constexpr int RSW = 64 / LPR, NPB = 4 * RSW;
-    extern __shared__ __align__(16) uint32_t smem[];
-    __shared__ int tok[MT];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int slot = lane / LPR, sl = lane % LPR;
-    int bid = blockIdx.x, e, n0, count, first;
-    const MoeMat *G, *U;
+// gate/up: wavefront w gets tiles (gate rows f0 + 16w.., up rows f0 + 16w..), so
+// a lane holds g and u of the same (token, f) and writes h = bf16(gelu(g) * u).
+template <int S, int WR, int WK, int SL>
+__global__ __launch_bounds__(64 * WR * WK) void moe_gate_up_kernel(MoeArgs a) {
+    extern __shared__ __align__(16) uint32_t lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, c16 = lane & 15;
+    const int bid = blockIdx.x;
+    int e = 0, f0, count, first = 0;
     bool shared;
     if (bid < a.amax * a.tiles_r) {
-        const int s = bid / a.tiles_r;
-        if (s >= *a.n_active) return;
-        e = a.active[s];
-        n0 = (bid % a.tiles_r) * NPB;
-        first = a.offsets[e];
-        count = a.offsets[e + 1] - first;
-        G = &a.gate;
-        U = &a.up;
+        const int4 w = a.work[bid / a.tiles_r];
+        if (w.x < 0) return;  // whole workgroup
+        e = w.x;
+        f0 = (bid % a.tiles_r) * 16 * WR;
+        first = w.y;
+        count = w.z;
         shared = false;
     } else {
-        e = 0;
-        n0 = (bid - a.amax * a.tiles_r) * NPB;
-        first = 0;
+        f0 = (bid - a.amax * a.tiles_r) * 16 * WR;
         count = a.M;
-        G = &a.sgate;
-        U = &a.sup;
         shared = true;
     }
-    const int F = G->N, D = G->K;
-    const int n = n0 + wave * RSW + slot;
-    const int nl = n < F ? n : F - 1;
-    Core core;
-    core.VR = D / Traits<S>::KV;
-    core.sl = sl;
-    row_ptrs<S>(*G, e, nl, core.crow[0], core.srow[0], core.brow[0]);
-    row_ptrs<S>(*U, e, nl, core.crow[1], core.srow[1], core.brow[1]);
-    uint32_t* xs = smem;
-    float* XS = reinterpret_cast<float*>(smem + MT * (D / 2));
-    typename Core::Buf A, B;
-    for (int t0 = 0; t0 < count; t0 += MT) {
-        const int mt = min(MT, count - t0);
-        core.load(A, 0);
-        if (t0) __syncthreads();
-        if (threadIdx.x < MT) {
-            const int i = t0 + (int)threadIdx.x < count ? t0 + threadIdx.x : t0;
-            tok[threadIdx.x] = shared ? i : a.pairs[first + i] / a.k;
-        }
-        __syncthreads();
-        stage_x<S, MT, V, 256>(a.x, D, tok, mt, D, xs, XS);
-        __syncthreads();
-        float acc[2][MT];
+    const MoeMat& G = shared ? a.sgate : a.gate;
+    const MoeMat& U = shared ? a.sup : a.up;
+    const int F = G.N, D = G.K;
+    MfmaTile tl[2 * WR];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[0][m] = acc[1][m] = 0.f;
-        core.run(A, B, xs, XS, D / 2, acc);
+    for (int w = 0; w < WR; ++w) {
+        tl[2 * w] = expert_tile<S>(G, e, f0 + 16 * w);
+        tl[2 * w + 1] = expert_tile<S>(U, e, f0 + 16 * w);
+    }
+    for (int t0 = 0; t0 < count; t0 += 16) {
+        if (t0) __syncthreads();  // LDS reuse across token tiles
+        const int t = min(t0 + c16, count - 1);
+        const int tok = shared ? t : a.pairs[first + t] / a.k;
+        f32x4_t acc[2];
+        mfma_tiles<S, 2, WK, 2, WR, SL>(tl, D, a.x, (uint32_t)tok * (uint32_t)D, lds, acc);
+        const int f = f0 + 16 * (wave % WR) + c16;
+        if (wave < WR && f < F) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            acc[0][m] = group_sum<LPR>(acc[0][m]);
-            acc[1][m] = group_sum<LPR>(acc[1][m]);
-        }
-        if (sl == 0 && n < F) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                if (m < mt) {
-                    const uint16_t hv = (uint16_t)f32_to_bf16_rne(gelu_tanh(acc[0][m]) * acc[1][m]);
-                    if (shared) a.hs[(int64_t)(t0 + m) * F + n] = hv;
-                    else a.h[(int64_t)a.pairs[first + t0 + m] * F + n] = hv;
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int m = t0 + 4 * g + r;
+                if (m >= count) continue;
+                const uint16_t hv = (uint16_t)f32_to_bf16_rne(gelu_tanh(acc[0][r]) * acc[1][r]);
+                if (shared) a.hs[(int64_t)m * F + f] = hv;
+                else a.h[(int64_t)a.pairs[first + m] * F + f] = hv;
             }
         }
     }
 }
 
-// down pass: rows n of W_down[e] against the h rows of the expert's pairs.
-template <int S, int MT, int LPR, int V, int R>
-__global__ __launch_bounds__(256) void moe_down_kernel(MoeArgs a) {
-    using Core = SkinnyCore<S, MT, LPR, V, R>;
-    constexpr int RSW = 64 / LPR, NPB = 4 * RSW * R;
-    extern __shared__ __align__(16) uint32_t smem[];
-    __shared__ int tok[MT];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int slot = lane / LPR, sl = lane % LPR;
-    int bid = blockIdx.x, e, n0, count, first;
-    const MoeMat* W;
+// down: wavefront w gets rows n0 + 32w .. of W_down[e] (two tiles) against the
+// h rows of the expert's pairs.
+template <int S, int WR, int WK, int SL>
+__global__ __launch_bounds__(64 * WR * WK) void moe_down_kernel(MoeArgs a) {
+    extern __shared__ __align__(16) uint32_t lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, c16 = lane & 15;
+    const int bid = blockIdx.x;
+    int e = 0, n0, count, first = 0;
     bool shared;
     if (bid < a.amax * a.tiles_r) {
-        const int s = bid / a.tiles_r;
-        if (s >= *a.n_active) return;
-        e = a.active[s];
-        n0 = (bid % a.tiles_r) * NPB;
-        first = a.offsets[e];
-        count = a.offsets[e + 1] - first;
-        W = &a.down;
+        const int4 w = a.work[bid / a.tiles_r];
+        if (w.x < 0) return;  // whole workgroup
+        e = w.x;
+        n0 = (bid % a.tiles_r) * 32 * WR;
+        first = w.y;
+        count = w.z;
         shared = false;
     } else {
-        e = 0;
-        n0 = (bid - a.amax * a.tiles_r) * NPB;
-        first = 0;
+        n0 = (bid - a.amax * a.tiles_r) * 32 * WR;
         count = a.M;
-        W = &a.sdown;
         shared = true;
     }
-    const int D = W->N, F = W->K;
+    const MoeMat& W = shared ? a.sdown : a.down;
+    const int Dm = W.N, F = W.K;
     const uint16_t* hin = shared ? a.hs : a.h;
-    Core core;
-    core.VR = F / Traits<S>::KV;
-    core.sl = sl;
-    int n[R];
+    MfmaTile tl[2 * WR];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        n[r] = n0 + wave * RSW * R + slot + r * RSW;
-        const int nl = n[r] < D ? n[r] : D - 1;
-        row_ptrs<S>(*W, e, nl, core.crow[r], core.srow[r], core.brow[r]);
-    }
-    uint32_t* xs = smem;
-    float* XS = reinterpret_cast<float*>(smem + MT * (F / 2));
-    typename Core::Buf A, B;
-    for (int t0 = 0; t0 < count; t0 += MT) {
-        const int mt = min(MT, count - t0);
-        core.load(A, 0);
-        if (t0) __syncthreads();
-        if (threadIdx.x < MT) {
-            const int i = t0 + (int)threadIdx.x < count ? t0 + threadIdx.x : t0;
-            tok[threadIdx.x] = shared ? i : a.pairs[first + i];
-        }
-        __syncthreads();
-        stage_x<S, MT, V, 256>(hin, F, tok, mt, F, xs, XS);
-        __syncthreads();
-        float acc[R][MT];
+    for (int w = 0; w < 2 * WR; ++w) tl[w] = expert_tile<S>(W, e, n0 + 16 * w);
+    for (int t0 = 0; t0 < count; t0 += 16) {
+        if (t0) __syncthreads();  // LDS reuse across token tiles
+        const int t = min(t0 + c16, count - 1);
+        const int row = shared ? t : a.pairs[first + t];
+        f32x4_t acc[2];
+        mfma_tiles<S, 2, WK, 2, WR, SL>(tl, F, hin, (uint32_t)row * (uint32_t)F, lds, acc);
+        if (wave >= WR) continue;
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int rt = 0; rt < 2; ++rt) {
+            const int n = n0 + 32 * wave + 16 * rt + c16;
+            if (n >= Dm) continue;
 #pragma unroll
-            for (int m = 0; m < MT; ++m) acc[r][m] = 0.f;
-        core.run(A, B, xs, XS, F / 2, acc);
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) acc[r][m] = group_sum<LPR>(acc[r][m]);
-        if (sl == 0) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                if (n[r] >= D) continue;
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    if (m >= mt) continue;
-                    if (shared) a.sout[(int64_t)(t0 + m) * D + n[r]] = acc[r][m];
-                    else a.part[(int64_t)a.pairs[first + t0 + m] * D + n[r]] = acc[r][m];
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int m = t0 + 4 * g + r;
+                if (m >= count) continue;
+                if (shared) a.sout[(int64_t)m * Dm + n] = acc[rt][r];
+                else a.part[(int64_t)a.pairs[first + m] * Dm + n] = acc[rt][r];
             }
         }
     }
@@ -327,9 +299,7 @@ static size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
 MoeWorkspace moe_workspace_layout(int64_t M, int k, int64_t E, int64_t D, int64_t F, int64_t Fs) {
     MoeWorkspace w{};
     size_t o = 0;
-    w.offsets = o; o += al((E + 1) * 4);
-    w.active = o;  o += al(E * 4);
-    w.n_active = o; o += al(4);
+    w.work = o;    o += al(E * 16);
     w.pairs = o;   o += al(M * k * 4);
     w.h = o;       o += al(M * k * F * 2);
     w.hs = o;      o += al(M * Fs * 2);
@@ -352,36 +322,32 @@ static MoeMat mm(const void* c, const void* s, const void* b, int64_t N, int64_t
     return m;
 }
 
-template <int S>
+template <int S, int WR, int WK>
 static hipError_t moe_passes(const MoeArgs& a0, int64_t Fs, hipStream_t st) {
     MoeArgs a = a0;
     const int D = a.gate.K, F = a.gate.N;
-    // gate/up: LPR 64 (one wavefront per (gate, up) row pair), 4 n per block
-    a.tiles_r = (F + 3) / 4;
-    a.tiles_s = a.has_shared ? (int)((Fs + 3) / 4) : 0;
+    // gate/up: 16 * WR (gate, up) rows per workgroup
+    a.tiles_r = (F + 16 * WR - 1) / (16 * WR);
+    a.tiles_s = a.has_shared ? (int)((Fs + 16 * WR - 1) / (16 * WR)) : 0;
     int blocks = a.amax * a.tiles_r + a.tiles_s;
-    const int kv = Traits<S>::KV;
-    const int Dmax = D;
-    if (a.M == 1) {
-        size_t lds = (size_t)1 * (Dmax / 2 + Dmax / kv) * 4;
-        hipLaunchKernelGGL((moe_gate_up_kernel<S, 1, 64, 1>), dim3(blocks), dim3(256), lds, st, a);
-    } else {
-        size_t lds = (size_t)4 * (Dmax / 2 + Dmax / kv) * 4;
-        hipLaunchKernelGGL((moe_gate_up_kernel<S, 4, 64, 1>), dim3(blocks), dim3(256), lds, st, a);
+    size_t lds = gemv_mfma_lds_bytes<S, 2, WK, WR>(D);
+    switch (mfma_slices(D / Traits<S>::GROUP)) {
+        case 1: hipLaunchKernelGGL((moe_gate_up_kernel<S, WR, WK, 1>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
+        case 2: hipLaunchKernelGGL((moe_gate_up_kernel<S, WR, WK, 2>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
+        default: hipLaunchKernelGGL((moe_gate_up_kernel<S, WR, WK, 4>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // down: LPR 16, V 2, R 2 -> 32 rows per block (K = F routed, Fs shared)
-    const int Kmax = a.has_shared ? (int)std::max<int64_t>(F, Fs) : F;
-    a.tiles_r = (D + 31) / 32;
+    // down: 32 * WR rows per workgroup (K = F routed, Fs shared)
+    const int64_t Kmax = a.has_shared ? std::max<int64_t>(F, Fs) : F;
+    a.tiles_r = (D + 32 * WR - 1) / (32 * WR);
     a.tiles_s = a.has_shared ? a.tiles_r : 0;
     blocks = a.amax * a.tiles_r + a.tiles_s;
-    if (a.M == 1) {
-        size_t lds = (size_t)1 * (Kmax / 2 + Kmax / kv) * 4;
-        hipLaunchKernelGGL((moe_down_kernel<S, 1, 16, 2, 2>), dim3(blocks), dim3(256), lds, st, a);
-    } else {
-        size_t lds = (size_t)4 * (Kmax / 2 + Kmax / kv) * 4;
-        hipLaunchKernelGGL((moe_down_kernel<S, 4, 16, 2, 2>), dim3(blocks), dim3(256), lds, st, a);
+    lds = gemv_mfma_lds_bytes<S, 2, WK, WR>(Kmax);
+    switch (mfma_slices(Kmax / Traits<S>::GROUP)) {
+        case 1: hipLaunchKernelGGL((moe_down_kernel<S, WR, WK, 1>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
+        case 2: hipLaunchKernelGGL((moe_down_kernel<S, WR, WK, 2>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
+        default: hipLaunchKernelGGL((moe_down_kernel<S, WR, WK, 4>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
     }
     return hipGetLastError();
 }
@@ -480,9 +446,7 @@ hipError_t launch_moe(int scheme, const MoeMats& W, const uint16_t* x, int64_t M
     a.k = k;
     a.E = (int)E;
     a.x = x;
-    a.offsets = (const int32_t*)(base + L.offsets);
-    a.active = (const int32_t*)(base + L.active);
-    a.n_active = (const int32_t*)(base + L.n_active);
+    a.work = (const int4*)(base + L.work);
     a.pairs = (const int32_t*)(base + L.pairs);
     a.h = (uint16_t*)(base + L.h);
     a.hs = (uint16_t*)(base + L.hs);
@@ -490,12 +454,12 @@ hipError_t launch_moe(int scheme, const MoeMats& W, const uint16_t* x, int64_t M
     a.sout = (float*)(base + L.sout);
     a.amax = (int)std::min<int64_t>(E, M * k);
     const int P = (int)(M * k);
-    hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(1024), 0, st, ids, P, (int)E,
-                       (int32_t*)(base + L.offsets), (int32_t*)(base + L.active),
-                       (int32_t*)(base + L.n_active), (int32_t*)(base + L.pairs));
+    hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(1024), 0, st, ids, P, (int)E, a.amax,
+                       (int4*)(base + L.work), (int32_t*)(base + L.pairs));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = scheme == SYM4_G128 ? moe_passes<SYM4_G128>(a, Fs, st) : moe_passes<AFF4_G64>(a, Fs, st);
+    e = scheme == SYM4_G128 ? moe_passes<SYM4_G128, 1, 4>(a, Fs, st)
+                            : moe_passes<AFF4_G64, 1, 4>(a, Fs, st);
     if (e != hipSuccess) return e;
     const int64_t tot = M * D;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,

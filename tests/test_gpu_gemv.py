@@ -71,13 +71,16 @@ def test_gemv_head_sampled_rows():
     _run("aff4_g64", 152064, 5120, 1, "llama13b.head", rows=rows)
 
 
+@pytest.mark.parametrize("ngroups", [2, 3])
 @pytest.mark.parametrize("scheme", ["aff4_g64", "sym4_g128", "aff8_g64"])
-def test_gemv_exact_on_dyadic_toy(scheme):
+def test_gemv_exact_on_dyadic_toy(scheme, ngroups):
     """8 x 64/128 toy with dyadic scales/biases and small-integer activations:
-    every partial sum is exactly representable, so the fp32 result is exact."""
+    every partial sum is exactly representable, so the fp32 result is exact.
+    Two tokens take the matrix-core path for the 4-bit schemes; an odd group
+    count covers its half step."""
     rng = np.random.default_rng(21)
     g = 128 if scheme == "sym4_g128" else 64
-    K, N = 2 * g, 8
+    K, N = ngroups * g, 8
     if scheme == "sym4_g128":
         q = rng.integers(-7, 8, size=(N, K))
         s = np.array([2.0 ** -(2 + n % 3) for n in range(N)] * (K // g), np.float32).reshape(K // g, N).T.copy()
