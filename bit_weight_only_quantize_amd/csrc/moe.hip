@@ -28,37 +28,82 @@
 namespace w4 {
 
 // ---------------------------------------------------------------- routing
-// One workgroup (64 threads) per token, E <= 1024. Every logit is ranked against
-// all E logits (staged in LDS): rank = #{j : l_j > l_e or (l_j == l_e and j < e)},
-// i.e. its position in a stable sort by logit descending. rank < k selects the
-// expert into slot `rank`. Softmax over all E raw logits; no renormalization.
+// Wave-wide reductions over DPP (row steps, then row_bcast15/31 into lane 63)
+// and a readlane broadcast: no LDS round trips. Lanes a DPP step does not
+// write keep their own value (old = src), the identity for max and min.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_keep(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_i(int v, Op op) {
+    v = op(v, dpp_keep<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
+    v = op(v, dpp_keep<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
+    v = op(v, dpp_keep<0x141, 0xF>(v));  // row_half_mirror
+    v = op(v, dpp_keep<0x140, 0xF>(v));  // row_mirror
+    v = op(v, dpp_keep<0x142, 0xA>(v));  // row_bcast15
+    v = op(v, dpp_keep<0x143, 0xC>(v));  // row_bcast31
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    return __int_as_float(wave_reduce_i(__float_as_int(v), [](int a, int b) {
+        return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+    }));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    return __int_as_float(wave_reduce_i(__float_as_int(v), [](int a, int b) {
+        return __float_as_int(__int_as_float(a) + __int_as_float(b));
+    }));
+}
+__device__ __forceinline__ int wave_min_dpp(int v) {
+    return wave_reduce_i(v, [](int a, int b) { return a < b ? a : b; });
+}
+
+// One wavefront per token, E <= 64 * EPL (EPL logits per lane, in registers). The
+// selection is the first k of a stable sort by logit descending: k rounds of a
+// wave-wide arg-max (highest logit, then lowest expert index), each winner
+// masked out. Softmax over all E raw logits; no renormalization. Every step is
+// register or DPP work: the only memory traffic is the logits in and k
+// results out. EPL is as small as E allows: a single wavefront on a CU whose
+// instruction cache is cold pays for every line of code it executes.
+template <int EPL>
 __global__ __launch_bounds__(64) void topk_softmax_kernel(const float* __restrict__ logits, int E,
                                                           int k, int32_t* __restrict__ ids,
                                                           float* __restrict__ wts) {
-    __shared__ float ls[1024];
     const int m = blockIdx.x, lane = threadIdx.x;
     const float* l = logits + (int64_t)m * E;
-    float mx = -INFINITY;
-    for (int e = lane; e < E; e += 64) {
-        ls[e] = l[e];
-        mx = fmaxf(mx, ls[e]);
+    float v[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {  // all loads issued at once (clamped), padding -inf
+        const int e = lane + 64 * j;
+        const float x = l[min(e, E - 1)];
+        v[j] = e < E ? x : -INFINITY;
     }
-    mx = wave_max(mx);
-    __syncthreads();
+    float mx = v[0];
+#pragma unroll
+    for (int j = 1; j < EPL; ++j) mx = fmaxf(mx, v[j]);
+    mx = wave_max_dpp(mx);
     float s = 0.f;
-    for (int e = lane; e < E; e += 64) s += expf(ls[e] - mx);
-    for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);  // same order in every lane
-    const float inv = 1.f / s;
-    for (int e = lane; e < E; e += 64) {
-        const float v = ls[e];
-        int rank = 0;
-        for (int j = 0; j < E; ++j) {
-            const float u = ls[j];
-            rank += (u > v) | ((u == v) & (j < e));
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) s += expf(v[j] - mx);
+    const float inv = 1.f / wave_sum_dpp(s);
+    unsigned taken = 0;
+    for (int r = 0; r < k; ++r) {
+        float bv = -INFINITY;
+        int be = 0x7FFFFFFF;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {  // this lane's best untaken (lowest index on ties)
+            const int e = lane + 64 * j;
+            const bool ok = e < E && !((taken >> j) & 1u) && (v[j] > bv || be == 0x7FFFFFFF);
+            bv = ok ? v[j] : bv;
+            be = ok ? e : be;
         }
-        if (rank < k) {
-            ids[(int64_t)m * k + rank] = e;
-            wts[(int64_t)m * k + rank] = expf(v - mx) * inv;
+        const float gv = wave_max_dpp(bv);
+        const int ge = wave_min_dpp(be != 0x7FFFFFFF && bv == gv ? be : 0x7FFFFFFF);
+        if ((ge & 63) == lane) taken |= 1u << (ge >> 6);
+        if (lane == 0) {
+            ids[(int64_t)m * k + r] = ge;
+            wts[(int64_t)m * k + r] = expf(gv - mx) * inv;
         }
     }
 }
@@ -68,8 +113,15 @@ hipError_t launch_route(int scheme, const void* codes, const void* scale, const 
                         int32_t* ids, float* wts, hipStream_t st) {
     hipError_t e = launch_gemv(scheme, codes, scale, bias, E, K, x, M, logits, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_softmax_kernel, dim3((unsigned)M), dim3(64), 0, st, logits, (int)E, k,
-                       ids, wts);
+    if (E <= 128)
+        hipLaunchKernelGGL(topk_softmax_kernel<2>, dim3((unsigned)M), dim3(64), 0, st, logits, (int)E,
+                           k, ids, wts);
+    else if (E <= 256)
+        hipLaunchKernelGGL(topk_softmax_kernel<4>, dim3((unsigned)M), dim3(64), 0, st, logits, (int)E,
+                           k, ids, wts);
+    else
+        hipLaunchKernelGGL(topk_softmax_kernel<16>, dim3((unsigned)M), dim3(64), 0, st, logits,
+                           (int)E, k, ids, wts);
     return hipGetLastError();
 }
 
