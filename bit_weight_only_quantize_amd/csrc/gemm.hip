@@ -176,16 +176,23 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint8_t* __restrict__ c
             for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bf[buf][j], acc[i][j], 0, 0, 0);
     };
+    // The scheduling barriers keep each fragment read batch ahead of the
+    // MFMAs it overlaps; left alone, the scheduler moves the reads in among
+    // those MFMAs and waits on them right away.
     __syncthreads();  // prologue stages ready
     frags(0, 0, 0);
     for (int s = 0; s < ksteps; ++s) {
         frags(1, s, 1);
+        __builtin_amdgcn_sched_barrier(0);
         mfmas(0);
         frags(0, s, 2);
+        __builtin_amdgcn_sched_barrier(0);
         mfmas(1);
         frags(1, s, 3);
+        __builtin_amdgcn_sched_barrier(0);
         mfmas(0);
         if (s + 1 < ksteps) frags(0, s + 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
         mfmas(1);
         __syncthreads();
     }
