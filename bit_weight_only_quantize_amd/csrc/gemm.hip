@@ -13,7 +13,7 @@
 //   * producers stream 64-wide k steps: the X tile (bf16, 32 KiB) is copied and
 //     the W tile's codes (4 KiB) are dequantized -- w = s*q (sym) or s*u + b
 //     (affine), in fp32, rounded to nearest even bf16 -- into a 3-stage LDS ring
-//     (144 KiB); global loads run two steps ahead of their LDS stores;
+//     (144 KiB); global loads run three steps ahead of their LDS stores;
 //   * 16-byte chunks are XOR-swizzled by row so MFMA operand reads from LDS are
 //     free of bank conflicts; one barrier per k step separates the ring stages;
 //   * tiles are ordered so consecutive tiles land on one XCD and share an X row
@@ -121,23 +121,32 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint8_t* __restrict__ c
                 B[gchunk(brow, 4 * bh + d)] = make_uint4(o[0], o[1], o[2], o[3]);
             }
         };
-        // prologue: stages 0 and 1 stored, step 2 in registers
-        Regs ra, rb;
+        // Three register buffers: while the consumers work on step s, steps
+        // s+3 .. s+5 are in flight from global memory (the producers are
+        // latency-bound: every N tile re-reads its X block from L2).
+        // prologue: stages 0 and 1 stored, steps 2..4 in registers
+        Regs ra, rb, rc;
         gload(ra, 0);
         if (ksteps > 1) gload(rb, 1);
+        if (ksteps > 2) gload(rc, 2);
         lstore(ra, 0);
-        if (ksteps > 2) gload(ra, 2);
+        if (ksteps > 3) gload(ra, 3);
         if (ksteps > 1) lstore(rb, 1);
-        if (ksteps > 3) gload(rb, 3);
+        if (ksteps > 4) gload(rb, 4);
         __syncthreads();
-        // iteration s: store step s+2 (loaded earlier), load step s+4
-        for (int s = 0; s < ksteps; s += 2) {
-            if (s + 2 < ksteps) lstore(ra, s + 2);
-            if (s + 4 < ksteps) gload(ra, s + 4);
+        // iteration s: store step s+2 (loaded three steps earlier), load step s+5
+        for (int s = 0; s < ksteps; s += 3) {
+            if (s + 2 < ksteps) lstore(rc, s + 2);
+            if (s + 5 < ksteps) gload(rc, s + 5);
             __syncthreads();
             if (s + 1 < ksteps) {
-                if (s + 3 < ksteps) lstore(rb, s + 3);
-                if (s + 5 < ksteps) gload(rb, s + 5);
+                if (s + 3 < ksteps) lstore(ra, s + 3);
+                if (s + 6 < ksteps) gload(ra, s + 6);
+                __syncthreads();
+            }
+            if (s + 2 < ksteps) {
+                if (s + 4 < ksteps) lstore(rb, s + 4);
+                if (s + 7 < ksteps) gload(rb, s + 7);
                 __syncthreads();
             }
         }
