@@ -6,16 +6,29 @@
 // dequantized copy in HBM.
 //
 // Design for gfx950 (256 CUs in 8 XCDs, 160 KiB LDS, bf16 MFMA 32x32x16):
-//   * a workgroup computes a 256 (M) x 128 (N) tile with 8 wavefronts: 4 MFMA
-//     wavefronts (a 2 x 2 grid of 128 x 64 sub-tiles, fp32 accumulators) and 4
-//     producer wavefronts, one of each per SIMD, so the dequantization VALU work
-//     of the producer issues in the shadow of the consumer's MFMAs;
-//   * producers stream 64-wide k steps: the X tile (bf16, 32 KiB) is copied and
-//     the W tile's codes (4 KiB) are dequantized -- w = s*q (sym) or s*u + b
-//     (affine), in fp32, rounded to nearest even bf16 -- into a 3-stage LDS ring
-//     (144 KiB); global loads run three steps ahead of their LDS stores;
-//   * 16-byte chunks are XOR-swizzled by row so MFMA operand reads from LDS are
-//     free of bank conflicts; one barrier per k step separates the ring stages;
+//   * a workgroup computes a 256 (M) x 128 (N) tile with 4 wavefronts, one per
+//     SIMD, each owning a 128 x 64 quadrant (4 x 2 MFMA blocks, fp32
+//     accumulators);
+//   * LDS bandwidth is the scarce resource (about 128 B/clk per CU for reads,
+//     half that for ds_write_b128), so only the activations are staged there:
+//     the X tile of each 64-wide k step (32 KiB) and the step's packed codes
+//     (4 KiB) arrive by direct global->LDS loads (global_load_lds_dwordx4: no
+//     registers, no ds_write) in a 4-stage ring, issued four steps ahead;
+//   * each wavefront dequantizes its own B fragments in registers straight from
+//     the codes -- w = s*q (sym) or s*u + b (affine), in fp32, rounded to nearest
+//     even bf16 -- so no bf16 weight tile is ever written to or read from LDS;
+//   * inside a step the contraction order of k is permuted so that one 16-byte
+//     code read per column and lane covers the step's four k slices: slice kk of
+//     lane half h takes the 8 weights of code word 4h + kk, and the A fragment
+//     reads the matching 16-byte chunk of X;
+//   * X chunks are XOR-swizzled by row (chosen through the source chunk each
+//     lane of a direct load fetches) so MFMA operand reads are free of bank
+//     conflicts;
+//   * one barrier per step, in the middle of it: after it the next step's ring
+//     stage is complete for every wavefront, the loads four steps ahead start
+//     into the stage just drained (spread over the following MFMAs), and the
+//     next step's first fragments are read and dequantized while this step's
+//     last MFMAs run;
 //   * tiles are ordered so consecutive tiles land on one XCD and share an X row
 //     block (workgroups are dispatched round-robin over the 8 XCDs), keeping
 //     that block resident in the XCD's L2;
@@ -25,22 +38,31 @@
 
 namespace w4 {
 
-constexpr int GBM = 256, GBN = 128, GBK = 64, GSTAGES = 3;
-constexpr int GCH = GBK / 8;  // 16-byte chunks per LDS row
+constexpr int GBM = 256, GBN = 128, GBK = 64, GSTAGES = 4;
+constexpr int X_BYTES = GBM * GBK * 2;  // X tile of one step
+constexpr int C_BYTES = GBN * GBK / 2;  // packed codes of one step
+constexpr int STAGE_BYTES = X_BYTES + C_BYTES;
 
-// LDS chunk index of chunk c (0..7) of row `row`
-__device__ __forceinline__ int gchunk(int row, int c) { return row * GCH + (c ^ (row & 7)); }
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+// s_waitcnt vmcnt(n) lgkmcnt(0)
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
+}
+
+// scheduling-group masks
+constexpr int SG_VALU = 0x2, SG_MFMA = 0x8, SG_VMEM = 0x20, SG_DSR = 0x100;
 
 template <int S>
-__global__ __launch_bounds__(512) void gemm_kernel(const uint8_t* __restrict__ codes,
-                                                   const uint8_t* __restrict__ scale,
-                                                   const uint8_t* __restrict__ bias, int M, int N,
-                                                   int K, const uint16_t* __restrict__ X,
-                                                   uint16_t* __restrict__ Y, int tiles_m,
-                                                   int tiles_n) {
+__global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* codes, const uint8_t* scale,
+                                                   const uint8_t* bias, int M, int N, int K,
+                                                   const uint16_t* X, uint16_t* __restrict__ Y,
+                                                   int tiles_m, int tiles_n) {
     using T = Traits<S>;
-    extern __shared__ __align__(16) uint4 gsm[];
-    constexpr int STAGE = (GBM + GBN) * GCH;  // chunks per ring stage
+    extern __shared__ __align__(16) uint8_t gsm[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
@@ -53,108 +75,69 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint8_t* __restrict__ c
     const int m0 = (L / tiles_n) * GBM, n0 = (L % tiles_n) * GBN;
     const int ksteps = K / GBK;
 
-    if (wave >= 4) {
-        // ---------------- producers: 256 threads
-        const int p = tid - 256;
-        const uint16_t* xrow[8];
-        int arow[8], ac[8];
+    // ---- direct-load sources of this wavefront. Rows and columns past the
+    // matrix edge are clamped to the last one; their results are never stored.
+    // X: load i covers tile rows 64*wave + 8*i + lane/8, and the lane fetches
+    // the chunk that the swizzle puts at position lane%8 of its row.
+    const uint16_t* xsrc[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int q = p + 256 * i;
-            arow[i] = q >> 3;
-            ac[i] = q & 7;
-            const int r = min(m0 + arow[i], M - 1);
-            xrow[i] = X + (int64_t)r * K + ac[i] * 8;
-        }
-        const int brow = p >> 1, bh = p & 1;
-        const int bn = min(n0 + brow, N - 1);
-        const uint8_t* crow = codes + (int64_t)bn * (K / 2) + bh * 16;
-        const int64_t groups = K / T::GROUP;
-        constexpr int SB = T::AFFINE ? 2 : 4;
-        const uint8_t* srow = scale + (int64_t)bn * groups * SB;
-        const uint8_t* bro = T::AFFINE ? bias + (int64_t)bn * groups * 2 : nullptr;
-
-        // Loaded values are kept raw until lstore: converting a scale right after
-        // its load would make the wavefront wait (vmcnt retires in order) for the
-        // whole load batch issued before it, defeating the prefetch.
-        struct Regs {
-            u32x4_t xa[8];
-            u32x4_t wc;
-            uint32_t ws, wb;  // raw scale / bias bits
-        };
-        auto gload = [&](Regs& R, int s) {
-            const int k0 = s * GBK;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) R.xa[i] = *reinterpret_cast<const u32x4_t*>(xrow[i] + k0);
-            R.wc = *reinterpret_cast<const u32x4_t*>(crow + k0 / 2);
-            const int g = k0 / T::GROUP;
-            if constexpr (T::AFFINE) {
-                R.ws = reinterpret_cast<const uint16_t*>(srow)[g];
-                R.wb = reinterpret_cast<const uint16_t*>(bro)[g];
-            } else {
-                R.ws = reinterpret_cast<const uint32_t*>(srow)[g];
-            }
-        };
-        auto lstore = [&](const Regs& R, int s) {
-            const float ws = T::AFFINE ? bf16_bits_to_f32(R.ws) : __uint_as_float(R.ws);
-            const float wb = T::AFFINE ? bf16_bits_to_f32(R.wb) : -8.f * ws;  // sym: q = u - 8
-            uint4* A = gsm + (s % GSTAGES) * STAGE;
-            uint4* B = A + GBM * GCH;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                A[gchunk(arow[i], ac[i])] = make_uint4(R.xa[i][0], R.xa[i][1], R.xa[i][2], R.xa[i][3]);
-            // 32 weights (4 code dwords) -> 4 chunks of 8 bf16 in natural k order
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                uint32_t c = R.wc[d];
-                if constexpr (S == SYM4_G128) c ^= 0x88888888u;  // two's complement -> q + 8
-                const uint32_t lo = c & 0x0F0F0F0Fu;             // elements 0, 2, 4, 6
-                const uint32_t hi = (c >> 4) & 0x0F0F0F0Fu;      // elements 1, 3, 5, 7
-                uint32_t o[4];
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const float e0 = (float)((lo >> (8 * b)) & 0xFFu);
-                    const float e1 = (float)((hi >> (8 * b)) & 0xFFu);
-                    const bf16x2_t pr = {(__bf16)fmaf(e0, ws, wb), (__bf16)fmaf(e1, ws, wb)};
-                    o[b] = __builtin_bit_cast(uint32_t, pr);
-                }
-                B[gchunk(brow, 4 * bh + d)] = make_uint4(o[0], o[1], o[2], o[3]);
-            }
-        };
-        // Three register buffers: while the consumers work on step s, steps
-        // s+3 .. s+5 are in flight from global memory (the producers are
-        // latency-bound: every N tile re-reads its X block from L2).
-        // prologue: stages 0 and 1 stored, steps 2..4 in registers
-        Regs ra, rb, rc;
-        gload(ra, 0);
-        if (ksteps > 1) gload(rb, 1);
-        if (ksteps > 2) gload(rc, 2);
-        lstore(ra, 0);
-        if (ksteps > 3) gload(ra, 3);
-        if (ksteps > 1) lstore(rb, 1);
-        if (ksteps > 4) gload(rb, 4);
-        __syncthreads();
-        // iteration s: store step s+2 (loaded three steps earlier), load step s+5
-        for (int s = 0; s < ksteps; s += 3) {
-            if (s + 2 < ksteps) lstore(rc, s + 2);
-            if (s + 5 < ksteps) gload(rc, s + 5);
-            __syncthreads();
-            if (s + 1 < ksteps) {
-                if (s + 3 < ksteps) lstore(ra, s + 3);
-                if (s + 6 < ksteps) gload(ra, s + 6);
-                __syncthreads();
-            }
-            if (s + 2 < ksteps) {
-                if (s + 4 < ksteps) lstore(rb, s + 4);
-                if (s + 7 < ksteps) gload(rb, s + 7);
-                __syncthreads();
-            }
-        }
-        return;
+    for (int i = 0; i < 8; ++i) {
+        const int r = 64 * wave + 8 * i + (lane >> 3);
+        const int c = (lane & 7) ^ ((lane >> 3) & 7);
+        xsrc[i] = X + (int64_t)min(m0 + r, M - 1) * K + c * 8;
     }
+    // codes: the load covers tile columns 32*wave + lane%32, half lane/32 of
+    // the step's 32 code bytes per column
+    const uint8_t* csrc =
+        codes + (int64_t)min(n0 + 32 * wave + (lane & 31), N - 1) * (K / 2) + (lane >> 5) * 16;
 
-    // ---------------- MFMA consumers: 4 wavefronts, 128 x 64 each
+    // ---- compute-side coordinates
     const int wm = wave >> 1, wn = wave & 1;
+    const int half = lane >> 5, l32 = lane & 31;
+    const int64_t groups = K / T::GROUP;
+    int64_t sidx[2];  // scale index of this lane's column j at group 0
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sidx[j] = (int64_t)min(n0 + wn * 64 + 32 * j + l32, N - 1) * groups;
+
+    // raw scale / bias bits of one step for the lane's two columns
+    struct Sc {
+        uint32_t s[2], b[2];
+    };
+    constexpr int NSC = T::AFFINE ? 4 : 2;  // scale loads per batch
+    constexpr int NB = NSC + 9;             // memory operations per batch
+
+    // Batch t: the scale loads, then the direct loads of step t into ring stage
+    // t % 4, issued in three parts spread over a step so that no wavefront
+    // stalls behind a burst of loads: part 0 (scales, X loads 0..3), part 1
+    // (X loads 4..7), part 2 (codes). A step past the end reloads the last step
+    // into a stage nobody reads again: every batch is issued, so the in-order
+    // load counter always holds whole batches and the waits below can count them.
+    auto issue = [&](int t, Sc& sc, int part) {
+        const int tc = min(t, ksteps - 1);
+        uint8_t* st = gsm + (t % GSTAGES) * STAGE_BYTES;
+        if (part == 0) {
+            const int g = tc * GBK / T::GROUP;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if constexpr (T::AFFINE) {
+                    sc.s[j] = reinterpret_cast<const uint16_t*>(scale)[sidx[j] + g];
+                    sc.b[j] = reinterpret_cast<const uint16_t*>(bias)[sidx[j] + g];
+                } else {
+                    sc.s[j] = reinterpret_cast<const uint32_t*>(scale)[sidx[j] + g];
+                }
+            }
+        }
+        if (part < 2) {
+#pragma unroll
+            for (int i = 4 * part; i < 4 * part + 4; ++i)
+                __builtin_amdgcn_global_load_lds((gbl_void_t*)(xsrc[i] + tc * GBK),
+                                                 (lds_void_t*)(st + (64 * wave + 8 * i) * 128), 16, 0, 0);
+        } else {
+            __builtin_amdgcn_global_load_lds((gbl_void_t*)(csrc + tc * (GBK / 2)),
+                                             (lds_void_t*)(st + X_BYTES + wave * 1024), 16, 0, 0);
+        }
+    };
+
     f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -162,49 +145,145 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint8_t* __restrict__ c
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    const int arow = wm * 128 + (lane & 31), brw = wn * 64 + (lane & 31), half = lane >> 5;
-    // Fragments are double-buffered across (step, kk): the reads for the next
-    // k slice are in flight while this slice's MFMAs issue. Stage s+1 is already
-    // complete during step s (the ring is 3 deep), so the pipeline runs across
-    // step boundaries; the barrier only has to follow the last read of stage s.
-    bf16x8_t af[2][4], bf[2][2];
-    auto frags = [&](int buf, int s, int kk) {
-        const uint4* A = gsm + (s % GSTAGES) * STAGE;
-        const uint4* B = A + GBM * GCH;
+
+    bf16x8_t af[2][4], bq[2][2];
+    u32x4_t cw[2];  // this lane's 16 code bytes of the step, per column j
+    // A fragments of slice kk: row wm*128 + 32i + l32, chunk 4*half + kk
+    auto load_a = [&](int t, int kk, int buf) {
+        const uint8_t* st = gsm + (t % GSTAGES) * STAGE_BYTES;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            af[buf][i] = __builtin_bit_cast(bf16x8_t, A[gchunk(arow + 32 * i, 2 * kk + half)]);
+        for (int i = 0; i < 4; ++i) {
+            const int r = wm * 128 + 32 * i + l32;
+            af[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + r * 128 + (((4 * half + kk) ^ (r & 7)) << 4));
+        }
+    };
+    auto load_codes = [&](int t) {
+        const uint8_t* st = gsm + (t % GSTAGES) * STAGE_BYTES + X_BYTES;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            bf[buf][j] = __builtin_bit_cast(bf16x8_t, B[gchunk(brw + 32 * j, 2 * kk + half)]);
+            cw[j] = *reinterpret_cast<const u32x4_t*>(st + (2 * wn + j) * 1024 + lane * 16);
+    };
+    // B fragments of slice kk: the 8 weights of code word kk (byte b holds
+    // elements 2b, low nibble, and 2b + 1)
+    auto dequant = [&](int kk, const Sc& sc, int buf) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float ws = T::AFFINE ? bf16_bits_to_f32(sc.s[j]) : __uint_as_float(sc.s[j]);
+            const float wb = T::AFFINE ? bf16_bits_to_f32(sc.b[j]) : -8.f * ws;  // sym: q = u - 8
+            uint32_t c = cw[j][kk];
+            if constexpr (S == SYM4_G128) c ^= 0x88888888u;  // two's complement -> q + 8
+            const uint32_t lo = c & 0x0F0F0F0Fu;
+            const uint32_t hi = (c >> 4) & 0x0F0F0F0Fu;
+            uint32_t o[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float e0 = (float)((lo >> (8 * b)) & 0xFFu);
+                const float e1 = (float)((hi >> (8 * b)) & 0xFFu);
+                const bf16x2_t pr = {(__bf16)fmaf(e0, ws, wb), (__bf16)fmaf(e1, ws, wb)};
+                o[b] = __builtin_bit_cast(uint32_t, pr);
+            }
+            bq[buf][j] = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
+        }
     };
     auto mfmas = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bf[buf][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bq[buf][j], acc[i][j], 0, 0, 0);
     };
-    // The scheduling barriers keep each fragment read batch ahead of the
-    // MFMAs it overlaps; left alone, the scheduler moves the reads in among
-    // those MFMAs and waits on them right away.
-    __syncthreads();  // prologue stages ready
-    frags(0, 0, 0);
-    for (int s = 0; s < ksteps; ++s) {
-        frags(1, s, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(0);
-        frags(0, s, 2);
-        __builtin_amdgcn_sched_barrier(0);
+    // The barrier orders the LDS traffic by itself (the counter waits before it
+    // make each wavefront's loads and reads complete); the empty asm keeps the
+    // compiler from moving memory operations across it.
+    auto barrier = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // interleave: each MFMA is followed by a share of the VALU, LDS reads and
+    // global loads
+    auto interleave = [&](int vm) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_DSR, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VALU, 6, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            if (r < vm) __builtin_amdgcn_sched_group_barrier(SG_VMEM, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VALU, 6, 0);
+        }
+    };
+
+    // One step. Slices 0..2 run their MFMAs while slice kk+1 is read and
+    // dequantized, and parts 1 and 2 of batch t+3 are issued. Then: this
+    // wavefront's batch t+1 has landed (batches t+2 and t+3 may still be in
+    // flight) and its LDS reads are done; the barrier makes that true for every
+    // wavefront, so stage t+1 is readable and stage t, fully read, takes batch
+    // t+4 (part 0 now). The last slice's MFMAs cover the reads and
+    // dequantization of step t+1's first slice.
+    auto step = [&](int t, Sc& cur, Sc& nxt, Sc& prev) {
+#pragma unroll
+        for (int kk = 0; kk < 3; ++kk) {
+            if (kk == 0) issue(t + 3, prev, 1);
+            if (kk == 1) issue(t + 3, prev, 2);
+            load_a(t, kk + 1, (kk + 1) & 1);
+            dequant(kk + 1, cur, (kk + 1) & 1);
+            mfmas(kk & 1);
+            interleave(kk == 0 ? 4 : kk == 1 ? 1 : 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_vm_lgkm0<2 * NB>();
+        barrier();
+        issue(t + 4, cur, 0);
+        load_codes(t + 1);
+        load_a(t + 1, 0, 0);
+        dequant(0, nxt, 0);
         mfmas(1);
-        frags(1, s, 3);
+        __builtin_amdgcn_sched_group_barrier(SG_DSR, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VMEM, NSC, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VMEM, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VALU, 8, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        mfmas(0);
-        if (s + 1 < ksteps) frags(0, s + 1, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(1);
-        __syncthreads();
+    };
+
+    Sc sc0, sc1, sc2, sc3;
+    for (int part = 0; part < 3; ++part) issue(0, sc0, part);
+    for (int part = 0; part < 3; ++part) issue(1, sc1, part);
+    for (int part = 0; part < 3; ++part) issue(2, sc2, part);
+    issue(3, sc3, 0);
+    // batch 0 landed: batches 1 and 2 and part 0 of batch 3 may be in flight
+    wait_vm_lgkm0<2 * NB + NSC + 4>();
+    barrier();
+    load_codes(0);
+    load_a(0, 0, 0);
+    dequant(0, sc0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // whole rounds of four steps keep the loop free of exits: its header joins
+    // one path only, so the compiler's own load-counter waits stay exact
+    int t = 0;
+    for (; t + 4 <= ksteps; t += 4) {
+        step(t, sc0, sc1, sc3);
+        step(t + 1, sc1, sc2, sc0);
+        step(t + 2, sc2, sc3, sc1);
+        step(t + 3, sc3, sc0, sc2);
     }
+    if (t < ksteps) step(t, sc0, sc1, sc3);
+    if (t + 1 < ksteps) step(t + 1, sc1, sc2, sc0);
+    if (t + 2 < ksteps) step(t + 2, sc2, sc3, sc1);
+    // no direct load may still be writing this workgroup's LDS when it retires
+    wait_vm_lgkm0<0>();
 
     // ---- epilogue: D[i][j] of a 32x32 block sits in lane j + 32 * ((i / 4) % 2),
     // register 4 * (i / 8) + i % 4.
@@ -212,7 +291,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(const uint8_t* __restrict__ c
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int n = n0 + wn * 64 + 32 * j + (lane & 31);
+            const int n = n0 + wn * 64 + 32 * j + l32;
             if (n >= N) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -230,10 +309,10 @@ hipError_t launch_gemm(int scheme, const void* codes, const void* scale, const v
                        hipStream_t st) {
     const int tm = (int)((M + GBM - 1) / GBM), tn = (int)((N + GBN - 1) / GBN);
     const int per = (tm * tn + 7) / 8;
-    const size_t lds = (size_t)GSTAGES * (GBM + GBN) * GCH * 16;
+    const size_t lds = (size_t)GSTAGES * STAGE_BYTES;
     auto kern = scheme == SYM4_G128 ? gemm_kernel<SYM4_G128> : gemm_kernel<AFF4_G64>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(kern, dim3(8 * per), dim3(512), lds, st, (const uint8_t*)codes,
+    hipLaunchKernelGGL(kern, dim3(8 * per), dim3(256), lds, st, (const uint8_t*)codes,
                        (const uint8_t*)scale, (const uint8_t*)bias, (int)M, (int)N, (int)K, X, Y,
                        tm, tn);
     return hipGetLastError();

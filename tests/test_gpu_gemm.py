@@ -42,7 +42,8 @@ def _case(scheme, M, N, K, name, rows=None, cols=None):
 
 @pytest.mark.parametrize("scheme", ["sym4_g128", "aff4_g64"])
 @pytest.mark.parametrize("M,N,K", [(300, 200, 512), (1, 128, 256), (17, 1, 128),
-                                   (257, 129, 384), (512, 256, 1024)])
+                                   (257, 129, 384), (512, 256, 1024), (65, 130, 192),
+                                   (3, 40, 64), (260, 300, 320)])
 def test_gemm_small_and_ragged(scheme, M, N, K):
     if K % (128 if scheme == "sym4_g128" else 64):
         pytest.skip("K not a multiple of the group")
