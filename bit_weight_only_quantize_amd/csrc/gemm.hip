@@ -172,8 +172,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* codes, const u
             const float wb = T::AFFINE ? bf16_bits_to_f32(sc.b[j]) : -8.f * ws;  // sym: q = u - 8
             uint32_t c = cw[j][kk];
             if constexpr (S == SYM4_G128) c ^= 0x88888888u;  // two's complement -> q + 8
-            const uint32_t lo = c & 0x0F0F0F0Fu;
-            const uint32_t hi = (c >> 4) & 0x0F0F0F0Fu;
+            uint32_t lo = c & 0x0F0F0F0Fu;
+            uint32_t hi = (c >> 4) & 0x0F0F0F0Fu;
+            // hide the masks from the optimizer: it would otherwise fold them
+            // into one bit-field extract per nibble instead of converting the
+            // bytes of lo and hi directly (v_cvt_f32_ubyte0..3)
+            asm("" : "+v"(lo), "+v"(hi));
             uint32_t o[4];
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
