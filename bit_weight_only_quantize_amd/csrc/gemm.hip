@@ -7,8 +7,9 @@
 //
 // Design for gfx950 (256 CUs in 8 XCDs, 160 KiB LDS, bf16 MFMA 32x32x16):
 //   * a workgroup computes a 256 (M) x 128 (N) tile with 4 wavefronts, one per
-//     SIMD, each owning a 128 x 64 quadrant (4 x 2 MFMA blocks, fp32
-//     accumulators);
+//     SIMD, each owning all 256 rows of 32 columns (8 MFMA blocks of 32 x 32,
+//     fp32 accumulators): every weight of the tile is dequantized once, at the
+//     price of each X fragment being read by all four wavefronts;
 //   * LDS bandwidth is the scarce resource (about 128 B/clk per CU for reads,
 //     half that for ds_write_b128), so only the activations are staged there:
 //     the X tile of each 64-wide k step (32 KiB) and the step's packed codes
@@ -39,6 +40,9 @@
 namespace w4 {
 
 constexpr int GBM = 256, GBN = 128, GBK = 64, GSTAGES = 4;
+// wavefront grid over the tile: WMN along M x WNN along N; each wavefront owns
+// RM x CN outputs, NI x NJ MFMA blocks of 32 x 32
+constexpr int WMN = 1, WNN = 4, RM = GBM / WMN, CN = GBN / WNN, NI = RM / 32, NJ = CN / 32;
 constexpr int X_BYTES = GBM * GBK * 2;  // X tile of one step
 constexpr int C_BYTES = GBN * GBK / 2;  // packed codes of one step
 constexpr int STAGE_BYTES = X_BYTES + C_BYTES;
@@ -92,18 +96,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* codes, const u
         codes + (int64_t)min(n0 + 32 * wave + (lane & 31), N - 1) * (K / 2) + (lane >> 5) * 16;
 
     // ---- compute-side coordinates
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WNN, wn = wave % WNN;
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t groups = K / T::GROUP;
-    int64_t sidx[2];  // scale index of this lane's column j at group 0
+    int64_t sidx[NJ];  // scale index of this lane's column j at group 0
 #pragma unroll
-    for (int j = 0; j < 2; ++j) sidx[j] = (int64_t)min(n0 + wn * 64 + 32 * j + l32, N - 1) * groups;
+    for (int j = 0; j < NJ; ++j) sidx[j] = (int64_t)min(n0 + wn * CN + 32 * j + l32, N - 1) * groups;
 
     // raw scale / bias bits of one step for the lane's two columns
     struct Sc {
-        uint32_t s[2], b[2];
+        uint32_t s[NJ], b[NJ];
     };
-    constexpr int NSC = T::AFFINE ? 4 : 2;  // scale loads per batch
+    constexpr int NSC = T::AFFINE ? 2 * NJ : NJ;  // scale loads per batch
     constexpr int NB = NSC + 9;             // memory operations per batch
 
     // Batch t: the scale loads, then the direct loads of step t into ring stage
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* codes, const u
         if (part == 0) {
             const int g = tc * GBK / T::GROUP;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 if constexpr (T::AFFINE) {
                     sc.s[j] = reinterpret_cast<const uint16_t*>(scale)[sidx[j] + g];
                     sc.b[j] = reinterpret_cast<const uint16_t*>(bias)[sidx[j] + g];
@@ -138,36 +142,36 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* codes, const u
         }
     };
 
-    f32x16_t acc[4][2];
+    f32x16_t acc[NI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    bf16x8_t af[2][4], bq[2][2];
-    u32x4_t cw[2];  // this lane's 16 code bytes of the step, per column j
-    // A fragments of slice kk: row wm*128 + 32i + l32, chunk 4*half + kk
+    bf16x8_t af[2][NI], bq[2][NJ];
+    u32x4_t cw[NJ];  // this lane's 16 code bytes of the step, per column j
+    // A fragments of slice kk: row wm*RM + 32i + l32, chunk 4*half + kk
     auto load_a = [&](int t, int kk, int buf) {
         const uint8_t* st = gsm + (t % GSTAGES) * STAGE_BYTES;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wm * 128 + 32 * i + l32;
+        for (int i = 0; i < NI; ++i) {
+            const int r = wm * RM + 32 * i + l32;
             af[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + r * 128 + (((4 * half + kk) ^ (r & 7)) << 4));
         }
     };
     auto load_codes = [&](int t) {
         const uint8_t* st = gsm + (t % GSTAGES) * STAGE_BYTES + X_BYTES;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            cw[j] = *reinterpret_cast<const u32x4_t*>(st + (2 * wn + j) * 1024 + lane * 16);
+        for (int j = 0; j < NJ; ++j)
+            cw[j] = *reinterpret_cast<const u32x4_t*>(st + (NJ * wn + j) * 1024 + lane * 16);
     };
     // B fragments of slice kk: the 8 weights of code word kk (byte b holds
     // elements 2b, low nibble, and 2b + 1)
     auto dequant = [&](int kk, const Sc& sc, int buf) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             const float ws = T::AFFINE ? bf16_bits_to_f32(sc.s[j]) : __uint_as_float(sc.s[j]);
             const float wb = T::AFFINE ? bf16_bits_to_f32(sc.b[j]) : -8.f * ws;  // sym: q = u - 8
             uint32_t c = cw[j][kk];
@@ -191,9 +195,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* codes, const u
     };
     auto mfmas = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bq[buf][j], acc[i][j], 0, 0, 0);
     };
     // The barrier orders the LDS traffic by itself (the counter waits before it
@@ -206,18 +210,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* codes, const u
     };
     // interleave: each MFMA is followed by a share of the VALU, LDS reads and
     // global loads
+    constexpr int VPM = (24 * NJ + NI * NJ - 1) / (NI * NJ);  // VALU per MFMA
     auto interleave = [&](int vm) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < NI * NJ; ++r) {
             __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_DSR, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_VALU, 6, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            if (r < vm) __builtin_amdgcn_sched_group_barrier(SG_VMEM, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_VALU, 6, 0);
+            if (r < NI) __builtin_amdgcn_sched_group_barrier(SG_DSR, 1, 0);
+            if (r >= NI * NJ - 4 && r - (NI * NJ - 4) < vm) __builtin_amdgcn_sched_group_barrier(SG_VMEM, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VALU, VPM, 0);
         }
     };
 
@@ -246,18 +246,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* codes, const u
         load_a(t + 1, 0, 0);
         dequant(0, nxt, 0);
         mfmas(1);
-        __builtin_amdgcn_sched_group_barrier(SG_DSR, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DSR, NJ + NI, 0);
         __builtin_amdgcn_sched_group_barrier(SG_VMEM, NSC, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < NI * NJ; ++r) {
             __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_VMEM, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_VALU, 8, 0);
+            if (r < 4) __builtin_amdgcn_sched_group_barrier(SG_VMEM, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VALU, VPM, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -292,14 +287,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* codes, const u
     // ---- epilogue: D[i][j] of a 32x32 block sits in lane j + 32 * ((i / 4) % 2),
     // register 4 * (i / 8) + i % 4.
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + wn * 64 + 32 * j + l32;
+        for (int j = 0; j < NJ; ++j) {
+            const int n = n0 + wn * CN + 32 * j + l32;
             if (n >= N) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+                const int m = m0 + wm * RM + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
                 if (m < M) {
                     const bf16x2_t pr = {(__bf16)acc[i][j][r], (__bf16)0.f};
                     Y[(int64_t)m * N + n] = (uint16_t)__builtin_bit_cast(uint32_t, pr);
