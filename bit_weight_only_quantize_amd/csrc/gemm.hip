@@ -130,6 +130,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* codes, const u
                     sc.s[j] = reinterpret_cast<const uint32_t*>(scale)[sidx[j] + g];
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (part < 2) {
 #pragma unroll
