@@ -369,6 +369,23 @@ def run_prefill(c: Ctx, a):
     for tag, (t, f) in res.items():
         out[f"{tag}_us"] = round(t * 1e3, 2)
         out[f"{tag}_TFLOPs"] = round(f / (t * 1e-3) / 1e12, 2)
+    # Context, not the product: the vendor dense bf16 GEMM (hipBLASLt through
+    # torch.matmul) on the same shapes with bf16 weights of the same layout
+    # ([N][K], read transposed), i.e. what the matrix cores give these shapes
+    # when no dequantization is involved and the weights are four times larger.
+    dense = {}
+    for tag, N, K in (("gate_up", 11008, 4096), ("down", 4096, 11008)):
+        Xd = torch.randn(M, K, device=c.dev, dtype=torch.bfloat16)
+        Wd = torch.randn(N, K, device=c.dev, dtype=torch.bfloat16)
+
+        def fd(Xd=Xd, Wd=Wd):
+            for _ in range(10):
+                torch.matmul(Xd, Wd.t())
+
+        gd = c.graph(fd)
+        t = c.time_graph(gd, a.steps, a.warmup) / 10
+        dense[tag] = {"us": round(t * 1e3, 2), "TFLOPs": round(2.0 * M * N * K / (t * 1e-3) / 1e12, 2)}
+    out["dense_bf16_reference"] = dict(dense, what="torch.matmul (hipBLASLt) bf16 x bf16, same shapes, no dequantization")
     t, f = res["gate_up"]
     out["roofline"] = {"bound": "mfma", "kernel": "gemm_kernel (2048x4096 . 4096->11008, sym4_g128)",
                        "achieved": round(f / (t * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
