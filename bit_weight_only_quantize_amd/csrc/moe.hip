@@ -543,41 +543,48 @@ bool moe1_ok(int64_t M, int k, int64_t D, int64_t F, int64_t Fs) {
 }
 
 template <int S, int NVD, int NVS>
-static void go_down1(const Moe1Args& a, int blocks, size_t lds, hipStream_t st) {
-    hipLaunchKernelGGL((moe1_down_kernel<S, NVD, NVS, 1, NVD + NVS>), dim3(blocks), dim3(320), lds,
-                       st, a);
+static void go_down1(const Moe1Args& a, int xv, int blocks, size_t lds, hipStream_t st) {
+    if (xv == 1)
+        hipLaunchKernelGGL((moe1_down_kernel<S, NVD, NVS, 1, 1, 4>), dim3(blocks), dim3(256), lds, st, a);
+    else
+        hipLaunchKernelGGL((moe1_down_kernel<S, NVD, NVS, 1, 2, 4>), dim3(blocks), dim3(256), lds, st, a);
 }
 
 template <int S, int NVD>
-static void pick_nvs(int nvs, const Moe1Args& a, int blocks, size_t lds, hipStream_t st) {
-    if (nvs == 0) go_down1<S, NVD, 0>(a, blocks, lds, st);
-    else if (nvs == 1) go_down1<S, NVD, 1>(a, blocks, lds, st);
-    else go_down1<S, NVD, 2>(a, blocks, lds, st);
+static void pick_nvs(int nvs, const Moe1Args& a, int xv, int blocks, size_t lds, hipStream_t st) {
+    if (nvs == 0) go_down1<S, NVD, 0>(a, xv, blocks, lds, st);
+    else if (nvs == 1) go_down1<S, NVD, 1>(a, xv, blocks, lds, st);
+    else go_down1<S, NVD, 2>(a, xv, blocks, lds, st);
 }
+
+// Row wavefronts per workgroup of both passes; each also stages a share of its
+// pass's activations (x: at most 128 vectors; h and hs: at most 384).
+constexpr int kMoe1RW = 4;
 
 template <int S>
 static hipError_t moe1_passes(Moe1Args a, hipStream_t st) {
     constexpr int R = 2;
     const int kv = Traits<S>::KV;
-    a.tiles_r = (a.F + 4 * R - 1) / (4 * R);
-    a.tiles_s = a.has_shared ? (a.Fs + 4 * R - 1) / (4 * R) : 0;
+    a.tiles_r = (a.F + kMoe1RW * R - 1) / (kMoe1RW * R);
+    a.tiles_s = a.has_shared ? (a.Fs + kMoe1RW * R - 1) / (kMoe1RW * R) : 0;
     const int blocks = a.k * a.tiles_r + a.tiles_s;
     const size_t lds = (size_t)(a.D / 2 + a.D / kv) * 4;
     if (a.D / kv <= 64)
-        hipLaunchKernelGGL((moe1_gate_up_kernel<S, 1, R, 1>), dim3(blocks), dim3(320), lds, st, a);
+        hipLaunchKernelGGL((moe1_gate_up_kernel<S, 1, R, 1, kMoe1RW>), dim3(blocks), dim3(64 * kMoe1RW), lds, st, a);
     else
-        hipLaunchKernelGGL((moe1_gate_up_kernel<S, 2, R, 2>), dim3(blocks), dim3(320), lds, st, a);
+        hipLaunchKernelGGL((moe1_gate_up_kernel<S, 2, R, 1, kMoe1RW>), dim3(blocks), dim3(64 * kMoe1RW), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int VRF = a.F / kv, VRS = a.has_shared ? a.Fs / kv : 0;
     const int nvd = (VRF + 7) / 8, nvs = (VRS + 63) / 64;
+    const int xv = (a.k * VRF + VRS + 64 * kMoe1RW - 1) / (64 * kMoe1RW);
     const size_t lds2 = (size_t)(8 * (a.F / 2 + VRF) + (a.has_shared ? a.Fs / 2 + VRS : 0)) * 4;
-    const int blocks2 = (a.D + 3) / 4;
+    const int blocks2 = (a.D + kMoe1RW - 1) / kMoe1RW;
     switch (nvd) {
-        case 1: pick_nvs<S, 1>(nvs, a, blocks2, lds2, st); break;
-        case 2: pick_nvs<S, 2>(nvs, a, blocks2, lds2, st); break;
-        case 3: pick_nvs<S, 3>(nvs, a, blocks2, lds2, st); break;
-        default: pick_nvs<S, 4>(nvs, a, blocks2, lds2, st); break;
+        case 1: pick_nvs<S, 1>(nvs, a, xv, blocks2, lds2, st); break;
+        case 2: pick_nvs<S, 2>(nvs, a, xv, blocks2, lds2, st); break;
+        case 3: pick_nvs<S, 3>(nvs, a, xv, blocks2, lds2, st); break;
+        default: pick_nvs<S, 4>(nvs, a, xv, blocks2, lds2, st); break;
     }
     return hipGetLastError();
 }

@@ -4,7 +4,10 @@
 // TurboFieldfare article (model section, 量化和精度): 8 experts of 128 per token,
 // a shared expert added without a routing weight, shared and routed FFNs side
 // by side. Both passes follow the wave-per-row GEMV design: weight loads issued
-// up front, activations staged into LDS by a dedicated staging wavefront.
+// up front; every row wavefront stages a share of the activations into LDS,
+// issuing those loads after the (small) routing loads and before its weight
+// loads, so the activation latency overlaps the routing latency and waiting
+// for the activations does not wait for the weights.
 //
 // gate/up pass: blocks cover (slot j < k or the shared expert) x row tiles; a
 //   row wavefront owns R (gate row n, up row n) pairs and writes
@@ -65,8 +68,8 @@ __device__ __forceinline__ void m1_scale(const uint8_t* s, const uint8_t* b, int
 }
 
 // ---------------------------------------------------------------- gate/up
-template <int S, int NV, int R, int XV>
-__global__ __launch_bounds__(320) void moe1_gate_up_kernel(Moe1Args a) {
+template <int S, int NV, int R, int XV, int RW>
+__global__ __launch_bounds__(64 * RW) void moe1_gate_up_kernel(Moe1Args a) {
     using T = Traits<S>;
     using L = XLayout<S, 1>;
     extern __shared__ __align__(16) uint32_t smem[];
@@ -77,24 +80,19 @@ __global__ __launch_bounds__(320) void moe1_gate_up_kernel(Moe1Args a) {
     const bool shared = bid >= a.k * a.tiles_r;
     const int slot = shared ? 0 : bid / a.tiles_r;
     const int tile = shared ? bid - a.k * a.tiles_r : bid % a.tiles_r;
-    int e = 0;
-    if (!shared) {
-        e = a.ids[slot];
-        if (e < 0 || e >= a.E) return;  // whole block: nothing routed to this slot
-    }
+    // the expert id, then this wavefront's share of the activations (they do
+    // not depend on the id), then the weights
+    const int e = shared ? 0 : a.ids[slot];
+    XStage<S, XV, 64 * RW> xstage;
+    xstage.fetch(a.x, VR, threadIdx.x);
+    asm volatile("" ::: "memory");  // keep the weight loads behind these
+    if (!shared && (e < 0 || e >= a.E)) return;  // whole block: nothing routed to this slot
     const int N = shared ? a.Fs : a.F;
     uint32_t* xs = smem;
     float* XS = reinterpret_cast<float*>(smem + D / 2);
-    if (wave >= 4) {
-        XStage<S, XV, 64> st;
-        st.fetch(a.x, VR, lane);
-        st.commit(VR, xs, XS, lane);
-        __syncthreads();
-        return;
-    }
     const Moe1Mat& G = shared ? a.sgate : a.gate;
     const Moe1Mat& U = shared ? a.sup : a.up;
-    const int row0 = tile * 4 * R + wave * R;
+    const int row0 = tile * RW * R + wave * R;
     u32x4_t c[2 * R][NV];
     float sc[2 * R][NV], bi[2 * R][NV];
 #pragma unroll
@@ -112,7 +110,8 @@ __global__ __launch_bounds__(320) void moe1_gate_up_kernel(Moe1Args a) {
             }
         }
     }
-    __syncthreads();
+    xstage.commit(VR, xs, XS, threadIdx.x);  // waits for the activations only
+    __syncthreads();  // activations staged; weight loads still in flight
     const uint32_t MASK = opaque(0x000F000Fu);
     const uint32_t MAGIC = unpack_magic<S>();
     float acc[2 * R];
@@ -142,11 +141,14 @@ __global__ __launch_bounds__(320) void moe1_gate_up_kernel(Moe1Args a) {
 
 // ---------------------------------------------------------------- down + combine
 // LDS: 8 slot regions of (F/2 pair dwords + F/KV sums), then the shared region.
-template <int S, int NVD, int NVS, int R, int XV>
-__global__ __launch_bounds__(320) void moe1_down_kernel(Moe1Args a) {
+// The k slot rows of h and the shared row hs are staged by all RW wavefronts,
+// XV 16-element vectors per thread.
+template <int S, int NVD, int NVS, int R, int XV, int RW>
+__global__ __launch_bounds__(64 * RW) void moe1_down_kernel(Moe1Args a) {
     using T = Traits<S>;
     using L = XLayout<S, 1>;
     constexpr int Q = T::BITS == 4 ? 4 : 2;
+    constexpr int NT = 64 * RW;
     extern __shared__ __align__(16) uint32_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -155,27 +157,59 @@ __global__ __launch_bounds__(320) void moe1_down_kernel(Moe1Args a) {
     const int regw = F / 2 + VRF;  // dwords per slot region
     uint32_t* sbase = smem + 8 * regw;
 
-    if (wave >= 4) {
-        // stage k slot rows of h and the shared row hs: fetch everything, then commit
-        const int total = k * VRF + VRS;
-        u32x4_t d[XV][Q];
+    // routing of this lane's slot group first, then this thread's share of h
+    // and hs (independent of the routing), then the weights
+    const int g = lane >> 3, sl = lane & 7;
+    int e = g < k ? a.ids[g] : -1;
+    const float w_raw = g < k ? a.wts[g] : 0.f;
+    const int total = k * VRF + VRS;
+    u32x4_t d[XV][Q];
 #pragma unroll
-        for (int t = 0; t < XV; ++t) {
-            const int i = min(lane + 64 * t, total - 1);
-            const uint16_t* src = i < k * VRF ? a.h + (int64_t)(i / VRF) * F + (i % VRF) * T::KV
-                                              : a.hs + (int64_t)(i - k * VRF) * T::KV;
+    for (int t = 0; t < XV; ++t) {
+        const int i = min((int)threadIdx.x + NT * t, total - 1);
+        const uint16_t* src = i < k * VRF ? a.h + (int64_t)(i / VRF) * F + (i % VRF) * T::KV
+                                          : a.hs + (int64_t)(i - k * VRF) * T::KV;
 #pragma unroll
-            for (int q = 0; q < Q; ++q) d[t][q] = reinterpret_cast<const u32x4_t*>(src)[q];
+        for (int q = 0; q < Q; ++q) d[t][q] = reinterpret_cast<const u32x4_t*>(src)[q];
+    }
+    asm volatile("" ::: "memory");  // keep the weight loads behind these
+    const bool valid = e >= 0 && e < a.E;
+    const float wg = valid ? w_raw : 0.f;
+    if (!valid) e = 0;  // a readable expert; its contribution is multiplied by 0
+    const int row0 = blockIdx.x * RW * R + wave * R;
+    u32x4_t cr[R][NVD], cs[R][NVS > 0 ? NVS : 1];
+    float sr[R][NVD], br[R][NVD], ss[R][NVS > 0 ? NVS : 1], bs[R][NVS > 0 ? NVS : 1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t n = min(row0 + r, D - 1);
+        const uint8_t *cp, *sp, *bp;
+        m1_row<S>(a.down, e, n, F, cp, sp, bp);
+#pragma unroll
+        for (int t = 0; t < NVD; ++t) {
+            const int v = min(sl + 8 * t, VRF - 1);
+            cr[r][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cp) + v);
+            m1_scale<S>(sp, bp, v / T::VPG, sr[r][t], br[r][t]);
         }
+        if constexpr (NVS > 0) {
+            m1_row<S>(a.sdown, 0, n, Fs, cp, sp, bp);
+#pragma unroll
+            for (int t = 0; t < NVS; ++t) {
+                const int v = min(lane + 64 * t, VRS - 1);
+                cs[r][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cp) + v);
+                m1_scale<S>(sp, bp, v / T::VPG, ss[r][t], bs[r][t]);
+            }
+        }
+    }
+    // commit the staged rows (waits for them only; the weights stay in flight)
+    {
         constexpr uint32_t ONES = 0x3F803F80u;
 #pragma unroll
         for (int t = 0; t < XV; ++t) {
-            const int i = lane + 64 * t;
+            const int i = (int)threadIdx.x + NT * t;
             if (i >= total) break;
             const bool sh = i >= k * VRF;
             uint32_t* reg = sh ? sbase : smem + (i / VRF) * regw;
             const int v = sh ? i - k * VRF : i % VRF;
-            const int vr = sh ? VRS : VRF;
             float sum = 0.f;
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
@@ -199,39 +233,6 @@ __global__ __launch_bounds__(320) void moe1_down_kernel(Moe1Args a) {
                 sum = dot2_bf16(ONES, ev[3], sum);
             }
             reinterpret_cast<float*>(reg + (sh ? Fs / 2 : F / 2))[v] = sum;
-            (void)vr;
-        }
-        __syncthreads();
-        return;
-    }
-
-    const int g = lane >> 3, sl = lane & 7;
-    int e = g < k ? a.ids[g] : -1;
-    const bool valid = e >= 0 && e < a.E;
-    const float wg = valid ? a.wts[g] : 0.f;
-    if (!valid) e = 0;  // a readable expert; its contribution is multiplied by 0
-    const int row0 = blockIdx.x * 4 * R + wave * R;
-    u32x4_t cr[R][NVD], cs[R][NVS > 0 ? NVS : 1];
-    float sr[R][NVD], br[R][NVD], ss[R][NVS > 0 ? NVS : 1], bs[R][NVS > 0 ? NVS : 1];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int64_t n = min(row0 + r, D - 1);
-        const uint8_t *cp, *sp, *bp;
-        m1_row<S>(a.down, e, n, F, cp, sp, bp);
-#pragma unroll
-        for (int t = 0; t < NVD; ++t) {
-            const int v = min(sl + 8 * t, VRF - 1);
-            cr[r][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cp) + v);
-            m1_scale<S>(sp, bp, v / T::VPG, sr[r][t], br[r][t]);
-        }
-        if constexpr (NVS > 0) {
-            m1_row<S>(a.sdown, 0, n, Fs, cp, sp, bp);
-#pragma unroll
-            for (int t = 0; t < NVS; ++t) {
-                const int v = min(lane + 64 * t, VRS - 1);
-                cs[r][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cp) + v);
-                m1_scale<S>(sp, bp, v / T::VPG, ss[r][t], bs[r][t]);
-            }
         }
     }
     __syncthreads();
