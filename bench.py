@@ -313,13 +313,23 @@ def run_moe(c: Ctx, a):
 
     lib = w4.lib()
 
+    # One token: router GEMV, then selection + experts in one call (the
+    # selection runs inside the gate/up pass). Several tokens: the fused
+    # router/top-k kernel, then the experts.
+    one = M == 1
+
     def step():
         st = torch.cuda.current_stream(c.dev).cuda_stream
         for l, (router, gate, up, down, shared) in enumerate(L):
-            rd = router.desc()
-            w4._check(lib.w4_moe_route(ctypes.byref(rd), x.data_ptr(), M, k, logits.data_ptr(),
-                                       ids[l].data_ptr(), wts[l].data_ptr(), st))
-            w4.moe_gemv(gate, up, down, x, ids[l], wts[l], shared=shared, workspace=ws, y=y)
+            if one:
+                w4.gemv_into(router, x, logits)
+                w4.moe_gemv_logits(gate, up, down, x, logits, top_k=k, shared=shared, workspace=ws,
+                                   y=y, ids=ids[l], weights=wts[l])
+            else:
+                rd = router.desc()
+                w4._check(lib.w4_moe_route(ctypes.byref(rd), x.data_ptr(), M, k, logits.data_ptr(),
+                                           ids[l].data_ptr(), wts[l].data_ptr(), st))
+                w4.moe_gemv(gate, up, down, x, ids[l], wts[l], shared=shared, workspace=ws, y=y)
 
     g = c.graph(step)
     ms = c.time_graph(g, a.steps, a.warmup)
@@ -334,12 +344,14 @@ def run_moe(c: Ctx, a):
                         "workload": "gemma-4-26b-a4b-shaped MoE FFN stack", "layers": layers, "M": M,
                         "experts": E, "top_k": k, "d_model": D, "expert_ffn": F, "shared_ffn": Fs,
                         "scheme": "aff4_g64 experts/shared, aff8_g64 router",
-                        "launches_per_layer": "router gemv, top-k, bucket, gate/up, down, combine"})
+                        "launches_per_layer": ("router gemv, gate/up with the top-k inside, down" if one else
+                                               "router gemv + top-k, bucket, gate/up, down, combine")})
     out["hbm_TBps"] = round(tbs, 4)
     out["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
     out["distinct_experts_per_layer"] = sum(distinct) / len(distinct)
     out["step_bytes"] = step_bytes
-    out["roofline"] = hbm_roofline("whole MoE layer (6 launches)", step_bytes // layers, ms * 1e3 / layers)
+    out["roofline"] = hbm_roofline(f"whole MoE layer ({3 if one else 5} launches)", step_bytes // layers,
+                                   ms * 1e3 / layers)
     return out
 
 

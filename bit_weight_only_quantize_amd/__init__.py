@@ -61,6 +61,9 @@ _SIGS = {
     "w4_moe_workspace_bytes": ([_I64, ctypes.c_int, _I64, _I64, _I64, _I64], ctypes.c_size_t),
     "w4a16_moe_gemv": ([ctypes.POINTER(_W4Matrix)] * 6 + [_P, _I64, _P, _P, ctypes.c_int, _P,
                                                           ctypes.c_size_t, _P, _P], ctypes.c_int),
+    "w4a16_moe_gemv_logits": ([ctypes.POINTER(_W4Matrix)] * 6 + [_P, _I64, _P, ctypes.c_int, _P, _P,
+                                                                 _P, ctypes.c_size_t, _P, _P],
+                              ctypes.c_int),
 }
 
 
@@ -235,6 +238,34 @@ def moe_route(router: QuantizedMatrix, x: torch.Tensor, top_k: int = 8):
 
 def moe_workspace_bytes(M: int, top_k: int, E: int, D: int, F: int, Fs: int = 0) -> int:
     return int(lib().w4_moe_workspace_bytes(M, top_k, E, D, F, Fs))
+
+
+def moe_gemv_logits(gate: QuantizedMatrix, up: QuantizedMatrix, down: QuantizedMatrix,
+                    x: torch.Tensor, logits: torch.Tensor, top_k: int = 8, shared=None,
+                    workspace=None, y: Optional[torch.Tensor] = None, ids=None, weights=None):
+    """Selection from router logits [M][E] and the MoE FFN in one call: (y, ids, weights)."""
+    x = _as_bf16_bits(x, "x")
+    M = x.shape[0]
+    E, F, D = gate.num_experts, gate.N, gate.K
+    if logits.dtype != torch.float32 or tuple(logits.shape) != (M, E) or not logits.is_contiguous():
+        raise ValueError(f"logits must be contiguous fp32 [{M}][{E}]")
+    Fs = shared[0].N if shared is not None else 0
+    need = moe_workspace_bytes(M, top_k, E, D, F, Fs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if y is None:
+        y = torch.empty((M, D), dtype=torch.float32, device=x.device)
+    if ids is None:
+        ids = torch.empty((M, top_k), dtype=torch.int32, device=x.device)
+    if weights is None:
+        weights = torch.empty((M, top_k), dtype=torch.float32, device=x.device)
+    descs = [m.desc() for m in (gate, up, down)]
+    sh = [s.desc() for s in shared] if shared is not None else [None, None, None]
+    refs = [ctypes.byref(d) for d in descs] + [ctypes.byref(s) if s is not None else None for s in sh]
+    _check(lib().w4a16_moe_gemv_logits(*refs, _ptr(x), M, _ptr(logits), top_k, _ptr(ids),
+                                       _ptr(weights), _ptr(workspace), workspace.numel(), _ptr(y),
+                                       _stream(x.device)))
+    return y, ids, weights
 
 
 def moe_gemv(gate: QuantizedMatrix, up: QuantizedMatrix, down: QuantizedMatrix, x: torch.Tensor,

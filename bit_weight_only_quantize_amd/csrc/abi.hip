@@ -205,16 +205,16 @@ size_t w4_moe_workspace_bytes(int64_t M, int top_k, int64_t E, int64_t D, int64_
     return w4::moe_workspace_layout(M, top_k, E, D, F, Fs).total;
 }
 
-int w4a16_moe_gemv(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
-                   const w4_matrix* shared_gate, const w4_matrix* shared_up,
-                   const w4_matrix* shared_down, const uint16_t* x, int64_t M,
-                   const int32_t* ids, const float* weights, int top_k, void* workspace,
-                   size_t workspace_bytes, float* y, void* stream) {
+// Checks shared by the two MoE entry points; fills W and the scheme.
+static int moe_check(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
+                     const w4_matrix* shared_gate, const w4_matrix* shared_up,
+                     const w4_matrix* shared_down, int64_t M, int top_k, w4::MoeMats& W,
+                     int& scheme) {
     int rc;
     if ((rc = check_matrix(gate, "gate", 0)) || (rc = check_matrix(up, "up", 0)) ||
         (rc = check_matrix(down, "down", 0)))
         return rc;
-    const int scheme = gate->scheme;
+    scheme = gate->scheme;
     if (scheme == W4_AFF8_G64) return fail(W4_EINVAL, "experts must use a 4-bit scheme");
     const int64_t E = gate->num_experts, F = gate->N, D = gate->K;
     if (up->scheme != scheme || down->scheme != scheme)
@@ -243,19 +243,10 @@ int w4a16_moe_gemv(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* 
     }
     if (top_k < 1 || top_k > 32) return fail(W4_ESHAPE, "top_k=%d out of range [1, 32]", top_k);
     if (M < 0 || M > 256) return fail(W4_ESHAPE, "M=%lld out of range [0, 256]", (long long)M);
-    if (M == 0 || D == 0) return ok();
-    if (F < 1) return fail(W4_ESHAPE, "F must be positive");
+    if (M > 0 && D > 0 && F < 1) return fail(W4_ESHAPE, "F must be positive");
     if (D > w4::kMaxSkinnyK / 4 || F > w4::kMaxSkinnyK / 4 || Fs > w4::kMaxSkinnyK / 4)
         return fail(W4_ESHAPE, "D, F and Fs must not exceed %lld", (long long)(w4::kMaxSkinnyK / 4));
-    if (!x || !ids || !weights || !y || !workspace)
-        return fail(W4_EINVAL, "null x, ids, weights, y or workspace");
-    if (!aligned16(x) || !aligned16(ids) || !aligned16(weights) || !aligned16(y) ||
-        !aligned16(workspace))
-        return fail(W4_EALIGN, "x, ids, weights, y and workspace must be 16-byte aligned");
-    const size_t need = w4::moe_workspace_layout(M, top_k, E, D, F, Fs).total;
-    if (workspace_bytes < need)
-        return fail(W4_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-    w4::MoeMats W{};
+    W = w4::MoeMats{};
     W.E = E; W.D = D; W.F = F; W.Fs = Fs;
     const w4_matrix* mats[6] = {gate, up, down, shared_gate, shared_up, shared_down};
     const void** dst[6] = {W.gate, W.up, W.down, W.sgate, W.sup, W.sdown};
@@ -265,9 +256,54 @@ int w4a16_moe_gemv(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* 
         dst[i][1] = mats[i]->scale;
         dst[i][2] = mats[i]->bias;
     }
+    return W4_OK;
+}
+
+int w4a16_moe_gemv(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
+                   const w4_matrix* shared_gate, const w4_matrix* shared_up,
+                   const w4_matrix* shared_down, const uint16_t* x, int64_t M,
+                   const int32_t* ids, const float* weights, int top_k, void* workspace,
+                   size_t workspace_bytes, float* y, void* stream) {
+    w4::MoeMats W;
+    int scheme = 0;
+    const int rc = moe_check(gate, up, down, shared_gate, shared_up, shared_down, M, top_k, W, scheme);
+    if (rc) return rc;
+    if (M == 0 || W.D == 0) return ok();
+    if (!x || !ids || !weights || !y || !workspace)
+        return fail(W4_EINVAL, "null x, ids, weights, y or workspace");
+    if (!aligned16(x) || !aligned16(ids) || !aligned16(weights) || !aligned16(y) ||
+        !aligned16(workspace))
+        return fail(W4_EALIGN, "x, ids, weights, y and workspace must be 16-byte aligned");
+    const size_t need = w4::moe_workspace_layout(M, top_k, W.E, W.D, W.F, W.Fs).total;
+    if (workspace_bytes < need)
+        return fail(W4_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     return hip_status(w4::launch_moe(scheme, W, x, M, ids, weights, top_k, workspace, y,
                                      (hipStream_t)stream),
                       "moe_gemv launch");
+}
+
+int w4a16_moe_gemv_logits(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
+                          const w4_matrix* shared_gate, const w4_matrix* shared_up,
+                          const w4_matrix* shared_down, const uint16_t* x, int64_t M,
+                          const float* logits, int top_k, int32_t* ids, float* weights,
+                          void* workspace, size_t workspace_bytes, float* y, void* stream) {
+    w4::MoeMats W;
+    int scheme = 0;
+    const int rc = moe_check(gate, up, down, shared_gate, shared_up, shared_down, M, top_k, W, scheme);
+    if (rc) return rc;
+    if (top_k > W.E) return fail(W4_ESHAPE, "top_k=%d exceeds E=%lld", top_k, (long long)W.E);
+    if (M == 0 || W.D == 0) return ok();
+    if (!x || !logits || !ids || !weights || !y || !workspace)
+        return fail(W4_EINVAL, "null x, logits, ids, weights, y or workspace");
+    if (!aligned16(x) || !aligned16(logits) || !aligned16(ids) || !aligned16(weights) ||
+        !aligned16(y) || !aligned16(workspace))
+        return fail(W4_EALIGN, "x, logits, ids, weights, y and workspace must be 16-byte aligned");
+    const size_t need = w4::moe_workspace_layout(M, top_k, W.E, W.D, W.F, W.Fs).total;
+    if (workspace_bytes < need)
+        return fail(W4_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    return hip_status(w4::launch_moe_logits(scheme, W, x, M, logits, top_k, ids, weights,
+                                            workspace, y, (hipStream_t)stream),
+                      "moe_gemv_logits launch");
 }
 
 }  // extern "C"

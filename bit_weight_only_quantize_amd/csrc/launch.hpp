@@ -73,5 +73,10 @@ hipError_t launch_route(int scheme, const void* codes, const void* scale, const 
                         int32_t* ids, float* wts, hipStream_t st);
 hipError_t launch_moe(int scheme, const MoeMats& W, const uint16_t* x, int64_t M, const int32_t* ids,
                       const float* wts, int k, void* ws, float* y, hipStream_t st);
+// Top-k selection from router logits [M][E], then launch_moe; ids/wts are
+// outputs. One token with E <= 128: the selection runs inside the gate/up pass.
+hipError_t launch_moe_logits(int scheme, const MoeMats& W, const uint16_t* x, int64_t M,
+                             const float* logits, int k, int32_t* ids, float* wts, void* ws,
+                             float* y, hipStream_t st);
 
 }  // namespace w4

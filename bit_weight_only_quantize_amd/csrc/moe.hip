@@ -28,75 +28,6 @@
 namespace w4 {
 
 // ---------------------------------------------------------------- routing
-// Wave-wide reductions over DPP (row steps, then row_bcast15/31 into lane 63)
-// and a readlane broadcast: no LDS round trips. Lanes a DPP step does not
-// write keep their own value (old = src), the identity for max and min.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ int dpp_keep(int v) {
-    return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xF, false);
-}
-template <typename Op>
-__device__ __forceinline__ int wave_reduce_i(int v, Op op) {
-    v = op(v, dpp_keep<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
-    v = op(v, dpp_keep<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
-    v = op(v, dpp_keep<0x141, 0xF>(v));  // row_half_mirror
-    v = op(v, dpp_keep<0x140, 0xF>(v));  // row_mirror
-    v = op(v, dpp_keep<0x142, 0xA>(v));  // row_bcast15
-    v = op(v, dpp_keep<0x143, 0xC>(v));  // row_bcast31
-    return __builtin_amdgcn_readlane(v, 63);
-}
-__device__ __forceinline__ float wave_max_dpp(float v) {
-    return __int_as_float(wave_reduce_i(__float_as_int(v), [](int a, int b) {
-        return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
-    }));
-}
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-    return __int_as_float(wave_reduce_i(__float_as_int(v), [](int a, int b) {
-        return __float_as_int(__int_as_float(a) + __int_as_float(b));
-    }));
-}
-__device__ __forceinline__ int wave_min_dpp(int v) {
-    return wave_reduce_i(v, [](int a, int b) { return a < b ? a : b; });
-}
-
-// Top-k of one token's E <= 64 * EPL logits, in one wavefront: v holds lane's
-// logits e = lane + 64 j (-inf past E). The selection is the first k of a
-// stable sort by logit descending: k rounds of a wave-wide arg-max (highest
-// logit, then lowest expert index), each winner masked out. Weights: softmax
-// over all E raw logits, not renormalized. Register and DPP work only.
-template <int EPL>
-__device__ __forceinline__ void topk_rounds(const float (&v)[EPL], int E, int k,
-                                            int32_t* __restrict__ ids, float* __restrict__ wts) {
-    const int lane = threadIdx.x & 63;
-    float mx = v[0];
-#pragma unroll
-    for (int j = 1; j < EPL; ++j) mx = fmaxf(mx, v[j]);
-    mx = wave_max_dpp(mx);
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) s += expf(v[j] - mx);
-    const float inv = 1.f / wave_sum_dpp(s);
-    unsigned taken = 0;
-    for (int r = 0; r < k; ++r) {
-        float bv = -INFINITY;
-        int be = 0x7FFFFFFF;
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) {  // this lane's best untaken (lowest index on ties)
-            const int e = lane + 64 * j;
-            const bool ok = e < E && !((taken >> j) & 1u) && (v[j] > bv || be == 0x7FFFFFFF);
-            bv = ok ? v[j] : bv;
-            be = ok ? e : be;
-        }
-        const float gv = wave_max_dpp(bv);
-        const int ge = wave_min_dpp(be != 0x7FFFFFFF && bv == gv ? be : 0x7FFFFFFF);
-        if ((ge & 63) == lane) taken |= 1u << (ge >> 6);
-        if (lane == 0) {
-            ids[r] = ge;
-            wts[r] = expf(gv - mx) * inv;
-        }
-    }
-}
-
 // One wavefront per token over precomputed logits. EPL is as small as E
 // allows: a single wavefront on a CU whose instruction cache is cold pays for
 // every line of code it executes.
@@ -561,7 +492,7 @@ static void pick_nvs(int nvs, const Moe1Args& a, int xv, int blocks, size_t lds,
 // pass's activations (x: at most 128 vectors; h and hs: at most 384).
 constexpr int kMoe1RW = 4;
 
-template <int S>
+template <int S, bool SEL = false>
 static hipError_t moe1_passes(Moe1Args a, hipStream_t st) {
     constexpr int R = 2;
     const int kv = Traits<S>::KV;
@@ -570,11 +501,15 @@ static hipError_t moe1_passes(Moe1Args a, hipStream_t st) {
     const int blocks = a.k * a.tiles_r + a.tiles_s;
     const size_t lds = (size_t)(a.D / 2 + a.D / kv) * 4;
     if (a.D / kv <= 64)
-        hipLaunchKernelGGL((moe1_gate_up_kernel<S, 1, R, 1, kMoe1RW>), dim3(blocks), dim3(64 * kMoe1RW), lds, st, a);
+        hipLaunchKernelGGL((moe1_gate_up_kernel<S, 1, R, 1, kMoe1RW, SEL>), dim3(blocks), dim3(64 * kMoe1RW), lds, st, a);
     else
-        hipLaunchKernelGGL((moe1_gate_up_kernel<S, 2, R, 1, kMoe1RW>), dim3(blocks), dim3(64 * kMoe1RW), lds, st, a);
+        hipLaunchKernelGGL((moe1_gate_up_kernel<S, 2, R, 1, kMoe1RW, SEL>), dim3(blocks), dim3(64 * kMoe1RW), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if constexpr (SEL) {  // the down pass reads the selection the gate/up pass published
+        a.ids = a.ids_out;
+        a.wts = a.wts_out;
+    }
     const int VRF = a.F / kv, VRS = a.has_shared ? a.Fs / kv : 0;
     const int nvd = (VRF + 7) / 8, nvs = (VRS + 63) / 64;
     const int xv = (a.k * VRF + VRS + 64 * kMoe1RW - 1) / (64 * kMoe1RW);
@@ -589,27 +524,60 @@ static hipError_t moe1_passes(Moe1Args a, hipStream_t st) {
     return hipGetLastError();
 }
 
+static Moe1Args moe1_args(int scheme, const MoeMats& W, const uint16_t* x, int k, void* ws, float* y) {
+    const int64_t E = W.E, D = W.D, F = W.F, Fs = W.Fs;
+    const MoeWorkspace L = moe_workspace_layout(1, k, E, D, F, Fs);
+    uint8_t* base = (uint8_t*)ws;
+    Moe1Args a{};
+    a.gate = m1m(W.gate, F, D, scheme);
+    a.up = m1m(W.up, F, D, scheme);
+    a.down = m1m(W.down, D, F, scheme);
+    a.has_shared = Fs > 0;
+    if (Fs > 0) {
+        a.sgate = m1m(W.sgate, Fs, D, scheme);
+        a.sup = m1m(W.sup, Fs, D, scheme);
+        a.sdown = m1m(W.sdown, D, Fs, scheme);
+    }
+    a.k = k; a.E = (int)E; a.D = (int)D; a.F = (int)F; a.Fs = (int)Fs;
+    a.x = x;
+    a.h = (uint16_t*)(base + L.h);
+    a.hs = (uint16_t*)(base + L.hs);
+    a.y = y;
+    return a;
+}
+
+hipError_t launch_moe_logits(int scheme, const MoeMats& W, const uint16_t* x, int64_t M,
+                             const float* logits, int k, int32_t* ids, float* wts, void* ws,
+                             float* y, hipStream_t st) {
+    const int64_t E = W.E;
+    if (moe1_ok(M, k, W.D, W.F, W.Fs) && E <= 128) {
+        Moe1Args a = moe1_args(scheme, W, x, k, ws, y);
+        a.logits = logits;
+        a.ids_out = ids;
+        a.wts_out = wts;
+        return scheme == SYM4_G128 ? moe1_passes<SYM4_G128, true>(a, st)
+                                   : moe1_passes<AFF4_G64, true>(a, st);
+    }
+    if (E <= 128)
+        hipLaunchKernelGGL(topk_softmax_kernel<2>, dim3((unsigned)M), dim3(64), 0, st, logits, (int)E, k, ids, wts);
+    else if (E <= 256)
+        hipLaunchKernelGGL(topk_softmax_kernel<4>, dim3((unsigned)M), dim3(64), 0, st, logits, (int)E, k, ids, wts);
+    else
+        hipLaunchKernelGGL(topk_softmax_kernel<16>, dim3((unsigned)M), dim3(64), 0, st, logits, (int)E, k, ids, wts);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_moe(scheme, W, x, M, ids, wts, k, ws, y, st);
+}
+
 hipError_t launch_moe(int scheme, const MoeMats& W, const uint16_t* x, int64_t M, const int32_t* ids,
                       const float* wts, int k, void* ws, float* y, hipStream_t st) {
     const int64_t E = W.E, D = W.D, F = W.F, Fs = W.Fs;
     const MoeWorkspace L = moe_workspace_layout(M, k, E, D, F, Fs);
     uint8_t* base = (uint8_t*)ws;
     if (moe1_ok(M, k, D, F, Fs)) {
-        Moe1Args a{};
-        a.gate = m1m(W.gate, F, D, scheme);
-        a.up = m1m(W.up, F, D, scheme);
-        a.down = m1m(W.down, D, F, scheme);
-        a.has_shared = Fs > 0;
-        if (Fs > 0) {
-            a.sgate = m1m(W.sgate, Fs, D, scheme);
-            a.sup = m1m(W.sup, Fs, D, scheme);
-            a.sdown = m1m(W.sdown, D, Fs, scheme);
-        }
-        a.k = k; a.E = (int)E; a.D = (int)D; a.F = (int)F; a.Fs = (int)Fs;
-        a.x = x; a.ids = ids; a.wts = wts;
-        a.h = (uint16_t*)(base + L.h);
-        a.hs = (uint16_t*)(base + L.hs);
-        a.y = y;
+        Moe1Args a = moe1_args(scheme, W, x, k, ws, y);
+        a.ids = ids;
+        a.wts = wts;
         return scheme == SYM4_G128 ? moe1_passes<SYM4_G128>(a, st) : moe1_passes<AFF4_G64>(a, st);
     }
     MoeArgs a{};

@@ -22,6 +22,7 @@
 #include "common.hpp"
 #include "gemv_wave.hpp"
 #include "skinny.hpp"
+#include "topk.hpp"
 
 namespace w4 {
 
@@ -38,6 +39,11 @@ struct Moe1Args {
     const uint16_t* x;   // [D]
     const int32_t* ids;  // [k]
     const float* wts;    // [k]
+    // selection inside the gate/up pass (SEL): router logits [E] in, the
+    // selected ids and weights out (written by workgroup 0)
+    const float* logits;
+    int32_t* ids_out;
+    float* wts_out;
     uint16_t* h;         // [k][F] bf16
     uint16_t* hs;        // [Fs] bf16
     float* y;            // [D]
@@ -68,7 +74,11 @@ __device__ __forceinline__ void m1_scale(const uint8_t* s, const uint8_t* b, int
 }
 
 // ---------------------------------------------------------------- gate/up
-template <int S, int NV, int R, int XV, int RW>
+// SEL: the workgroup selects the token's experts itself from the router
+// logits (E <= 128, one wavefront, the same top-k as the routing kernel), so no
+// launch of its own is needed for the selection; workgroup 0 publishes the
+// selection for the down pass and the caller.
+template <int S, int NV, int R, int XV, int RW, bool SEL>
 __global__ __launch_bounds__(64 * RW) void moe1_gate_up_kernel(Moe1Args a) {
     using T = Traits<S>;
     using L = XLayout<S, 1>;
@@ -82,10 +92,33 @@ __global__ __launch_bounds__(64 * RW) void moe1_gate_up_kernel(Moe1Args a) {
     const int tile = shared ? bid - a.k * a.tiles_r : bid % a.tiles_r;
     // the expert id, then this wavefront's share of the activations (they do
     // not depend on the id), then the weights
-    const int e = shared ? 0 : a.ids[slot];
+    int e = 0;
+    if constexpr (!SEL) e = shared ? 0 : a.ids[slot];
     XStage<S, XV, 64 * RW> xstage;
     xstage.fetch(a.x, VR, threadIdx.x);
     asm volatile("" ::: "memory");  // keep the weight loads behind these
+    if constexpr (SEL) {
+        if (!shared) {  // block-uniform
+            __shared__ int32_t sel_id[8];
+            __shared__ float sel_w[8];
+            if (wave == 0) {
+                float v[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int ei = lane + 64 * j;
+                    const float l = a.logits[min(ei, a.E - 1)];
+                    v[j] = ei < a.E ? l : -INFINITY;
+                }
+                topk_rounds<2>(v, a.E, a.k, sel_id, sel_w);
+            }
+            __syncthreads();
+            e = sel_id[slot];
+            if (bid == 0 && threadIdx.x < a.k) {
+                a.ids_out[threadIdx.x] = sel_id[threadIdx.x];
+                a.wts_out[threadIdx.x] = sel_w[threadIdx.x];
+            }
+        }
+    }
     if (!shared && (e < 0 || e >= a.E)) return;  // whole block: nothing routed to this slot
     const int N = shared ? a.Fs : a.F;
     uint32_t* xs = smem;

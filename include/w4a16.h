@@ -165,6 +165,27 @@ int w4a16_moe_gemv(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* 
                    const uint16_t* x, int64_t M, const int32_t* ids, const float* weights,
                    int top_k, void* workspace, size_t workspace_bytes, float* y, void* stream);
 
+/*
+ * Router selection and the MoE FFN in one call, from router logits computed
+ * beforehand (e.g. by w4a16_gemv on the router): the selection of
+ * w4_moe_route ([TurboFieldfare], model section: top_k experts by logit,
+ * largest first, ties to the lower expert index; softmax probabilities over all
+ * E raw logits, no softcap, not renormalized), then w4a16_moe_gemv with it.
+ * For one token with E <= 128 the selection runs inside the expert launches
+ * instead of in a launch of its own.
+ * logits: fp32 [M][E], E = the experts' count. Outputs: ids int32 [M][top_k],
+ * weights fp32 [M][top_k], y fp32 [M][D]; ids and weights equal what
+ * w4_moe_route selects from the same logits, bit for bit. Everything else
+ * (matrices, shapes, workspace, errors) as for w4a16_moe_gemv;
+ * 1 <= top_k <= min(E, 32).
+ */
+int w4a16_moe_gemv_logits(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
+                          const w4_matrix* shared_gate, const w4_matrix* shared_up,
+                          const w4_matrix* shared_down,
+                          const uint16_t* x, int64_t M, const float* logits, int top_k,
+                          int32_t* ids, float* weights, void* workspace, size_t workspace_bytes,
+                          float* y, void* stream);
+
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char* w4_last_error(void);
 

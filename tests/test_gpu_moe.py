@@ -157,3 +157,40 @@ def test_moe_single_token_fast_path_edges(scheme, k, ids_row, shared):
     ids = np.array([ids_row], dtype=np.int32)
     p = np.linspace(0.3, 0.05, k)[None, :]
     _moe_case(1, E, D, F, Fs if shared else 0, k, scheme, 7, f"m1.{scheme}.{k}.{int(shared)}", ids=ids, p=p)
+
+
+def _dev_stack(E, N, K, seed, name, scheme):
+    q = w4.empty_quantized(scheme, N, K, num_experts=E)
+    for e in range(E):
+        w4.quantize_pack(dev_f32(synth.weights(N, K, 0.02, seed, f"{name}.{e}")), scheme, out=q, expert=e)
+    return q
+
+
+@pytest.mark.parametrize("M,E,F,Fs,k", [
+    (1, 128, 768, 2048, 8),   # one token, E <= 128: selection inside the gate/up pass
+    (1, 64, 256, 0, 3),       # same path, fewer slots, no shared expert
+    (1, 256, 256, 512, 8),    # one token, E > 128: a top-k launch first
+    (2, 128, 256, 512, 8),    # several tokens: top-k launch, then the bucketed passes
+])
+def test_moe_gemv_logits_equals_route_then_gemv(M, E, F, Fs, k):
+    """w4a16_moe_gemv_logits from router logits gives, bit for bit, the ids and
+    weights w4_moe_route selects and the output w4a16_moe_gemv computes with them."""
+    D, scheme, seed = 2048, "aff4_g64", 11
+    tag = f"logits.{M}.{E}.{F}.{Fs}.{k}"
+    qr = w4.quantize_pack(dev_f32(synth.weights(E, D, 0.02, seed, f"{tag}.router")), "aff8_g64")
+    gate = _dev_stack(E, F, D, seed, f"{tag}.gate", scheme)
+    up = _dev_stack(E, F, D, seed, f"{tag}.up", scheme)
+    down = _dev_stack(E, D, F, seed, f"{tag}.down", scheme)
+    shared = None
+    if Fs:
+        shared = [w4.quantize_pack(dev_f32(synth.weights(n, kk, 0.02, seed, f"{tag}.s{nm}")), scheme)
+                  for n, kk, nm in ((Fs, D, "g"), (Fs, D, "u"), (D, Fs, "d"))]
+    x = dev_bf16(synth.activations_bf16(M, D, seed, f"{tag}.x"))
+    ids_r, w_r, logits = w4.moe_route(qr, x, top_k=k)
+    y_r = w4.moe_gemv(gate, up, down, x, ids_r, w_r, shared=shared)
+    for _ in range(2):  # the second call also checks nothing is left over from the first
+        y, ids, w = w4.moe_gemv_logits(gate, up, down, x, logits, top_k=k, shared=shared)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ids_r)
+        assert torch.equal(w, w_r)
+        assert torch.equal(y, y_r)
