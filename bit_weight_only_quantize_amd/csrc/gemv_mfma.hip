@@ -26,7 +26,8 @@ static void pick_mfma(int RT, int WK, const GemvGroupArgs& a, int blocks, int K,
                       const uint16_t* x, hipStream_t st) {
     if (RT == 2) {
         if (WK == 8) go_mfma<S, 2, 8>(a, blocks, K, M, x, st);
-        else go_mfma<S, 2, 4>(a, blocks, K, M, x, st);
+        else if (WK == 4) go_mfma<S, 2, 4>(a, blocks, K, M, x, st);
+        else go_mfma<S, 2, 2>(a, blocks, K, M, x, st);
     } else {
         if (WK == 8) go_mfma<S, 1, 8>(a, blocks, K, M, x, st);
         else go_mfma<S, 1, 4>(a, blocks, K, M, x, st);
@@ -39,12 +40,14 @@ hipError_t launch_gemv_mfma(int scheme, int count, const void* const* codes,
                             hipStream_t st) {
     int64_t total_rows = 0;
     for (int i = 0; i < count; ++i) total_rows += N[i];
-    // Measured on the 7B (sym) and 13B (affine) decode shapes: two row tiles
-    // per wavefront amortize the activation loads once a launch has many rows;
-    // eight split-K wavefronts give the smaller launches enough loads in flight.
+    // Measured on the 7B (sym) and 13B (affine) decode shapes at M = 4, 8, 16:
+    // two row tiles per wavefront amortize the activation loads once a launch
+    // has many rows (four do not pay); such launches run best with fewer
+    // split-K wavefronts (sym 2, affine 4), while eight give the smaller
+    // launches enough loads in flight.
     const bool big = scheme == AFF4_G64 || total_rows >= 16384;
     const int RT = big ? 2 : 1;
-    const int WK = (scheme == SYM4_G128 && big) ? 4 : 8;
+    const int WK = big ? (scheme == SYM4_G128 ? 2 : 4) : 8;
     GemvGroupArgs a{};
     int blocks = 0;
     for (int i = 0; i < count; ++i) {
