@@ -1,4 +1,6 @@
 // Launch side of the skinny MFMA decode GEMM (2 <= M <= 16, 4-bit schemes).
+#include <algorithm>
+
 #include "gemv_mfma.hpp"
 #include "launch.hpp"
 
@@ -34,17 +36,92 @@ static void pick_mfma(int RT, int WK, const GemvGroupArgs& a, int blocks, int K,
     }
 }
 
+// Activations in LDS (gemv_mfma_lds_kernel): one workgroup per CU holds TP =
+// ceil(tiles / CUs) tiles and splits each tile's steps over WK wavefronts, up
+// to 16 wavefronts in all, with x staged in as few chunks of steps as LDS
+// allows; launches of more than 16 tiles per CU take the split-K kernel.
+template <int S>
+static bool try_mfma_lds(int count, const void* const* codes, const void* const* scale,
+                         const void* const* bias, const int64_t* N, int64_t K,
+                         const uint16_t* x, int64_t M, float* const* y, hipStream_t st) {
+    constexpr int kCUs = 256, kMaxWaves = 16;
+    constexpr size_t kLds = 160 * 1024;
+    GemvGroupArgs a{};
+    int tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        a.codes[i] = (const uint8_t*)codes[i];
+        a.scale[i] = (const uint8_t*)scale[i];
+        a.bias[i] = (const uint8_t*)bias[i];
+        a.y[i] = y[i];
+        a.N[i] = (int)N[i];
+        a.tile_start[i] = tiles;
+        tiles += (int)((N[i] + 15) / 16);
+    }
+    a.tile_start[count] = tiles;
+    a.count = count;
+    if (tiles == 0) return false;
+    const int TP = (tiles + kCUs - 1) / kCUs;
+    if (TP > kMaxWaves) return false;
+    const MfmaLdsLayout<S> whole((int)K, (int)M, 1);
+    const int steps = whole.steps, GPS = whole.GPS;
+    int WK = std::min(std::max(1, kMaxWaves / TP), steps);
+    // every K-slice of a whole-K chunk non-empty
+    while (WK > 1 && (WK - 1) * ((steps + WK - 1) / WK) >= steps) --WK;
+    const int nw = TP * WK;
+    // the staging lanes of one group of all tokens must fit the workgroup
+    if (64 * nw < whole.mp * (Traits<S>::GROUP / 8)) return false;
+    // fewest chunks whose activations, sums and scale blocks fit in LDS
+    int CS = 0, SG = 0, spw = 0;
+    size_t lds = 0;
+    for (int chunks = 1; chunks <= steps; ++chunks) {
+        CS = (steps + chunks - 1) / chunks;
+        spw = (CS + WK - 1) / WK;
+        const int sgmax = std::min(spw * GPS, whole.groups);
+        if (sgmax > 64) continue;
+        SG = sgmax <= 16 ? 16 : sgmax <= 32 ? 32 : 64;
+        lds = MfmaLdsLayout<S>((int)K, (int)M, CS).bytes() + (size_t)nw * 16 * (SG + 1) * 4;
+        lds = std::max(lds, WK > 1 ? (size_t)nw * 64 * 16 : (size_t)0);
+        if (lds <= kLds) break;
+        lds = 0;
+    }
+    if (lds == 0) return false;
+    const int grid = (tiles + TP - 1) / TP;
+    auto go = [&](auto kern) {
+        if (lds > 64 * 1024)
+            (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * nw), lds, st, a, (int)K, (int)M, x, tiles, TP, WK, CS);
+    };
+    // measured on the 7B and 13B decode shapes: four steps in flight beat
+    // eight; slices under four steps take two. The chunk loop costs the
+    // registers of two more steps in flight, so chunked launches keep two.
+    auto by_depth = [&](auto sgc) {
+        constexpr int G = decltype(sgc)::value;
+        if (CS < steps) go(gemv_mfma_lds_kernel<S, 2, G, true>);
+        else if (spw >= 4) go(gemv_mfma_lds_kernel<S, 4, G, false>);
+        else go(gemv_mfma_lds_kernel<S, 2, G, false>);
+    };
+    if (SG == 16) by_depth(std::integral_constant<int, 16>{});
+    else if (SG == 32) by_depth(std::integral_constant<int, 32>{});
+    else by_depth(std::integral_constant<int, 64>{});
+    return true;
+}
+
 hipError_t launch_gemv_mfma(int scheme, int count, const void* const* codes,
                             const void* const* scale, const void* const* bias, const int64_t* N,
                             int64_t K, const uint16_t* x, int64_t M, float* const* y,
                             hipStream_t st) {
+    if (scheme == SYM4_G128 ? try_mfma_lds<SYM4_G128>(count, codes, scale, bias, N, K, x, M, y, st)
+                            : try_mfma_lds<AFF4_G64>(count, codes, scale, bias, N, K, x, M, y, st))
+        return hipGetLastError();
     int64_t total_rows = 0;
     for (int i = 0; i < count; ++i) total_rows += N[i];
-    // Measured on the 7B (sym) and 13B (affine) decode shapes at M = 4, 8, 16:
-    // two row tiles per wavefront amortize the activation loads once a launch
-    // has many rows (four do not pay); such launches run best with fewer
-    // split-K wavefronts (sym 2, affine 4), while eight give the smaller
-    // launches enough loads in flight.
+    // The split-K kernel takes what the LDS kernel does not: more than 16 row
+    // tiles per CU (the 13B tied head) and launches too small for one
+    // workgroup of staging lanes. Measured on the 7B (sym) and 13B (affine)
+    // decode shapes at M = 4, 8, 16: two row tiles per wavefront amortize the
+    // activation loads once a launch has many rows (four do not pay); such
+    // launches run best with fewer split-K wavefronts (sym 2, affine 4),
+    // while eight give the smaller launches enough loads in flight.
     const bool big = scheme == AFF4_G64 || total_rows >= 16384;
     const int RT = big ? 2 : 1;
     const int WK = big ? (scheme == SYM4_G128 ? 2 : 4) : 8;

@@ -350,4 +350,305 @@ __global__ __launch_bounds__(64 * WK) void gemv_mfma_kernel(GemvGroupArgs a, int
     }
 }
 
+// ---------------------------------------------------------------- activations in LDS
+// Variant for launches of at most 16 tiles per CU. One workgroup per CU
+// stages x in LDS, already permuted into the MFMA A-operand layout and with
+// every (group, token) activation sum, so a step costs a wavefront one
+// 16-byte code load, four LDS reads, one LDS scale read per group and the
+// MFMAs of one 16-row tile: no per-step activation loads, permutes or sum
+// MFMAs, which cost more than the weight stream itself in the kernel above
+// once M reaches 8-16. The workgroup owns TP consecutive 16-row tiles; each
+// tile's steps are split over WK wavefronts (K-slices) whose partial sums
+// meet in LDS at the end, so a CU has TP * WK wavefronts streaming codes.
+// When x does not fit, the steps go in chunks of CS: the workgroup stages a
+// chunk, its wavefronts run their slices of it, and the next chunk replaces
+// it after a barrier.
+//   LDS words: A unit (s, d, g, t) -- the 8 activations of piece d of lane
+//   group g at chunk step s for token t, as the MFMA operand (x0,x4)(x1,x5)
+//   (x2,x6)(x3,x7) -- in row (s * 4 + d) * 4 + g of Mp units (M rounded up
+//   to a power of two), at column t ^ swz(Mp, d * 4 + g); then the sums as
+//   floats [(s * GPS + q) * 16 + t]; then one scale block per wavefront.
+//   The swizzle sends the 16 rows of a step that the staging lanes of one
+//   (group, token) pair write to 16 different bank slots, and keeps every
+//   row a permutation of its tokens for the readers. After the last chunk
+//   the same memory holds the K-slices' partial tiles.
+template <int S>
+struct MfmaLdsLayout {
+    static constexpr int GPS = MfmaStep<S>::GPS;
+    int groups, steps, mp, aw, sw;  // whole-K groups and steps; A and sums words of a chunk
+    __host__ __device__ MfmaLdsLayout(int K, int M, int CS) {
+        groups = K / Traits<S>::GROUP;
+        steps = (groups + GPS - 1) / GPS;
+        mp = 2;
+        while (mp < M) mp *= 2;
+        aw = CS * 16 * mp * 4;
+        sw = CS * GPS * 16;
+    }
+    // bytes of A and sums for a chunk of CS steps
+    __host__ __device__ size_t bytes() const { return (size_t)(aw + sw) * 4; }
+};
+
+// Column swizzle of row lr (0..15 within a step) for rows of mp = 2^b units:
+// the row's top b bits, rotated left by one. Units of one row slot (lr mod
+// 16/mp) then differ in their column for every top-bits value, and the two
+// pairs a 16-lane group of the 4-bit g64 staging holds (tokens t, t + 1) land
+// on opposite column parities.
+__device__ __forceinline__ int lds_swz(int mp, int lr) {
+    const int b = 31 - __builtin_clz(mp);
+    const int x = lr >> (4 - b);
+    return ((x << 1) | (x >> (b - 1))) & (mp - 1);
+}
+
+// blockDim.x = 64 * TP * WK; wavefront w works on tile blockIdx.x * TP + w % TP
+// over K-slice w / TP (ceil(chunk steps / WK) steps of every chunk; in a short
+// last chunk a slice can be empty). DEPTH steps of code loads in flight per
+// wavefront. SGMAX (at most 64) bounds the groups of a slice: the scale
+// block's row stride. CHUNKED: x goes in several chunks (CS < steps).
+template <int S, int DEPTH, int SGMAX, bool CHUNKED>
+__global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, int K, int M,
+                                                              const uint16_t* x, int tiles,
+                                                              int TP, int WK, int CS) {
+    using T = Traits<S>;
+    using P = MfmaStep<S>;
+    constexpr int GPS = P::GPS;
+    constexpr int NV = T::GROUP / 8;  // 16-byte activation vectors per group
+    constexpr int U = CHUNKED ? 2 : 4;  // staging vectors in flight per lane (registers)
+    constexpr uint32_t ONE2 = 0x3F803F80u;
+    const int NT = blockDim.x;
+    extern __shared__ __align__(16) uint32_t lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, c16 = lane & 15;
+    const MfmaLdsLayout<S> Lo(K, M, CS);
+    const int groups = Lo.groups, steps = Lo.steps, mp = Lo.mp;
+    const bool odd = GPS == 2 && (groups & 1);
+    float* xd = reinterpret_cast<float*>(lds + Lo.aw);
+    uint32_t* sl = lds + Lo.aw + Lo.sw + wave * 16 * (SGMAX + 1);
+
+    // this wavefront's tile and K-slice (the last workgroup's wavefronts past
+    // the last tile redo the last tile and store nothing)
+    const int tw = wave % TP, ks = wave / TP;
+    const int tile_raw = blockIdx.x * TP + tw;
+    const int tile = min(tile_raw, tiles - 1);
+    int i = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxGroup; ++q)
+        if (q < a.count && tile >= a.tile_start[q]) i = q;
+    const int N = a.N[i];
+    const int row0 = (tile - a.tile_start[i]) * 16;
+    const uint8_t* codes = a.codes[i];
+    const uint8_t* scale = a.scale[i];
+    const uint8_t* bias = a.bias[i];
+    const int n = min(row0 + c16, N - 1);
+    const uint8_t* crow = codes + (int64_t)n * (K / 2);
+    const int tm = min(c16, M - 1);  // tokens past M read token M-1; their outputs are dropped
+
+    // staging lanes: a lane keeps one token t and one 16-byte vector iv of a
+    // group (NV consecutive lanes cover a group of one token: coalesced, and
+    // the group's sum is a DPP reduction over them) and walks the chunk's
+    // groups gi0, gi0 + GS, ...; C lanes cover a group of all tokens, the
+    // workgroup's first GS * C threads stage (GS >= 1), the rest load clamped
+    // addresses and store nothing, as do lanes of tokens past M
+    const int C = mp * NV, GS = NT / C;
+    const int c = threadIdx.x % C;
+    const int gi0 = (int)threadIdx.x < GS * C ? (int)threadIdx.x / C : groups;
+    const int t = c / NV, iv = c % NV;
+    const bool live = t < M;
+    const uint16_t* xl = x + (int64_t)min(t, M - 1) * K + iv * 8;
+    // vector iv of a group is piece d of lane group gg (the inverse of the
+    // codes' piece order); for GPS = 2, d also depends on q
+    const int gg = GPS == 1 ? (iv >> 2) : ((iv >> 2) | (((iv >> 1) & 1) << 1));
+
+    const uint32_t MASK = opaque(0x000F000Fu);
+    const uint32_t MAGIC = unpack_magic<S>();
+    auto unpack = [&](uint32_t w) {
+        auto pair = [&](uint32_t v) {
+            return S == SYM4_G128 ? ((v & MASK) ^ MAGIC) : ((v & MASK) | MAGIC);
+        };
+        return as_bf16x8(pair(w), pair(w >> 4), pair(w >> 8), pair(w >> 12));
+    };
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // one pass when x fits (CHUNKED false: no loop for the compiler to hoist
+    // lane constants out of, which would cost registers the ring needs)
+    const int c_end = CHUNKED ? steps : 1;
+    for (int c0 = 0; c0 < c_end; c0 += CHUNKED ? CS : 1) {
+        const int cn = min(CS, steps - c0);                        // chunk steps
+        const int cg0 = c0 * GPS, cgn = min(groups, (c0 + cn) * GPS) - cg0;  // chunk groups
+        const int spw = (cn + WK - 1) / WK;
+        const int lb = ks * spw;                   // slice start (chunk step)
+        const int ns = min(cn, lb + spw) - lb;     // slice steps, <= 0 if empty
+        const int lbl = min(lb, cn - 1), nsl = max(ns, 1);  // addresses of an empty slice
+        if (c0 > 0) __syncthreads();               // the previous chunk's LDS reads are done
+
+        u32x4_t xr[U];
+        auto stage_load = [&](int gb) {
+#pragma unroll
+            for (int j = 0; j < U; ++j)
+                xr[j] = *gmem<u32x4_t>(xl + (cg0 + min(gb + j * GS, cgn - 1)) * T::GROUP);
+        };
+        auto stage_store = [&](int gb) {
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                float part = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) part = dot2_bf16(ONE2, xr[j][e], part);
+                const float sum = group_sum<NV>(part);
+                const int gi = gb + j * GS;
+                if (live && gi < cgn) {
+                    const int st = gi / GPS, q = gi - st * GPS;
+                    const int d = GPS == 1 ? (iv & 3) : (2 * q + (iv & 1));
+                    const u32x4_t o = {__builtin_amdgcn_perm(xr[j][2], xr[j][0], 0x05040100u),
+                                       __builtin_amdgcn_perm(xr[j][2], xr[j][0], 0x07060302u),
+                                       __builtin_amdgcn_perm(xr[j][3], xr[j][1], 0x05040100u),
+                                       __builtin_amdgcn_perm(xr[j][3], xr[j][1], 0x07060302u)};
+                    const int lr = d * 4 + gg;
+                    *reinterpret_cast<u32x4_t*>(lds + 4 * ((st * 16 + lr) * mp + (t ^ lds_swz(mp, lr)))) = o;
+                    if (iv == 0) xd[(st * GPS + q) * 16 + t] = sum;
+                }
+            }
+        };
+        // codes of slice step ls (lane: row c16, 16-byte piece g of the step;
+        // a half step redirects group B's piece into group A); steps past the
+        // slice reload its last
+        using Buf = u32x4_t;
+        auto load = [&](Buf& B, int ls) {
+            const int s = c0 + lbl + min(ls, nsl - 1);
+            const bool half = odd && s == steps - 1;
+            const int gl = half ? (g & 1) : g;
+            B = *gmem<u32x4_t>(crow + (uint32_t)s * 64 + 16 * gl);
+        };
+
+        // 1. the chunk's first round of activation loads goes out first: the
+        //    load counter drains in order, so its waits then cover these L2
+        //    reads only, not the HBM loads issued after it
+        stage_load(gi0);
+        __builtin_amdgcn_sched_barrier(0);
+        // 2. the slice's scales (affine: bf16 scale low, bf16 bias high) of
+        //    the tile's 16 rows, for the wavefront's LDS block of 16 rows x
+        //    (SGMAX + 1) words (odd stride: the 16 rows a step reads sit in
+        //    16 banks); lanes walk a row's groups (coalesced)
+        const int sg0 = (c0 + lbl) * GPS, sg = min(groups, (c0 + lbl + nsl) * GPS) - sg0;
+        const int sgl = min(lane, sg - 1);
+        uint32_t sv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t e = (uint32_t)min(row0 + r, N - 1) * (uint32_t)groups + (uint32_t)(sg0 + sgl);
+            if constexpr (T::AFFINE)
+                sv[r] = (uint32_t)gmem<uint16_t>(scale)[e] | ((uint32_t)gmem<uint16_t>(bias)[e] << 16);
+            else
+                sv[r] = gmem<uint32_t>(scale)[e];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // 3. the first DEPTH - 1 steps' code loads, in flight during the
+        //    staging; issued step by step (the loop's order) so the
+        //    load-counter wait the compiler puts at the loop head is the same
+        //    from both predecessors
+        Buf cb[DEPTH];
+#pragma unroll
+        for (int p = 0; p < DEPTH - 1; ++p) {
+            load(cb[p], p);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // 4. activations and sums into LDS, then the scales (unconditional:
+        //    a branch would leave the scale loads possibly in flight at the
+        //    join and blur the load waits after it; lanes past the slice
+        //    write columns nobody reads, or the padding column)
+        stage_store(gi0);
+        for (int gb = gi0 + GS * U; gb < cgn; gb += GS * U) {
+            stage_load(gb);
+            stage_store(gb);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sl[r * (SGMAX + 1) + min(lane, SGMAX)] = sv[r];
+        __syncthreads();
+
+        // 5. the slice's steps
+        auto compute = [&](const Buf& B, int ls) {
+            const int sc_ = lb + ls;  // chunk step
+            const bool half = odd && c0 + sc_ == steps - 1;
+            bf16x8_t A[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                A[d] = *reinterpret_cast<const bf16x8_t*>(
+                    lds + 4 * ((sc_ * 16 + d * 4 + g) * mp + (tm ^ lds_swz(mp, d * 4 + g))));
+            uint32_t w[4] = {B[0], B[1], B[2], B[3]};
+            if constexpr (GPS == 2) {
+                // lanes 0-31 hold group A, lanes 32-63 group B: swap the upper
+                // half of words 0/1 with the lower half of words 2/3
+                const auto p02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+                const auto p13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+                w[0] = p02[0]; w[2] = p02[1];
+                w[1] = p13[0]; w[3] = p13[1];
+            }
+#pragma unroll
+            for (int q = 0; q < GPS; ++q) {
+                if (q == 1 && half) continue;
+                f32x4_t D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int d = 4 / GPS * q; d < 4 / GPS * (q + 1); ++d)
+                    D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[d], unpack(w[d]), D, 0, 0, 0);
+                const f32x4_t DX = *reinterpret_cast<const f32x4_t*>(xd + (sc_ * GPS + q) * 16 + 4 * g);
+                const uint32_t swd = sl[c16 * (SGMAX + 1) + min(ls * GPS + q, sg - 1)];
+                float sc, corr;
+                if constexpr (T::AFFINE) {
+                    sc = bf16_bits_to_f32(swd & 0xFFFFu);
+                    corr = fmaf(-T::BIAS, sc, __uint_as_float(swd & 0xFFFF0000u));
+                } else {
+                    sc = __uint_as_float(swd);
+                    corr = -T::BIAS * sc;
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = fmaf(corr, DX[r], fmaf(sc, D[r], acc[r]));
+            }
+        };
+        // step ls + DEPTH - 1 is loaded while step ls is computed; the ring
+        // is unrolled so every buffer index is static. Whole rounds run in
+        // the loop (nothing in it is conditional: a skipped load would make
+        // the compiler's load-counter waits conservative); the last round,
+        // after it, loads once and computes only the slice's remaining steps
+        if (ns > 0) {  // wave-uniform
+            const int rounds = (ns + DEPTH - 1) / DEPTH;
+            for (int r0 = 0; r0 < (rounds - 1) * DEPTH; r0 += DEPTH) {
+#pragma unroll
+                for (int u = 0; u < DEPTH; ++u) {
+                    load(cb[(u + DEPTH - 1) % DEPTH], r0 + u + DEPTH - 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute(cb[u], r0 + u);
+                }
+            }
+            const int r0 = (rounds - 1) * DEPTH;
+            load(cb[DEPTH - 1], r0 + DEPTH - 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < DEPTH; ++u)
+                if (r0 + u < ns) compute(cb[u], r0 + u);
+        }
+    }
+
+    // K-slices meet: every wavefront parks its partial tile in LDS (the
+    // activations are no longer read), slice 0 adds the others and stores
+    if (WK > 1) {
+        __syncthreads();
+        *reinterpret_cast<f32x4_t*>(lds + 4 * threadIdx.x) = acc;
+        __syncthreads();
+        if (ks != 0) return;  // wave-uniform, after the last barrier
+        for (int k = 1; k < WK; ++k) {
+            const f32x4_t o = *reinterpret_cast<const f32x4_t*>(lds + 4 * ((k * TP + tw) * 64 + lane));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] += o[r];
+        }
+    }
+    if (tile_raw >= tiles) return;
+    float* y = a.y[i];
+    const int nn = row0 + c16;
+    if (nn < N) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * g + r;
+            if (m < M) y[(int64_t)m * N + nn] = acc[r];
+        }
+    }
+}
+
 }  // namespace w4

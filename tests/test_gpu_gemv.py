@@ -49,6 +49,8 @@ def _run(scheme, N, K, M, name, rows=None, quantize_on_gpu=True):
     ("aff4_g64", 333, 768, 13),
     ("aff4_g64", 17, 64, 6),          # one k step: most split-K wavefronts get none
     ("sym4_g128", 31, 128, 11),
+    ("sym4_g128", 12370, 512, 3),     # > 256 row tiles: 4 per workgroup, ragged last workgroup
+    ("aff4_g64", 600, 13888, 8),      # activations staged in chunks; odd group count
 ])
 def test_gemv_matches_oracle(scheme, N, K, M):
     _run(scheme, N, K, M, f"small.{scheme}.{N}x{K}")
