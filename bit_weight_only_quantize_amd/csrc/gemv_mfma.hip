@@ -37,14 +37,17 @@ static void pick_mfma(int RT, int WK, const GemvGroupArgs& a, int blocks, int K,
 }
 
 // Activations in LDS (gemv_mfma_lds_kernel): one workgroup per CU holds TP =
-// ceil(tiles / CUs) tiles and splits each tile's steps over WK wavefronts, up
-// to 16 wavefronts in all, with x staged in as few chunks of steps as LDS
-// allows; launches of more than 16 tiles per CU take the split-K kernel.
+// ceil(tiles / CUs) tiles; 16 wavefronts stage x (in as few chunks of steps
+// as LDS allows), and TP * WK of them stream codes, each tile's steps split
+// over WK of them. Measured on the 7B shapes with the code stream alone:
+// about 24 steps (KB) of code loads in flight per CU read fastest, more read
+// slower (16 wavefronts x 4 steps on one tile: 1.6 TB/s against 2.4 with 4
+// x 4). Launches of more than 16 tiles per CU take the split-K kernel.
 template <int S>
 static bool try_mfma_lds(int count, const void* const* codes, const void* const* scale,
                          const void* const* bias, const int64_t* N, int64_t K,
                          const uint16_t* x, int64_t M, float* const* y, hipStream_t st) {
-    constexpr int kCUs = 256, kMaxWaves = 16;
+    constexpr int kCUs = 256, kWaves = 16;
     constexpr size_t kLds = 160 * 1024;
     GemvGroupArgs a{};
     int tiles = 0;
@@ -61,26 +64,28 @@ static bool try_mfma_lds(int count, const void* const* codes, const void* const*
     a.count = count;
     if (tiles == 0) return false;
     const int TP = (tiles + kCUs - 1) / kCUs;
-    if (TP > kMaxWaves) return false;
+    if (TP > kWaves) return false;
     const MfmaLdsLayout<S> whole((int)K, (int)M, 1);
     const int steps = whole.steps, GPS = whole.GPS;
-    int WK = std::min(std::max(1, kMaxWaves / TP), steps);
-    // every K-slice of a whole-K chunk non-empty
-    while (WK > 1 && (WK - 1) * ((steps + WK - 1) / WK) >= steps) --WK;
-    const int nw = TP * WK;
     // the staging lanes of one group of all tokens must fit the workgroup
-    if (64 * nw < whole.mp * (Traits<S>::GROUP / 8)) return false;
-    // fewest chunks whose activations, sums and scale blocks fit in LDS
-    int CS = 0, SG = 0, spw = 0;
+    if (64 * kWaves < whole.mp * (Traits<S>::GROUP / 8)) return false;
+    // fewest chunks whose activations, sums and scale blocks fit in LDS; the
+    // tile split WK puts about 24 steps of code loads in flight per CU
+    int CS = 0, SG = 0, spw = 0, WK = 1;
     size_t lds = 0;
     for (int chunks = 1; chunks <= steps; ++chunks) {
         CS = (steps + chunks - 1) / chunks;
+        const int depth = chunks > 1 ? 2 : 4;
+        WK = (24 + TP * depth / 2) / (TP * depth);
+        WK = std::max(1, std::min({WK, kWaves / TP, CS}));
+        // every K-slice of a full chunk non-empty
+        while (WK > 1 && (WK - 1) * ((CS + WK - 1) / WK) >= CS) --WK;
         spw = (CS + WK - 1) / WK;
         const int sgmax = std::min(spw * GPS, whole.groups);
-        if (sgmax > 64) continue;
-        SG = sgmax <= 16 ? 16 : sgmax <= 32 ? 32 : 64;
-        lds = MfmaLdsLayout<S>((int)K, (int)M, CS).bytes() + (size_t)nw * 16 * (SG + 1) * 4;
-        lds = std::max(lds, WK > 1 ? (size_t)nw * 64 * 16 : (size_t)0);
+        if (sgmax > (chunks > 1 ? 64 : 128)) continue;  // chunked: registers (see below)
+        SG = sgmax <= 16 ? 16 : sgmax <= 32 ? 32 : sgmax <= 64 ? 64 : 128;
+        lds = MfmaLdsLayout<S>((int)K, (int)M, CS).bytes() + (size_t)TP * WK * 16 * (SG + 1) * 4;
+        lds = std::max(lds, WK > 1 ? (size_t)TP * WK * 64 * 16 : (size_t)0);
         if (lds <= kLds) break;
         lds = 0;
     }
@@ -89,20 +94,26 @@ static bool try_mfma_lds(int count, const void* const* codes, const void* const*
     auto go = [&](auto kern) {
         if (lds > 64 * 1024)
             (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * nw), lds, st, a, (int)K, (int)M, x, tiles, TP, WK, CS);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWaves), lds, st, a, (int)K, (int)M, x, tiles, TP, WK, CS);
     };
-    // measured on the 7B and 13B decode shapes: four steps in flight beat
-    // eight; slices under four steps take two. The chunk loop costs the
-    // registers of two more steps in flight, so chunked launches keep two.
+    // four steps in flight (eight read slower, see above); slices under four
+    // steps take two. The chunk loop costs the registers of two more steps in
+    // flight, so chunked launches keep two.
     auto by_depth = [&](auto sgc) {
         constexpr int G = decltype(sgc)::value;
-        if (CS < steps) go(gemv_mfma_lds_kernel<S, 2, G, true>);
-        else if (spw >= 4) go(gemv_mfma_lds_kernel<S, 4, G, false>);
+        if constexpr (G <= 64) {
+            if (CS < steps) {
+                go(gemv_mfma_lds_kernel<S, 2, G, true>);
+                return;
+            }
+        }
+        if (spw >= 4) go(gemv_mfma_lds_kernel<S, 4, G, false>);
         else go(gemv_mfma_lds_kernel<S, 2, G, false>);
     };
     if (SG == 16) by_depth(std::integral_constant<int, 16>{});
     else if (SG == 32) by_depth(std::integral_constant<int, 32>{});
-    else by_depth(std::integral_constant<int, 64>{});
+    else if (SG == 64) by_depth(std::integral_constant<int, 64>{});
+    else by_depth(std::integral_constant<int, 128>{});
     return true;
 }
 

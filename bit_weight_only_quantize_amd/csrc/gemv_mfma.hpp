@@ -399,10 +399,11 @@ __device__ __forceinline__ int lds_swz(int mp, int lr) {
     return ((x << 1) | (x >> (b - 1))) & (mp - 1);
 }
 
-// blockDim.x = 64 * TP * WK; wavefront w works on tile blockIdx.x * TP + w % TP
-// over K-slice w / TP (ceil(chunk steps / WK) steps of every chunk; in a short
-// last chunk a slice can be empty). DEPTH steps of code loads in flight per
-// wavefront. SGMAX (at most 64) bounds the groups of a slice: the scale
+// blockDim.x >= 64 * TP * WK; wavefront w < TP * WK works on tile
+// blockIdx.x * TP + w % TP over K-slice w / TP (ceil(chunk steps / WK) steps
+// of every chunk; in a short last chunk a slice can be empty); all wavefronts
+// stage activations. DEPTH steps of code loads in flight per streaming
+// wavefront. SGMAX (at most 128) bounds the groups of a slice: the scale
 // block's row stride. CHUNKED: x goes in several chunks (CS < steps).
 template <int S, int DEPTH, int SGMAX, bool CHUNKED>
 __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, int K, int M,
@@ -423,11 +424,13 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
     const int groups = Lo.groups, steps = Lo.steps, mp = Lo.mp;
     const bool odd = GPS == 2 && (groups & 1);
     float* xd = reinterpret_cast<float*>(lds + Lo.aw);
-    uint32_t* sl = lds + Lo.aw + Lo.sw + wave * 16 * (SGMAX + 1);
+    uint32_t* sl = lds + Lo.aw + Lo.sw + wave * 16 * (SGMAX + 1);  // streaming wavefronts only
 
-    // this wavefront's tile and K-slice (the last workgroup's wavefronts past
-    // the last tile redo the last tile and store nothing)
-    const int tw = wave % TP, ks = wave / TP;
+    // the first TP * WK wavefronts stream codes: this one's tile and K-slice
+    // (the last workgroup's wavefronts past the last tile redo the last tile
+    // and store nothing); the others only help stage the activations
+    const bool comp = wave < TP * WK;
+    const int tw = wave % TP, ks = min(wave / TP, WK - 1);
     const int tile_raw = blockIdx.x * TP + tw;
     const int tile = min(tile_raw, tiles - 1);
     int i = 0;
@@ -524,20 +527,35 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
         //    reads only, not the HBM loads issued after it
         stage_load(gi0);
         __builtin_amdgcn_sched_barrier(0);
+        // staging-only wavefronts: the rest of the staging, the barrier, and
+        // (branch taken per wavefront, so each path's load waits stay exact)
+        if (!comp) {
+            stage_store(gi0);
+            for (int gb = gi0 + GS * U; gb < cgn; gb += GS * U) {
+                stage_load(gb);
+                stage_store(gb);
+            }
+            __syncthreads();
+            continue;
+        }
         // 2. the slice's scales (affine: bf16 scale low, bf16 bias high) of
         //    the tile's 16 rows, for the wavefront's LDS block of 16 rows x
         //    (SGMAX + 1) words (odd stride: the 16 rows a step reads sit in
-        //    16 banks); lanes walk a row's groups (coalesced)
+        //    16 banks); lanes walk a row's groups (coalesced), 64 at a time
         const int sg0 = (c0 + lbl) * GPS, sg = min(groups, (c0 + lbl + nsl) * GPS) - sg0;
-        const int sgl = min(lane, sg - 1);
-        uint32_t sv[16];
+        constexpr int SR = (SGMAX + 63) / 64;
+        uint32_t sv[SR][16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint32_t e = (uint32_t)min(row0 + r, N - 1) * (uint32_t)groups + (uint32_t)(sg0 + sgl);
-            if constexpr (T::AFFINE)
-                sv[r] = (uint32_t)gmem<uint16_t>(scale)[e] | ((uint32_t)gmem<uint16_t>(bias)[e] << 16);
-            else
-                sv[r] = gmem<uint32_t>(scale)[e];
+        for (int h = 0; h < SR; ++h) {
+            const int sgl = min(lane + 64 * h, sg - 1);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const uint32_t e = (uint32_t)min(row0 + r, N - 1) * (uint32_t)groups + (uint32_t)(sg0 + sgl);
+                if constexpr (T::AFFINE)
+                    sv[h][r] = (uint32_t)gmem<uint16_t>(scale)[e] | ((uint32_t)gmem<uint16_t>(bias)[e] << 16);
+                else
+                    sv[h][r] = gmem<uint32_t>(scale)[e];
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         // 3. the first DEPTH - 1 steps' code loads, in flight during the
@@ -560,7 +578,9 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
             stage_store(gb);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sl[r * (SGMAX + 1) + min(lane, SGMAX)] = sv[r];
+        for (int h = 0; h < SR; ++h)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sl[r * (SGMAX + 1) + min(lane + 64 * h, SGMAX)] = sv[h][r];
         __syncthreads();
 
         // 5. the slice's steps
@@ -626,8 +646,11 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
         }
     }
 
-    // K-slices meet: every wavefront parks its partial tile in LDS (the
-    // activations are no longer read), slice 0 adds the others and stores
+    // staging-only wavefronts leave (a barrier waits for surviving
+    // wavefronts only)
+    if (!comp) return;
+    // K-slices meet: every streaming wavefront parks its partial tile in LDS
+    // (the activations are no longer read), slice 0 adds the others, stores
     if (WK > 1) {
         __syncthreads();
         *reinterpret_cast<f32x4_t*>(lds + 4 * threadIdx.x) = acc;
