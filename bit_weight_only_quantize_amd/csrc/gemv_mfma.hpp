@@ -512,8 +512,9 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
             }
         };
         // codes of slice step ls (lane: row c16, 16-byte piece g of the step;
-        // a half step redirects group B's piece into group A); steps past the
-        // slice reload its last
+        // a half step redirects group B's piece into group A; plain loads:
+        // nontemporal ones measured slower here); steps past the slice reload
+        // its last
         using Buf = u32x4_t;
         auto load = [&](Buf& B, int ls) {
             const int s = c0 + lbl + min(ls, nsl - 1);
