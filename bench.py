@@ -309,27 +309,16 @@ def run_moe(c: Ctx, a):
     wts = [torch.empty((M, k), dtype=torch.float32, device=c.dev) for _ in range(layers)]
     logits = torch.empty((M, E), dtype=torch.float32, device=c.dev)
     y = torch.empty((M, D), dtype=torch.float32, device=c.dev)
-    import ctypes
-
-    lib = w4.lib()
-
-    # One token: router GEMV, then selection + experts in one call (the
-    # selection runs inside the gate/up pass). Several tokens: the fused
-    # router/top-k kernel, then the experts.
+    # Router GEMV, then selection + experts in one call (one token: the
+    # selection runs inside the gate/up pass; several: selection and bucketing
+    # share one workgroup).
     one = M == 1
 
     def step():
-        st = torch.cuda.current_stream(c.dev).cuda_stream
         for l, (router, gate, up, down, shared) in enumerate(L):
-            if one:
-                w4.gemv_into(router, x, logits)
-                w4.moe_gemv_logits(gate, up, down, x, logits, top_k=k, shared=shared, workspace=ws,
-                                   y=y, ids=ids[l], weights=wts[l])
-            else:
-                rd = router.desc()
-                w4._check(lib.w4_moe_route(ctypes.byref(rd), x.data_ptr(), M, k, logits.data_ptr(),
-                                           ids[l].data_ptr(), wts[l].data_ptr(), st))
-                w4.moe_gemv(gate, up, down, x, ids[l], wts[l], shared=shared, workspace=ws, y=y)
+            w4.gemv_into(router, x, logits)
+            w4.moe_gemv_logits(gate, up, down, x, logits, top_k=k, shared=shared, workspace=ws,
+                               y=y, ids=ids[l], weights=wts[l])
 
     g = c.graph(step)
     ms = c.time_graph(g, a.steps, a.warmup)
@@ -345,7 +334,7 @@ def run_moe(c: Ctx, a):
                         "experts": E, "top_k": k, "d_model": D, "expert_ffn": F, "shared_ffn": Fs,
                         "scheme": "aff4_g64 experts/shared, aff8_g64 router",
                         "launches_per_layer": ("router gemv, gate/up with the top-k inside, down" if one else
-                                               "router gemv + top-k, bucket, gate/up, down, combine")})
+                                               "router gemv, top-k + bucketing, gate/up, down, combine")})
     out["hbm_TBps"] = round(tbs, 4)
     out["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
     out["distinct_experts_per_layer"] = sum(distinct) / len(distinct)

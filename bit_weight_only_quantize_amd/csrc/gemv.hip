@@ -4,6 +4,8 @@
 // after the weights are loaded; §3.3: decode is memory-bound, so the kernel is
 // built to stream the packed codes at HBM speed. See skinny.hpp for the
 // per-lane arithmetic.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "skinny.hpp"
@@ -292,7 +294,13 @@ static void go_mt(const GemvGroupArgs& a, int blocks, int K, int M, const uint16
     constexpr int SW = 2, XV = (NV + 1) / 2;
     auto kern = gemv_wave_mt_kernel<S, NV, R, MT, XV, SW>;
     allow_lds(kern, lds);
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256 + 64 * SW), lds, st, a, K, M, x);
+    // few row blocks (a router: 128 rows in 16 blocks): split the token tiles
+    // over workgroups too, up to about two workgroups per CU
+    const int ttiles = (M + MT - 1) / MT;
+    const int ts = std::max(1, std::min(ttiles, 512 / std::max(blocks, 1)));
+    const int tpw = MT * ((ttiles + ts - 1) / ts);
+    const int gy = (M + tpw - 1) / tpw;
+    hipLaunchKernelGGL(kern, dim3(blocks, gy), dim3(256 + 64 * SW), lds, st, a, K, M, x, tpw);
 }
 
 template <int S, int NV>

@@ -222,9 +222,12 @@ namespace w4 {
 // while the row wavefronts consume the other. Per token tile a row wavefront
 // unpacks each code vector once and issues 16 v_dot2 per token.
 // LDS: 2 * MT * (K/2 + K/KV) dwords (up to the 160 KiB of a gfx950 CU).
+// Workgroup (row block, blockIdx.y) takes tokens [blockIdx.y * TPW, + TPW):
+// launches with few row blocks split the tokens to fill the chip.
 template <int S, int NV, int R, int MT, int XV, int SW>
 __global__ __launch_bounds__(256 + 64 * SW) void gemv_wave_mt_kernel(GemvGroupArgs a, int K, int M,
-                                                                     const uint16_t* __restrict__ x) {
+                                                                     const uint16_t* __restrict__ x,
+                                                                     int TPW) {
     using T = Traits<S>;
     using L = XLayout<S, 1>;
     constexpr int XW = L::XW;
@@ -233,7 +236,9 @@ __global__ __launch_bounds__(256 + 64 * SW) void gemv_wave_mt_kernel(GemvGroupAr
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int VR = K / T::KV;
     const int tokw = K / 2 + VR;             // dwords per staged token
-    const int tiles = (M + MT - 1) / MT;
+    const int tb = blockIdx.y * TPW;         // this workgroup's first token
+    const int Mw = min(M - tb, TPW);         // and its token count (>= 1)
+    const int tiles = (Mw + MT - 1) / MT;
 
     const int t = blockIdx.x;
     int i = 0;
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void gemv_wave_mt_kernel(GemvGroupAr
             XStage<S, XV, 64 * SW> st[MT];  // all loads of the tile first, then the LDS writes
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const int tok = min(s * MT + m, M - 1);  // rows past M re-stage the last (unused)
+                const int tok = tb + min(s * MT + m, Mw - 1);  // rows past Mw re-stage the last (unused)
                 st[m].fetch(x + (int64_t)tok * K, VR, sl);
             }
 #pragma unroll
@@ -353,7 +358,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void gemv_wave_mt_kernel(GemvGroupAr
             for (int m = 0; m < MT; ++m) {
                 const float tot = wave_sum_to_lane63(acc[r][m]);
                 const int tok = s * MT + m;
-                if (lane == 63 && row0 + r < N && tok < M) a.y[i][(int64_t)tok * N + row0 + r] = tot;
+                if (lane == 63 && row0 + r < N && tok < Mw) a.y[i][(int64_t)(tb + tok) * N + row0 + r] = tot;
             }
     }
 }

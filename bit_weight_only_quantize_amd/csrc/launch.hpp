@@ -62,6 +62,11 @@ struct MoeMats {
 
 // Routed (token, slot) pairs per call: M <= 256 tokens times top_k <= 32.
 constexpr int kMoeMaxPairs = 256 * 32;
+constexpr int kMoeDescPairs = 16;  // pairs per work descriptor (one MFMA token tile)
+// work descriptors for P pairs over E experts (one per 16 pairs of an expert)
+inline int moe_slots(int64_t E, int64_t P) {
+    return (int)((E < P ? E : P) + (P + kMoeDescPairs - 1) / kMoeDescPairs);
+}
 
 struct MoeWorkspace {  // byte offsets inside the caller's workspace
     size_t work, pairs, h, hs, part, sout, total;

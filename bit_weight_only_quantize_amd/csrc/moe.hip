@@ -24,6 +24,7 @@
 #include "gemv_mfma.hpp"
 #include "skinny.hpp"
 #include "moe1.hpp"
+#include "moe_grouped.hpp"
 
 namespace w4 {
 
@@ -178,37 +179,34 @@ hipError_t launch_route(int scheme, const void* codes, const void* scale, const 
 }
 
 // ---------------------------------------------------------------- bucketing
-// Single workgroup. Pair p = m * k + j (token m, slot j), P <= kMoeMaxPairs.
+// One 1024-thread workgroup. Pair p = m * k + j (token m, slot j), P <=
+// kMoeMaxPairs, expert ids already in LDS (sid, -1 for ids outside [0, E)).
 // For every expert e, the pairs routed to it in increasing p; the experts with
-// at least one pair get work descriptors {e, first pair index, pair count} in
-// increasing e, the remaining descriptors up to `slots` are {-1, 0, 0}. Ids
-// outside [0, E) are ignored. Counts use LDS integer atomics (exact in any
-// order); the placement is sequential per expert, so the output is
-// deterministic.
-__global__ __launch_bounds__(1024) void moe_bucket_kernel(const int32_t* __restrict__ ids, int P,
-                                                          int E, int slots, int4* __restrict__ work,
-                                                          int32_t* __restrict__ pairs) {
-    __shared__ int sid[kMoeMaxPairs];
+// at least one pair get work descriptors {e, first pair index, pair count},
+// one per kMoeDescPairs pairs (so a descriptor is one MFMA token tile), in
+// increasing e; the remaining descriptors up to `slots` are {-1, 0, 0} and
+// descriptor `slots` holds {number of descriptors in use, 0, 0}. Counts
+// use LDS integer atomics (exact in any order); a pair's place is the
+// expert's offset plus the number of earlier pairs of the same expert, so the
+// output is deterministic.
+__device__ __forceinline__ void bucket_pairs(const int* sid, int P, int E, int slots,
+                                             int4* __restrict__ work, int32_t* __restrict__ pairs) {
     __shared__ int cnt[1024], off[1024], act[1024];
     __shared__ int n_act;
     const int t = threadIdx.x;
-    for (int p = t; p < P; p += blockDim.x) {
-        const int v = ids[p];
-        sid[p] = v >= 0 && v < E ? v : -1;
-    }
     for (int e = t; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
     for (int p = t; p < P; p += blockDim.x)
         if (sid[p] >= 0) atomicAdd(&cnt[sid[p]], 1);
     __syncthreads();
-    if (t < 64) {  // exclusive scans of counts and of active flags: 16 experts per lane
+    if (t < 64) {  // exclusive scans of counts and of descriptor counts: 16 experts per lane
         int c[16], loc = 0, la = 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int e = 16 * t + i;
             c[i] = e < E ? cnt[e] : 0;
             loc += c[i];
-            la += c[i] > 0;
+            la += (c[i] + kMoeDescPairs - 1) / kMoeDescPairs;
         }
         int incl = loc, inca = la;
 #pragma unroll
@@ -222,19 +220,74 @@ __global__ __launch_bounds__(1024) void moe_bucket_kernel(const int32_t* __restr
             const int e = 16 * t + i;
             if (e < E) { off[e] = o; act[e] = c[i] > 0 ? oa : -1; }
             o += c[i];
-            oa += c[i] > 0;
+            oa += (c[i] + kMoeDescPairs - 1) / kMoeDescPairs;
         }
         if (t == 63) n_act = inca;
     }
     __syncthreads();
-    for (int e = t; e < E; e += blockDim.x) {
-        if (act[e] < 0) continue;
-        work[act[e]] = make_int4(e, off[e], cnt[e], 0);
-        int w = off[e];
-        for (int p = 0; p < P; ++p)
-            if (sid[p] == e) pairs[w++] = p;
+    for (int e = t; e < E; e += blockDim.x)
+        if (act[e] >= 0)
+            for (int i = 0; i * kMoeDescPairs < cnt[e]; ++i)
+                work[act[e] + i] = make_int4(e, off[e] + i * kMoeDescPairs,
+                                             min(kMoeDescPairs, cnt[e] - i * kMoeDescPairs), 0);
+    // rank among earlier pairs of the same expert: every lane of a wavefront
+    // reads the same sid words (LDS broadcast), four at a time
+    const int4* sid4 = reinterpret_cast<const int4*>(sid);
+    for (int p = t; p < P; p += blockDim.x) {
+        const int e = sid[p];
+        if (e < 0) continue;
+        int rank = 0;
+        for (int q = 0; q < p / 4; ++q) {
+            const int4 v = sid4[q];
+            rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+        }
+        for (int q = p & ~3; q < p; ++q) rank += sid[q] == e;
+        pairs[off[e] + rank] = p;
     }
     for (int s = n_act + t; s < slots; s += blockDim.x) work[s] = make_int4(-1, 0, 0, 0);
+    if (t == 0) work[slots] = make_int4(n_act, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(1024) void moe_bucket_kernel(const int32_t* __restrict__ ids, int P,
+                                                          int E, int slots, int4* __restrict__ work,
+                                                          int32_t* __restrict__ pairs) {
+    __shared__ __align__(16) int sid[kMoeMaxPairs];
+    for (int p = threadIdx.x; p < P; p += blockDim.x) {
+        const int v = ids[p];
+        sid[p] = v >= 0 && v < E ? v : -1;
+    }
+    __syncthreads();
+    bucket_pairs(sid, P, E, slots, work, pairs);
+}
+
+// Selection and bucketing in one workgroup (several tokens, E <= 64 * EPL):
+// wavefront w selects tokens w, w + 16, ... from their logits (ids into LDS
+// and to `ids`, weights to `wts`), then the workgroup buckets the pairs. One
+// launch instead of a top-k launch and a bucketing launch.
+template <int EPL>
+__global__ __launch_bounds__(1024) void moe_select_bucket_kernel(const float* __restrict__ logits,
+                                                                 int M, int E, int k, int slots,
+                                                                 int32_t* __restrict__ ids,
+                                                                 float* __restrict__ wts,
+                                                                 int4* __restrict__ work,
+                                                                 int32_t* __restrict__ pairs) {
+    __shared__ __align__(16) int sid[kMoeMaxPairs];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int m = wave; m < M; m += 16) {
+        const float* l = logits + (int64_t)m * E;
+        float v[EPL];
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lane + 64 * j;
+            const float xv = l[min(e, E - 1)];
+            v[j] = e < E ? xv : -INFINITY;
+        }
+        topk_rounds<EPL>(v, E, k, sid + m * k, wts + (int64_t)m * k);
+    }
+    __syncthreads();
+    const int P = M * k;
+    for (int p = threadIdx.x; p < P; p += blockDim.x) ids[p] = sid[p];
+    bucket_pairs(sid, P, E, slots, work, pairs);
 }
 
 // ---------------------------------------------------------------- expert passes
@@ -251,13 +304,13 @@ struct MoeArgs {
     int has_shared;
     int M, k, E;
     const uint16_t* x;        // [M][D]
-    const int4* work;         // [amax] {expert, first pair, pair count} or {-1, ..}
+    const int4* work;         // [amax + 1] {expert, first pair, pair count <= 16} or {-1, ..}
     const int32_t* pairs;     // [M*k]
     uint16_t* h;              // [M*k][F] bf16
     uint16_t* hs;             // [M][Fs] bf16
     float* part;              // [M*k][D]
     float* sout;              // [M][D]
-    int amax;                 // routed slots in the grid = min(E, M*k)
+    int amax;                 // descriptor slots (moe_slots)
     int tiles_r, tiles_s;     // row tiles per routed slot / for the shared expert
 };
 
@@ -275,7 +328,7 @@ __device__ __forceinline__ MfmaTile expert_tile(const MoeMat& W, int e, int row0
 
 // gate/up: wavefront w gets tiles (gate rows f0 + 16w.., up rows f0 + 16w..), so
 // a lane holds g and u of the same (token, f) and writes h = bf16(gelu(g) * u).
-template <int S, int WR, int WK, int SL>
+template <int S, int WR, int WK, int SL, int DEPTH = 2>
 __global__ __launch_bounds__(64 * WR * WK) void moe_gate_up_kernel(MoeArgs a) {
     extern __shared__ __align__(16) uint32_t lds[];
     const int lane = threadIdx.x & 63;
@@ -311,7 +364,7 @@ __global__ __launch_bounds__(64 * WR * WK) void moe_gate_up_kernel(MoeArgs a) {
         const int t = min(t0 + c16, count - 1);
         const int tok = shared ? t : a.pairs[first + t] / a.k;
         f32x4_t acc[2];
-        mfma_tiles<S, 2, WK, 2, WR, SL>(tl, D, a.x, (uint32_t)tok * (uint32_t)D, lds, acc);
+        mfma_tiles<S, 2, WK, DEPTH, WR, SL>(tl, D, a.x, (uint32_t)tok * (uint32_t)D, lds, acc);
         const int f = f0 + 16 * (wave % WR) + c16;
         if (wave < WR && f < F) {
 #pragma unroll
@@ -328,7 +381,7 @@ __global__ __launch_bounds__(64 * WR * WK) void moe_gate_up_kernel(MoeArgs a) {
 
 // down: wavefront w gets rows n0 + 32w .. of W_down[e] (two tiles) against the
 // h rows of the expert's pairs.
-template <int S, int WR, int WK, int SL>
+template <int S, int WR, int WK, int SL, int DEPTH = 2>
 __global__ __launch_bounds__(64 * WR * WK) void moe_down_kernel(MoeArgs a) {
     extern __shared__ __align__(16) uint32_t lds[];
     const int lane = threadIdx.x & 63;
@@ -361,7 +414,7 @@ __global__ __launch_bounds__(64 * WR * WK) void moe_down_kernel(MoeArgs a) {
         const int t = min(t0 + c16, count - 1);
         const int row = shared ? t : a.pairs[first + t];
         f32x4_t acc[2];
-        mfma_tiles<S, 2, WK, 2, WR, SL>(tl, F, hin, (uint32_t)row * (uint32_t)F, lds, acc);
+        mfma_tiles<S, 2, WK, DEPTH, WR, SL>(tl, F, hin, (uint32_t)row * (uint32_t)F, lds, acc);
         if (wave >= WR) continue;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -403,7 +456,7 @@ static size_t al(size_t b) { return (b + 255) & ~(size_t)255; }
 MoeWorkspace moe_workspace_layout(int64_t M, int k, int64_t E, int64_t D, int64_t F, int64_t Fs) {
     MoeWorkspace w{};
     size_t o = 0;
-    w.work = o;    o += al(E * 16);
+    w.work = o;    o += al(((size_t)moe_slots(E, M * k) + 1) * 16);
     w.pairs = o;   o += al(M * k * 4);
     w.h = o;       o += al(M * k * F * 2);
     w.hs = o;      o += al(M * Fs * 2);
@@ -426,33 +479,45 @@ static MoeMat mm(const void* c, const void* s, const void* b, int64_t N, int64_t
     return m;
 }
 
-template <int S, int WR, int WK>
-static hipError_t moe_passes(const MoeArgs& a0, int64_t Fs, hipStream_t st) {
-    MoeArgs a = a0;
+template <int S, int WR, int WK, int DEPTH>
+static void moe_gate_up_launch(MoeArgs a, int64_t Fs, hipStream_t st) {
     const int D = a.gate.K, F = a.gate.N;
     // gate/up: 16 * WR (gate, up) rows per workgroup
     a.tiles_r = (F + 16 * WR - 1) / (16 * WR);
     a.tiles_s = a.has_shared ? (int)((Fs + 16 * WR - 1) / (16 * WR)) : 0;
-    int blocks = a.amax * a.tiles_r + a.tiles_s;
-    size_t lds = gemv_mfma_lds_bytes<S, 2, WK, WR>(D);
+    const int blocks = a.amax * a.tiles_r + a.tiles_s;
+    const size_t lds = gemv_mfma_lds_bytes<S, 2, WK, WR>(D);
     switch (mfma_slices(D / Traits<S>::GROUP)) {
-        case 1: hipLaunchKernelGGL((moe_gate_up_kernel<S, WR, WK, 1>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
-        case 2: hipLaunchKernelGGL((moe_gate_up_kernel<S, WR, WK, 2>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
-        default: hipLaunchKernelGGL((moe_gate_up_kernel<S, WR, WK, 4>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
+        case 1: hipLaunchKernelGGL((moe_gate_up_kernel<S, WR, WK, 1, DEPTH>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
+        case 2: hipLaunchKernelGGL((moe_gate_up_kernel<S, WR, WK, 2, DEPTH>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
+        default: hipLaunchKernelGGL((moe_gate_up_kernel<S, WR, WK, 4, DEPTH>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+}
+
+template <int S, int WR, int WK, int DEPTH>
+static void moe_down_launch(MoeArgs a, int64_t Fs, hipStream_t st) {
+    const int D = a.gate.K, F = a.gate.N;
     // down: 32 * WR rows per workgroup (K = F routed, Fs shared)
     const int64_t Kmax = a.has_shared ? std::max<int64_t>(F, Fs) : F;
     a.tiles_r = (D + 32 * WR - 1) / (32 * WR);
     a.tiles_s = a.has_shared ? a.tiles_r : 0;
-    blocks = a.amax * a.tiles_r + a.tiles_s;
-    lds = gemv_mfma_lds_bytes<S, 2, WK, WR>(Kmax);
+    const int blocks = a.amax * a.tiles_r + a.tiles_s;
+    const size_t lds = gemv_mfma_lds_bytes<S, 2, WK, WR>(Kmax);
     switch (mfma_slices(Kmax / Traits<S>::GROUP)) {
-        case 1: hipLaunchKernelGGL((moe_down_kernel<S, WR, WK, 1>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
-        case 2: hipLaunchKernelGGL((moe_down_kernel<S, WR, WK, 2>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
-        default: hipLaunchKernelGGL((moe_down_kernel<S, WR, WK, 4>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
+        case 1: hipLaunchKernelGGL((moe_down_kernel<S, WR, WK, 1, DEPTH>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
+        case 2: hipLaunchKernelGGL((moe_down_kernel<S, WR, WK, 2, DEPTH>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
+        default: hipLaunchKernelGGL((moe_down_kernel<S, WR, WK, 4, DEPTH>), dim3(blocks), dim3(64 * WR * WK), lds, st, a); break;
     }
+}
+
+// Measured on the Gemma-shaped layer at M = 32 over (WR, WK, DEPTH) in
+// {1, 2, 4, 8} x {1, 2, 4} x {2, 4}: one row wavefront, two split-K wavefronts
+// and four steps in flight read fastest for both passes (by 1-2% over 1, 4,
+// 2; wider row blocks, 4-8 row wavefronts, up to 40% slower).
+template <int S>
+static hipError_t moe_passes(const MoeArgs& a, int64_t Fs, bool gate_up, hipStream_t st) {
+    if (gate_up) moe_gate_up_launch<S, 1, 2, 4>(a, Fs, st);
+    moe_down_launch<S, 1, 2, 4>(a, Fs, st);
     return hipGetLastError();
 }
 
@@ -546,6 +611,56 @@ static Moe1Args moe1_args(int scheme, const MoeMats& W, const uint16_t* x, int k
     return a;
 }
 
+// The grouped gate/up pass (moe_grouped.hpp): up to 32 tokens, every K a
+// multiple of 128 (whole steps, even affine group counts), the activation
+// stage, the descriptors and the pair list within LDS.
+constexpr int kMoeGroupedMaxM = 32;
+static size_t moe_grouped_lds(int64_t M, int k, int64_t E, int64_t D) {
+    return (size_t)moe_gx_words((int)D, (int)M) * 4 + ((size_t)moe_slots(E, M * k) + 1) * 16 +
+           (size_t)M * k * 4;
+}
+static bool moe_grouped_ok(int64_t M, int k, int64_t E, int64_t D, int64_t F, int64_t Fs) {
+    return M >= 2 && M <= kMoeGroupedMaxM && D % 128 == 0 && F % 128 == 0 && Fs % 128 == 0 &&
+           moe_grouped_lds(M, k, E, D) <= 160 * 1024;
+}
+static GMat gmat(const MoeMat& m) { return GMat{m.codes, m.scale, m.bias, m.stride_c, m.stride_s, m.N, m.K}; }
+
+// The gate/up pass as one grouped launch: one workgroup per CU, 16
+// wavefronts staging x, 4 of them streaming codes (swept 2-8: 4 to 8 within
+// 1%, 2 slower).
+template <int S>
+static hipError_t moe_grouped_gate_up(const MoeArgs& a, hipStream_t st) {
+    constexpr int kCUs = 256;
+    MoeGArgs g{};
+    g.has_shared = a.has_shared;
+    g.M = a.M;
+    g.k = a.k;
+    g.slots = a.amax;
+    g.P = a.M * a.k;
+    g.x = a.x;
+    g.work = a.work;
+    g.pairs = a.pairs;
+    g.h = a.h;
+    g.hs = a.hs;
+    g.r0 = gmat(a.gate);
+    g.r1 = gmat(a.up);
+    if (a.has_shared) {
+        g.s0 = gmat(a.sgate);
+        g.s1 = gmat(a.sup);
+    }
+    g.NS = 4;
+    const size_t lds = moe_grouped_lds(a.M, a.k, a.E, a.gate.K);
+    auto kern = moe_grouped_kernel<S, 4>;
+    if (lds > 64 * 1024)
+        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipLaunchKernelGGL(kern, dim3(kCUs), dim3(1024), lds, st, g);
+    return hipGetLastError();
+}
+
+static hipError_t moe_multi(int scheme, const MoeMats& W, const uint16_t* x, int64_t M,
+                            const int32_t* ids, const float* wts, int k, void* ws, float* y,
+                            bool bucketed, hipStream_t st);
+
 hipError_t launch_moe_logits(int scheme, const MoeMats& W, const uint16_t* x, int64_t M,
                              const float* logits, int k, int32_t* ids, float* wts, void* ws,
                              float* y, hipStream_t st) {
@@ -558,28 +673,39 @@ hipError_t launch_moe_logits(int scheme, const MoeMats& W, const uint16_t* x, in
         return scheme == SYM4_G128 ? moe1_passes<SYM4_G128, true>(a, st)
                                    : moe1_passes<AFF4_G64, true>(a, st);
     }
-    if (E <= 128)
-        hipLaunchKernelGGL(topk_softmax_kernel<2>, dim3((unsigned)M), dim3(64), 0, st, logits, (int)E, k, ids, wts);
-    else if (E <= 256)
-        hipLaunchKernelGGL(topk_softmax_kernel<4>, dim3((unsigned)M), dim3(64), 0, st, logits, (int)E, k, ids, wts);
-    else
-        hipLaunchKernelGGL(topk_softmax_kernel<16>, dim3((unsigned)M), dim3(64), 0, st, logits, (int)E, k, ids, wts);
+    if (moe1_ok(M, k, W.D, W.F, W.Fs)) {  // one token, E > 128: top-k launch, then the M = 1 passes
+        if (E <= 256)
+            hipLaunchKernelGGL(topk_softmax_kernel<4>, dim3((unsigned)M), dim3(64), 0, st, logits, (int)E, k, ids, wts);
+        else
+            hipLaunchKernelGGL(topk_softmax_kernel<16>, dim3((unsigned)M), dim3(64), 0, st, logits, (int)E, k, ids, wts);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_moe(scheme, W, x, M, ids, wts, k, ws, y, st);
+    }
+    // several tokens: selection and bucketing in one workgroup
+    const MoeWorkspace L = moe_workspace_layout(M, k, E, W.D, W.F, W.Fs);
+    uint8_t* base = (uint8_t*)ws;
+    const int slots = moe_slots(E, M * k);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(1), dim3(1024), 0, st, logits, (int)M, (int)E, k, slots, ids, wts,
+                           (int4*)(base + L.work), (int32_t*)(base + L.pairs));
+    };
+    if (E <= 128) go(moe_select_bucket_kernel<2>);
+    else if (E <= 256) go(moe_select_bucket_kernel<4>);
+    else go(moe_select_bucket_kernel<16>);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_moe(scheme, W, x, M, ids, wts, k, ws, y, st);
+    return moe_multi(scheme, W, x, M, ids, wts, k, ws, y, true, st);
 }
 
-hipError_t launch_moe(int scheme, const MoeMats& W, const uint16_t* x, int64_t M, const int32_t* ids,
-                      const float* wts, int k, void* ws, float* y, hipStream_t st) {
+// The M > 1 path after routing: bucketing (unless `bucketed`: the selection
+// kernel did it), the expert passes and the combine.
+static hipError_t moe_multi(int scheme, const MoeMats& W, const uint16_t* x, int64_t M,
+                            const int32_t* ids, const float* wts, int k, void* ws, float* y,
+                            bool bucketed, hipStream_t st) {
     const int64_t E = W.E, D = W.D, F = W.F, Fs = W.Fs;
     const MoeWorkspace L = moe_workspace_layout(M, k, E, D, F, Fs);
     uint8_t* base = (uint8_t*)ws;
-    if (moe1_ok(M, k, D, F, Fs)) {
-        Moe1Args a = moe1_args(scheme, W, x, k, ws, y);
-        a.ids = ids;
-        a.wts = wts;
-        return scheme == SYM4_G128 ? moe1_passes<SYM4_G128>(a, st) : moe1_passes<AFF4_G64>(a, st);
-    }
     MoeArgs a{};
     a.gate = mm(W.gate[0], W.gate[1], W.gate[2], F, D, scheme);
     a.up = mm(W.up[0], W.up[1], W.up[2], F, D, scheme);
@@ -600,19 +726,39 @@ hipError_t launch_moe(int scheme, const MoeMats& W, const uint16_t* x, int64_t M
     a.hs = (uint16_t*)(base + L.hs);
     a.part = (float*)(base + L.part);
     a.sout = (float*)(base + L.sout);
-    a.amax = (int)std::min<int64_t>(E, M * k);
-    const int P = (int)(M * k);
-    hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(1024), 0, st, ids, P, (int)E, a.amax,
-                       (int4*)(base + L.work), (int32_t*)(base + L.pairs));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = scheme == SYM4_G128 ? moe_passes<SYM4_G128, 1, 4>(a, Fs, st)
-                            : moe_passes<AFF4_G64, 1, 4>(a, Fs, st);
+    a.amax = moe_slots(E, M * k);
+    hipError_t e;
+    if (!bucketed) {
+        const int P = (int)(M * k);
+        hipLaunchKernelGGL(moe_bucket_kernel, dim3(1), dim3(1024), 0, st, ids, P, (int)E, a.amax,
+                           (int4*)(base + L.work), (int32_t*)(base + L.pairs));
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // gate/up: the grouped launch where it applies, else per expert block
+    const bool grouped = moe_grouped_ok(M, k, E, D, F, Fs);
+    if (grouped) {
+        e = scheme == SYM4_G128 ? moe_grouped_gate_up<SYM4_G128>(a, st) : moe_grouped_gate_up<AFF4_G64>(a, st);
+        if (e != hipSuccess) return e;
+    }
+    e = scheme == SYM4_G128 ? moe_passes<SYM4_G128>(a, Fs, !grouped, st)
+                            : moe_passes<AFF4_G64>(a, Fs, !grouped, st);
     if (e != hipSuccess) return e;
     const int64_t tot = M * D;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
                        a.part, a.sout, wts, ids, (int)M, k, (int)D, (int)E, a.has_shared, y);
     return hipGetLastError();
+}
+
+hipError_t launch_moe(int scheme, const MoeMats& W, const uint16_t* x, int64_t M, const int32_t* ids,
+                      const float* wts, int k, void* ws, float* y, hipStream_t st) {
+    if (moe1_ok(M, k, W.D, W.F, W.Fs)) {
+        Moe1Args a = moe1_args(scheme, W, x, k, ws, y);
+        a.ids = ids;
+        a.wts = wts;
+        return scheme == SYM4_G128 ? moe1_passes<SYM4_G128>(a, st) : moe1_passes<AFF4_G64>(a, st);
+    }
+    return moe_multi(scheme, W, x, M, ids, wts, k, ws, y, false, st);
 }
 
 }  // namespace w4

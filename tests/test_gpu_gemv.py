@@ -51,6 +51,8 @@ def _run(scheme, N, K, M, name, rows=None, quantize_on_gpu=True):
     ("sym4_g128", 31, 128, 11),
     ("sym4_g128", 12370, 512, 3),     # > 256 row tiles: 4 per workgroup, ragged last workgroup
     ("aff4_g64", 600, 13888, 8),      # activations staged in chunks; odd group count
+    ("aff8_g64", 128, 2048, 32),      # router shape, several tokens: token tiles split over workgroups
+    ("sym4_g128", 40, 4096, 37),      # > 16 tokens (VALU multi-token path), ragged token split
 ])
 def test_gemv_matches_oracle(scheme, N, K, M):
     _run(scheme, N, K, M, f"small.{scheme}.{N}x{K}")

@@ -111,6 +111,18 @@ def test_moe_small_ragged_and_edge_ids(scheme):
     _moe_case(M, E, D, F, 0, k, scheme, 4, f"noshared.{scheme}", ids=ids, p=p)
 
 
+@pytest.mark.parametrize("scheme", ["sym4_g128", "aff4_g64"])
+@pytest.mark.parametrize("M", [20, 32])
+def test_moe_expert_with_more_than_16_pairs(scheme, M):
+    """Every token sends slot 0 to expert 1: its M pairs span two work
+    descriptors of at most 16 pairs (the grouped gate/up pass and the down pass
+    take one token tile per descriptor)."""
+    E, D, F, k = 8, 256, 384, 2
+    ids = np.stack([np.ones(M, np.int32), (np.arange(M) * 3 % E).astype(np.int32)], axis=1)
+    p = np.stack([np.full(M, 0.75), np.full(M, 0.25)], axis=1)
+    _moe_case(M, E, D, F, 256, k, scheme, 7, f"split.{scheme}.{M}", ids=ids, p=p)
+
+
 def test_moe_end_to_end_route_then_experts_and_determinism():
     M, E, D, F, Fs = 4, 128, 2048, 768, 2048
     _, (rc, rs, rb), qr = _router(E, D, 5, "e2e.router")
@@ -170,7 +182,9 @@ def _dev_stack(E, N, K, seed, name, scheme):
     (1, 128, 768, 2048, 8),   # one token, E <= 128: selection inside the gate/up pass
     (1, 64, 256, 0, 3),       # same path, fewer slots, no shared expert
     (1, 256, 256, 512, 8),    # one token, E > 128: a top-k launch first
-    (2, 128, 256, 512, 8),    # several tokens: top-k launch, then the bucketed passes
+    (2, 128, 256, 512, 8),    # several tokens: selection + bucketing in one workgroup, then the passes
+    (32, 128, 768, 2048, 8),  # the decode batch of the MoE bench
+    (20, 256, 256, 512, 8),   # > 16 tokens (two per wavefront), E > 128
 ])
 def test_moe_gemv_logits_equals_route_then_gemv(M, E, F, Fs, k):
     """w4a16_moe_gemv_logits from router logits gives, bit for bit, the ids and
