@@ -510,6 +510,8 @@ static void moe_down_launch(MoeArgs a, int64_t Fs, hipStream_t st) {
     }
 }
 
+static GMat gmat(const MoeMat& m) { return GMat{m.codes, m.scale, m.bias, m.stride_c, m.stride_s, m.N, m.K}; }
+
 // Measured on the Gemma-shaped layer at M = 32 over (WR, WK, DEPTH) in
 // {1, 2, 4, 8} x {1, 2, 4} x {2, 4}: one row wavefront, two split-K wavefronts
 // and four steps in flight read fastest for both passes (by 1-2% over 1, 4,
@@ -517,6 +519,33 @@ static void moe_down_launch(MoeArgs a, int64_t Fs, hipStream_t st) {
 template <int S>
 static hipError_t moe_passes(const MoeArgs& a, int64_t Fs, bool gate_up, hipStream_t st) {
     if (gate_up) moe_gate_up_launch<S, 1, 2, 4>(a, Fs, st);
+    // routed down: one workgroup per (descriptor, 64 rows) with the
+    // descriptor's h rows in LDS where it applies (M = 32 Gemma-shaped layer:
+    // the down pass ~87 -> ~27 us); the shared expert's down product then runs
+    // alone on the per-expert-block kernel
+    const int D = a.down.N, F = a.down.K;
+    const int groups = F / Traits<S>::GROUP;
+    const int nw = 4;  // wavefronts (16-row tiles) per workgroup: 4 measured 1% over 8, 4% over 16
+    if (D % (16 * nw) == 0 && F % 128 == 0 && groups <= 64) {
+        const int sg = groups <= 16 ? 16 : groups <= 32 ? 32 : 64;
+        const size_t lds = moe_down_lds_bytes(F, Traits<S>::GROUP, sg, nw);
+        MoeDownArgs d{gmat(a.down), a.h, a.work, a.pairs, a.part};
+        auto go = [&](auto kern) {
+            if (lds > 64 * 1024)
+                (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+            hipLaunchKernelGGL(kern, dim3(D / (16 * nw), a.amax), dim3(64 * nw), lds, st, d);
+        };
+        const bool deep = F / 128 >= 4;
+        if (sg == 16) deep ? go(moe_down_routed_kernel<S, 4, 16>) : go(moe_down_routed_kernel<S, 2, 16>);
+        else if (sg == 32) deep ? go(moe_down_routed_kernel<S, 4, 32>) : go(moe_down_routed_kernel<S, 2, 32>);
+        else deep ? go(moe_down_routed_kernel<S, 4, 64>) : go(moe_down_routed_kernel<S, 2, 64>);
+        if (a.has_shared) {
+            MoeArgs b = a;
+            b.amax = 0;  // shared blocks only
+            moe_down_launch<S, 1, 2, 4>(b, Fs, st);
+        }
+        return hipGetLastError();
+    }
     moe_down_launch<S, 1, 2, 4>(a, Fs, st);
     return hipGetLastError();
 }
@@ -623,7 +652,6 @@ static bool moe_grouped_ok(int64_t M, int k, int64_t E, int64_t D, int64_t F, in
     return M >= 2 && M <= kMoeGroupedMaxM && D % 128 == 0 && F % 128 == 0 && Fs % 128 == 0 &&
            moe_grouped_lds(M, k, E, D) <= 160 * 1024;
 }
-static GMat gmat(const MoeMat& m) { return GMat{m.codes, m.scale, m.bias, m.stride_c, m.stride_s, m.N, m.K}; }
 
 // The gate/up pass as one grouped launch: one workgroup per CU, 16
 // wavefronts staging x, 4 of them streaming codes (swept 2-8: 4 to 8 within

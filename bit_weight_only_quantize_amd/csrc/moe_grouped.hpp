@@ -17,8 +17,8 @@
 // (The same scheme for the down pass, whose activations are each pair's own h
 // row and so come from L2 with every step, measured slower than the
 // per-expert-block kernel: the gathers of those rows, four 16-byte loads per
-// lane per kilobyte of codes, dominate; sharing them over four row tiles per
-// item still left it behind.)
+// lane per kilobyte of codes, dominate. The down pass below stages them in
+// LDS per work descriptor instead.)
 //
 // The MFMA step is the skinny GEMM's (16 tokens x 32 k x 16 rows, codes
 // unpacked in registers, group sums from one MFMA against a ones operand).
@@ -340,6 +340,210 @@ __global__ __launch_bounds__(1024) void moe_grouped_kernel(MoeGArgs a) {
 #pragma unroll
     for (int u = 0; u < DEPTH - 1; ++u)
         if (full + u < Q) compute(cb[u]);
+}
+
+}  // namespace w4
+
+namespace w4 {
+
+// Routed down pass for several tokens: one workgroup per (work descriptor j,
+// block of 16 rows per wavefront of the expert's W_down). The descriptor's pairs (at
+// most 16) are the MFMA tokens: their h rows are gathered from L2 once per
+// workgroup into LDS in the A-operand layout (the skinny kernel's layout and
+// swizzle, with every (group, pair) activation sum), then wavefront w streams
+// row tile w over all K, its scales in a private LDS block, DEPTH steps of
+// code loads in flight, and writes part[pair][row]. A small LDS footprint (a
+// 768-wide h: 25 KB of activations) lets several workgroups share a CU, so one
+// workgroup's staging overlaps the others' streaming.
+struct MoeDownArgs {
+    GMat W;                 // routed W_down (stacked)
+    const uint16_t* h;      // [P][F]
+    const int4* work;       // descriptors (count <= 16); x < 0 past the last
+    const int32_t* pairs;   // [P]
+    float* part;            // [P][D]
+};
+
+// LDS bytes of moe_down_routed_kernel for K = F and SGMAX
+__host__ __device__ inline size_t moe_down_lds_bytes(int K, int group, int sgmax, int waves) {
+    const int steps = K / 128;
+    const int gps = 128 / group;
+    return ((size_t)steps * 16 * 16 * 4 + (size_t)steps * gps * 16 + (size_t)waves * 16 * (sgmax + 1)) * 4;
+}
+
+template <int S, int DEPTH, int SGMAX>
+__global__ __launch_bounds__(1024) void moe_down_routed_kernel(MoeDownArgs a) {
+    using T = Traits<S>;
+    using P = MfmaStep<S>;
+    constexpr int GPS = P::GPS;
+    constexpr int NV = T::GROUP / 8;  // 16-byte activation vectors per group
+    constexpr int U = 4;
+    constexpr uint32_t ONE2 = 0x3F803F80u;
+    extern __shared__ __align__(16) uint32_t lds[];
+    const int NT = blockDim.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, c16 = lane & 15;
+    const int4 wd = a.work[blockIdx.y];
+    const int e = __builtin_amdgcn_readfirstlane(wd.x);
+    if (e < 0) return;  // whole workgroup: an unused descriptor slot
+    const int first = __builtin_amdgcn_readfirstlane(wd.y), cnt = __builtin_amdgcn_readfirstlane(wd.z);
+    const int K = a.W.K, N = a.W.N;
+    const int groups = K / T::GROUP, steps = K / 128;
+    int mp = 2;
+    while (mp < cnt) mp *= 2;
+    const int aw = steps * 16 * mp * 4;
+    float* xd = reinterpret_cast<float*>(lds + steps * 16 * 16 * 4);
+    uint32_t* sl = lds + steps * 16 * 16 * 4 + steps * GPS * 16 + wave * 16 * (SGMAX + 1);
+    (void)aw;
+
+    const int row0 = (blockIdx.x * (NT / 64) + wave) * 16;  // N % (16 * wavefronts) == 0
+    const uint8_t* codes = a.W.codes + (int64_t)e * a.W.stride_c;
+    const uint8_t* scale = a.W.scale + (int64_t)e * a.W.stride_s;
+    const uint8_t* bias = T::AFFINE ? a.W.bias + (int64_t)e * a.W.stride_s : nullptr;
+    const uint8_t* crow = codes + (int64_t)(row0 + c16) * (K / 2);
+
+    // staging lanes: one token (pair) t and one 16-byte vector iv of a group;
+    // NV consecutive lanes cover a group of one pair (coalesced; the group's
+    // sum is a DPP reduction over them). Pairs past cnt store nothing.
+    const int C = mp * NV, GS = NT / C;
+    const int c = threadIdx.x % C;
+    const int gi0 = (int)threadIdx.x < GS * C ? (int)threadIdx.x / C : groups;
+    const int t = c / NV, iv = c % NV;
+    const bool live = t < cnt;
+    const uint16_t* xl = a.h + (int64_t)a.pairs[first + min(t, cnt - 1)] * K + iv * 8;
+    const int gg = GPS == 1 ? (iv >> 2) : ((iv >> 2) | (((iv >> 1) & 1) << 1));
+    u32x4_t xr[U];
+    auto stage_load = [&](int gb) {
+#pragma unroll
+        for (int j = 0; j < U; ++j) xr[j] = *gmem<u32x4_t>(xl + min(gb + j * GS, groups - 1) * T::GROUP);
+    };
+    auto stage_store = [&](int gb) {
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            float part = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) part = dot2_bf16(ONE2, xr[j][q], part);
+            const float sum = group_sum<NV>(part);
+            const int gi = gb + j * GS;
+            if (live && gi < groups) {
+                const int st = gi / GPS, q = gi - st * GPS;
+                const int d = GPS == 1 ? (iv & 3) : (2 * q + (iv & 1));
+                const u32x4_t o = {__builtin_amdgcn_perm(xr[j][2], xr[j][0], 0x05040100u),
+                                   __builtin_amdgcn_perm(xr[j][2], xr[j][0], 0x07060302u),
+                                   __builtin_amdgcn_perm(xr[j][3], xr[j][1], 0x05040100u),
+                                   __builtin_amdgcn_perm(xr[j][3], xr[j][1], 0x07060302u)};
+                const int lr = d * 4 + gg;
+                *reinterpret_cast<u32x4_t*>(lds + 4 * ((st * 16 + lr) * mp + (t ^ gswz(mp, lr)))) = o;
+                if (iv == 0) xd[(st * GPS + q) * 16 + t] = sum;
+            }
+        }
+    };
+    // 1. the first activation loads first (their waits then cover L2 only)
+    stage_load(gi0);
+    __builtin_amdgcn_sched_barrier(0);
+    // 2. the tile's scales (affine: bf16 scale low, bias high) for the
+    //    wavefront's LDS block, lanes over a row's groups
+    constexpr int SR = (SGMAX + 63) / 64;
+    uint32_t sv[SR][16];
+#pragma unroll
+    for (int hh = 0; hh < SR; ++hh) {
+        const int gl = min(lane + 64 * hh, groups - 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const uint32_t ei = (uint32_t)(row0 + r) * (uint32_t)groups + (uint32_t)gl;
+            if constexpr (T::AFFINE)
+                sv[hh][r] = (uint32_t)gmem<uint16_t>(scale)[ei] | ((uint32_t)gmem<uint16_t>(bias)[ei] << 16);
+            else
+                sv[hh][r] = gmem<uint32_t>(scale)[ei];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. the first DEPTH - 1 steps' codes, in the loop's order
+    using Buf = u32x4_t;
+    auto load = [&](Buf& B, int s) { B = *gmem<u32x4_t>(crow + (uint32_t)min(s, steps - 1) * 64 + 16 * g); };
+    Buf cb[DEPTH];
+#pragma unroll
+    for (int p = 0; p < DEPTH - 1; ++p) {
+        load(cb[p], p);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // 4. activations and sums, then the scales (unconditional stores)
+    stage_store(gi0);
+    for (int gb = gi0 + GS * U; gb < groups; gb += GS * U) {
+        stage_load(gb);
+        stage_store(gb);
+    }
+#pragma unroll
+    for (int hh = 0; hh < SR; ++hh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sl[r * (SGMAX + 1) + min(lane + 64 * hh, SGMAX)] = sv[hh][r];
+    __syncthreads();
+
+    // 5. the tile's steps
+    const uint32_t MASK = opaque(0x000F000Fu);
+    const uint32_t MAGIC = unpack_magic<S>();
+    const int tm = min(c16, cnt - 1);  // A rows past cnt read the last pair; their outputs are dropped
+    auto unpack = [&](uint32_t w) {
+        auto pair = [&](uint32_t v) {
+            return S == SYM4_G128 ? ((v & MASK) ^ MAGIC) : ((v & MASK) | MAGIC);
+        };
+        return as_bf16x8(pair(w), pair(w >> 4), pair(w >> 8), pair(w >> 12));
+    };
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const Buf& B, int s) {
+        bf16x8_t A[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            A[d] = *reinterpret_cast<const bf16x8_t*>(
+                lds + 4 * ((s * 16 + d * 4 + g) * mp + (tm ^ gswz(mp, d * 4 + g))));
+        uint32_t w[4] = {B[0], B[1], B[2], B[3]};
+        if constexpr (GPS == 2) {
+            const auto p02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+            const auto p13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+            w[0] = p02[0]; w[2] = p02[1];
+            w[1] = p13[0]; w[3] = p13[1];
+        }
+#pragma unroll
+        for (int q = 0; q < GPS; ++q) {
+            f32x4_t D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int d = 4 / GPS * q; d < 4 / GPS * (q + 1); ++d)
+                D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[d], unpack(w[d]), D, 0, 0, 0);
+            const f32x4_t DX = *reinterpret_cast<const f32x4_t*>(xd + (s * GPS + q) * 16 + 4 * g);
+            const uint32_t swd = sl[c16 * (SGMAX + 1) + s * GPS + q];
+            float sc, corr;
+            if constexpr (T::AFFINE) {
+                sc = bf16_bits_to_f32(swd & 0xFFFFu);
+                corr = fmaf(-T::BIAS, sc, __uint_as_float(swd & 0xFFFF0000u));
+            } else {
+                sc = __uint_as_float(swd);
+                corr = -T::BIAS * sc;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = fmaf(corr, DX[r], fmaf(sc, D[r], acc[r]));
+        }
+    };
+    const int full = steps / DEPTH * DEPTH;
+    for (int r0 = 0; r0 < full; r0 += DEPTH) {
+#pragma unroll
+        for (int u = 0; u < DEPTH; ++u) {
+            load(cb[(u + DEPTH - 1) % DEPTH], r0 + u + DEPTH - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(cb[u], r0 + u);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < DEPTH - 1; ++u)
+        if (full + u < steps) compute(cb[u], full + u);
+
+    // 6. part[pair][row] for the descriptor's pairs (slots past cnt hold
+    //    garbage: their group sums were never staged)
+    const int n = row0 + c16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int slot = 4 * g + r;
+        if (slot < cnt) a.part[(int64_t)a.pairs[first + slot] * N + n] = acc[r];
+    }
 }
 
 }  // namespace w4
