@@ -62,7 +62,7 @@ struct MoeMats {
 
 // Routed (token, slot) pairs per call: M <= 256 tokens times top_k <= 32.
 constexpr int kMoeMaxPairs = 256 * 32;
-constexpr int kMoeDescPairs = 16;  // pairs per work descriptor (one MFMA token tile)
+constexpr int kMoeDescPairs = 8;  // pairs per work descriptor (at most one MFMA token tile)
 // work descriptors for P pairs over E experts (one per 16 pairs of an expert)
 inline int moe_slots(int64_t E, int64_t P) {
     return (int)((E < P ? E : P) + (P + kMoeDescPairs - 1) / kMoeDescPairs);

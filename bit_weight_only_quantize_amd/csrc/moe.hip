@@ -24,7 +24,7 @@
 #include "gemv_mfma.hpp"
 #include "skinny.hpp"
 #include "moe1.hpp"
-#include "moe_grouped.hpp"
+#include "moe_routed.hpp"
 
 namespace w4 {
 
@@ -516,37 +516,55 @@ static GMat gmat(const MoeMat& m) { return GMat{m.codes, m.scale, m.bias, m.stri
 // {1, 2, 4, 8} x {1, 2, 4} x {2, 4}: one row wavefront, two split-K wavefronts
 // and four steps in flight read fastest for both passes (by 1-2% over 1, 4,
 // 2; wider row blocks, 4-8 row wavefronts, up to 40% slower).
-template <int S>
-static hipError_t moe_passes(const MoeArgs& a, int64_t Fs, bool gate_up, hipStream_t st) {
-    if (gate_up) moe_gate_up_launch<S, 1, 2, 4>(a, Fs, st);
-    // routed down: one workgroup per (descriptor, 64 rows) with the
-    // descriptor's h rows in LDS where it applies (M = 32 Gemma-shaped layer:
-    // the down pass ~87 -> ~27 us); the shared expert's down product then runs
-    // alone on the per-expert-block kernel
-    const int D = a.down.N, F = a.down.K;
-    const int groups = F / Traits<S>::GROUP;
-    const int nw = 4;  // wavefronts (16-row tiles) per workgroup: 4 measured 1% over 8, 4% over 16
-    if (D % (16 * nw) == 0 && F % 128 == 0 && groups <= 64) {
-        const int sg = groups <= 16 ? 16 : groups <= 32 ? 32 : 64;
-        const size_t lds = moe_down_lds_bytes(F, Traits<S>::GROUP, sg, nw);
-        MoeDownArgs d{gmat(a.down), a.h, a.work, a.pairs, a.part};
-        auto go = [&](auto kern) {
-            if (lds > 64 * 1024)
-                (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-            hipLaunchKernelGGL(kern, dim3(D / (16 * nw), a.amax), dim3(64 * nw), lds, st, d);
-        };
-        const bool deep = F / 128 >= 4;
-        if (sg == 16) deep ? go(moe_down_routed_kernel<S, 4, 16>) : go(moe_down_routed_kernel<S, 2, 16>);
-        else if (sg == 32) deep ? go(moe_down_routed_kernel<S, 4, 32>) : go(moe_down_routed_kernel<S, 2, 32>);
-        else deep ? go(moe_down_routed_kernel<S, 4, 64>) : go(moe_down_routed_kernel<S, 2, 64>);
-        if (a.has_shared) {
-            MoeArgs b = a;
-            b.amax = 0;  // shared blocks only
-            moe_down_launch<S, 1, 2, 4>(b, Fs, st);
-        }
-        return hipGetLastError();
+// Routed pass on moe_routed_kernel where it applies (rows a multiple of 64,
+// K of 128, at most 128 groups per row): returns false otherwise.
+template <int S, bool GU>
+static bool moe_routed_pass(const MoeArgs& a, hipStream_t st) {
+    constexpr int nw = 4;  // wavefronts (16-row tiles) per workgroup: 4 measured 1% over 8, 4% over 16
+    const GMat W0 = gmat(GU ? a.gate : a.down);
+    const int N = W0.N, K = W0.K;
+    const int groups = K / Traits<S>::GROUP;
+    if (N % (16 * nw) != 0 || K % 128 != 0 || groups > 128) return false;
+    const int sg = groups <= 16 ? 16 : groups <= 32 ? 32 : groups <= 64 ? 64 : 128;
+    const size_t lds = moe_routed_lds_bytes(K, Traits<S>::GROUP, sg, nw, GU ? 2 : 1);
+    if (lds > 160 * 1024) return false;
+    MoeRoutedArgs r{W0, GU ? gmat(a.up) : GMat{}, GU ? a.x : a.h, GU ? a.k : 1, a.work, a.pairs, a.h, a.part};
+    auto go = [&](auto kern) {
+        if (lds > 64 * 1024)
+            (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        hipLaunchKernelGGL(kern, dim3(N / (16 * nw), a.amax), dim3(64 * nw), lds, st, r);
+    };
+    const bool deep = K / 128 >= 4;  // four steps in flight, two for shorter rows
+    switch (sg) {
+        case 16: deep ? go(moe_routed_kernel<S, GU, 4, 16>) : go(moe_routed_kernel<S, GU, 2, 16>); break;
+        case 32: deep ? go(moe_routed_kernel<S, GU, 4, 32>) : go(moe_routed_kernel<S, GU, 2, 32>); break;
+        case 64: deep ? go(moe_routed_kernel<S, GU, 4, 64>) : go(moe_routed_kernel<S, GU, 2, 64>); break;
+        default: deep ? go(moe_routed_kernel<S, GU, 4, 128>) : go(moe_routed_kernel<S, GU, 2, 128>); break;
     }
-    moe_down_launch<S, 1, 2, 4>(a, Fs, st);
+    return true;
+}
+
+// The expert passes for several tokens: each routed pass on moe_routed_kernel
+// (one workgroup per work descriptor and 64 rows, the descriptor's
+// activation rows staged in LDS) followed by the shared expert's rows alone on the
+// per-expert-block kernel; where it does not apply, the per-expert-block
+// kernel for everything.
+template <int S>
+static hipError_t moe_passes(const MoeArgs& a, int64_t Fs, hipStream_t st) {
+    MoeArgs shared_only = a;
+    shared_only.amax = 0;  // the per-expert-block kernels' shared blocks only
+    if (moe_routed_pass<S, true>(a, st)) {
+        if (a.has_shared) moe_gate_up_launch<S, 1, 2, 4>(shared_only, Fs, st);
+    } else {
+        moe_gate_up_launch<S, 1, 2, 4>(a, Fs, st);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (moe_routed_pass<S, false>(a, st)) {
+        if (a.has_shared) moe_down_launch<S, 1, 2, 4>(shared_only, Fs, st);
+    } else {
+        moe_down_launch<S, 1, 2, 4>(a, Fs, st);
+    }
     return hipGetLastError();
 }
 
@@ -640,51 +658,6 @@ static Moe1Args moe1_args(int scheme, const MoeMats& W, const uint16_t* x, int k
     return a;
 }
 
-// The grouped gate/up pass (moe_grouped.hpp): up to 32 tokens, every K a
-// multiple of 128 (whole steps, even affine group counts), the activation
-// stage, the descriptors and the pair list within LDS.
-constexpr int kMoeGroupedMaxM = 32;
-static size_t moe_grouped_lds(int64_t M, int k, int64_t E, int64_t D) {
-    return (size_t)moe_gx_words((int)D, (int)M) * 4 + ((size_t)moe_slots(E, M * k) + 1) * 16 +
-           (size_t)M * k * 4;
-}
-static bool moe_grouped_ok(int64_t M, int k, int64_t E, int64_t D, int64_t F, int64_t Fs) {
-    return M >= 2 && M <= kMoeGroupedMaxM && D % 128 == 0 && F % 128 == 0 && Fs % 128 == 0 &&
-           moe_grouped_lds(M, k, E, D) <= 160 * 1024;
-}
-
-// The gate/up pass as one grouped launch: one workgroup per CU, 16
-// wavefronts staging x, 4 of them streaming codes (swept 2-8: 4 to 8 within
-// 1%, 2 slower).
-template <int S>
-static hipError_t moe_grouped_gate_up(const MoeArgs& a, hipStream_t st) {
-    constexpr int kCUs = 256;
-    MoeGArgs g{};
-    g.has_shared = a.has_shared;
-    g.M = a.M;
-    g.k = a.k;
-    g.slots = a.amax;
-    g.P = a.M * a.k;
-    g.x = a.x;
-    g.work = a.work;
-    g.pairs = a.pairs;
-    g.h = a.h;
-    g.hs = a.hs;
-    g.r0 = gmat(a.gate);
-    g.r1 = gmat(a.up);
-    if (a.has_shared) {
-        g.s0 = gmat(a.sgate);
-        g.s1 = gmat(a.sup);
-    }
-    g.NS = 4;
-    const size_t lds = moe_grouped_lds(a.M, a.k, a.E, a.gate.K);
-    auto kern = moe_grouped_kernel<S, 4>;
-    if (lds > 64 * 1024)
-        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    hipLaunchKernelGGL(kern, dim3(kCUs), dim3(1024), lds, st, g);
-    return hipGetLastError();
-}
-
 static hipError_t moe_multi(int scheme, const MoeMats& W, const uint16_t* x, int64_t M,
                             const int32_t* ids, const float* wts, int k, void* ws, float* y,
                             bool bucketed, hipStream_t st);
@@ -763,14 +736,7 @@ static hipError_t moe_multi(int scheme, const MoeMats& W, const uint16_t* x, int
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    // gate/up: the grouped launch where it applies, else per expert block
-    const bool grouped = moe_grouped_ok(M, k, E, D, F, Fs);
-    if (grouped) {
-        e = scheme == SYM4_G128 ? moe_grouped_gate_up<SYM4_G128>(a, st) : moe_grouped_gate_up<AFF4_G64>(a, st);
-        if (e != hipSuccess) return e;
-    }
-    e = scheme == SYM4_G128 ? moe_passes<SYM4_G128>(a, Fs, !grouped, st)
-                            : moe_passes<AFF4_G64>(a, Fs, !grouped, st);
+    e = scheme == SYM4_G128 ? moe_passes<SYM4_G128>(a, Fs, st) : moe_passes<AFF4_G64>(a, Fs, st);
     if (e != hipSuccess) return e;
     const int64_t tot = M * D;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,

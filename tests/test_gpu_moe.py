@@ -114,9 +114,9 @@ def test_moe_small_ragged_and_edge_ids(scheme):
 @pytest.mark.parametrize("scheme", ["sym4_g128", "aff4_g64"])
 @pytest.mark.parametrize("M", [20, 32])
 def test_moe_expert_with_more_than_16_pairs(scheme, M):
-    """Every token sends slot 0 to expert 1: its M pairs span two work
-    descriptors of at most 16 pairs (the grouped gate/up pass and the down pass
-    take one token tile per descriptor)."""
+    """Every token sends slot 0 to expert 1: its M pairs span several work
+    descriptors (at most 8 pairs each; the routed passes stage one
+    descriptor's activation rows per workgroup)."""
     E, D, F, k = 8, 256, 384, 2
     ids = np.stack([np.ones(M, np.int32), (np.arange(M) * 3 % E).astype(np.int32)], axis=1)
     p = np.stack([np.full(M, 0.75), np.full(M, 0.25)], axis=1)
