@@ -516,25 +516,46 @@ static GMat gmat(const MoeMat& m) { return GMat{m.codes, m.scale, m.bias, m.stri
 // {1, 2, 4, 8} x {1, 2, 4} x {2, 4}: one row wavefront, two split-K wavefronts
 // and four steps in flight read fastest for both passes (by 1-2% over 1, 4,
 // 2; wider row blocks, 4-8 row wavefronts, up to 40% slower).
-// Routed pass on moe_routed_kernel where it applies (rows a multiple of 64,
-// K of 128, at most 128 groups per row): returns false otherwise.
+// One launch of moe_routed_kernel over the routed descriptors (shared =
+// false) or over the shared expert's token descriptors (shared = true), where
+// it applies (rows a multiple of 64, K of 128, at most 128 groups per row):
+// false otherwise. (Both in one launch measured slower: its grid and LDS
+// layout must cover the larger of the two shapes.)
 template <int S, bool GU>
-static bool moe_routed_pass(const MoeArgs& a, hipStream_t st) {
+static bool moe_routed_launch(const MoeArgs& a, bool shared, hipStream_t st) {
     constexpr int nw = 4;  // wavefronts (16-row tiles) per workgroup: 4 measured 1% over 8, 4% over 16
-    const GMat W0 = gmat(GU ? a.gate : a.down);
-    const int N = W0.N, K = W0.K;
-    const int groups = K / Traits<S>::GROUP;
-    if (N % (16 * nw) != 0 || K % 128 != 0 || groups > 128) return false;
+    MoeRoutedArgs r{};
+    if (shared) {
+        r.S0 = gmat(GU ? a.sgate : a.sdown);
+        if (GU) r.S1 = gmat(a.sup);
+    } else {
+        r.W0 = gmat(GU ? a.gate : a.down);
+        if (GU) r.W1 = gmat(a.up);
+    }
+    const GMat& W = shared ? r.S0 : r.W0;
+    const int groups = W.K / Traits<S>::GROUP;
+    if (W.N % (16 * nw) != 0 || W.K % 128 != 0 || groups > 128) return false;
     const int sg = groups <= 16 ? 16 : groups <= 32 ? 32 : groups <= 64 ? 64 : 128;
-    const size_t lds = moe_routed_lds_bytes(K, Traits<S>::GROUP, sg, nw, GU ? 2 : 1);
+    const size_t lds = moe_routed_lds_bytes(W.K, Traits<S>::GROUP, sg, nw, GU ? 2 : 1);
     if (lds > 160 * 1024) return false;
-    MoeRoutedArgs r{W0, GU ? gmat(a.up) : GMat{}, GU ? a.x : a.h, GU ? a.k : 1, a.work, a.pairs, a.h, a.part};
+    r.xin = GU ? a.x : a.h;
+    r.xsh = GU ? a.x : a.hs;
+    r.k = GU ? a.k : 1;
+    r.work = a.work;
+    r.pairs = a.pairs;
+    r.h = a.h;
+    r.hs = a.hs;
+    r.part = a.part;
+    r.sout = a.sout;
+    r.M = a.M;
+    r.kmax = W.K;
+    const int ny = shared ? (a.M + kMoeDescPairs - 1) / kMoeDescPairs : a.amax;
     auto go = [&](auto kern) {
         if (lds > 64 * 1024)
             (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        hipLaunchKernelGGL(kern, dim3(N / (16 * nw), a.amax), dim3(64 * nw), lds, st, r);
+        hipLaunchKernelGGL(kern, dim3(W.N / (16 * nw), ny), dim3(64 * nw), lds, st, r);
     };
-    const bool deep = K / 128 >= 4;  // four steps in flight, two for shorter rows
+    const bool deep = W.K / 128 >= 4;  // four steps in flight, two for shorter rows
     switch (sg) {
         case 16: deep ? go(moe_routed_kernel<S, GU, 4, 16>) : go(moe_routed_kernel<S, GU, 2, 16>); break;
         case 32: deep ? go(moe_routed_kernel<S, GU, 4, 32>) : go(moe_routed_kernel<S, GU, 2, 32>); break;
@@ -544,27 +565,30 @@ static bool moe_routed_pass(const MoeArgs& a, hipStream_t st) {
     return true;
 }
 
-// The expert passes for several tokens: each routed pass on moe_routed_kernel
-// (one workgroup per work descriptor and 64 rows, the descriptor's
-// activation rows staged in LDS) followed by the shared expert's rows alone on the
-// per-expert-block kernel; where it does not apply, the per-expert-block
-// kernel for everything.
+template <int S, bool GU>
+static void moe_pass(const MoeArgs& a, int64_t Fs, hipStream_t st) {
+    const bool routed = moe_routed_launch<S, GU>(a, false, st);
+    const bool shared = a.has_shared && moe_routed_launch<S, GU>(a, true, st);
+    if (routed && (shared || !a.has_shared)) return;
+    // the per-expert-block kernel for what the routed kernel did not take
+    MoeArgs b = a;
+    if (routed) b.amax = 0;           // its shared blocks only
+    if (shared) b.has_shared = 0;     // its routed blocks only
+    if (GU) moe_gate_up_launch<S, 1, 2, 4>(b, Fs, st);
+    else moe_down_launch<S, 1, 2, 4>(b, Fs, st);
+}
+
+// The expert passes for several tokens: each pass on moe_routed_kernel (one
+// workgroup per work descriptor and 64 rows, the descriptor's activation
+// rows staged in LDS; the shared expert in a launch of its own as
+// descriptors of 8 tokens), or where it does not apply on the
+// per-expert-block kernel.
 template <int S>
 static hipError_t moe_passes(const MoeArgs& a, int64_t Fs, hipStream_t st) {
-    MoeArgs shared_only = a;
-    shared_only.amax = 0;  // the per-expert-block kernels' shared blocks only
-    if (moe_routed_pass<S, true>(a, st)) {
-        if (a.has_shared) moe_gate_up_launch<S, 1, 2, 4>(shared_only, Fs, st);
-    } else {
-        moe_gate_up_launch<S, 1, 2, 4>(a, Fs, st);
-    }
+    moe_pass<S, true>(a, Fs, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (moe_routed_pass<S, false>(a, st)) {
-        if (a.has_shared) moe_down_launch<S, 1, 2, 4>(shared_only, Fs, st);
-    } else {
-        moe_down_launch<S, 1, 2, 4>(a, Fs, st);
-    }
+    moe_pass<S, false>(a, Fs, st);
     return hipGetLastError();
 }
 

@@ -53,14 +53,23 @@ __device__ __forceinline__ int gswz(int mp, int lr) {
 // h[pair][row] = bf16(gelu(g) * u), or part[pair][row]. A small LDS footprint
 // and few wavefronts (4) let several workgroups share a CU, so one
 // workgroup's staging overlaps the others' streaming.
+// The shared expert, when present (S0.codes set), comes first as
+// ceil(M / kMoeDescPairs) token descriptors of its own matrices (token t of
+// descriptor s is token s * kMoeDescPairs + t); the amax routed descriptor
+// slots follow.
 struct MoeRoutedArgs {
     GMat W0, W1;            // gate, up (gate/up pass) or down (W1 unused)
-    const uint16_t* xin;    // gate/up: x [M][D]; down: h [P][F]
+    GMat S0, S1;            // the shared expert's, same roles
+    const uint16_t* xin;    // routed activations: gate/up x [M][D]; down h [P][F]
+    const uint16_t* xsh;    // shared activations: gate/up x [M][D]; down hs [M][Fs]
     int k;                  // gate/up: slots per token (pair -> token); down: 1 (pair -> h row)
     const int4* work;       // descriptors (count <= kMoeDescPairs); x < 0 past the last
     const int32_t* pairs;   // [P]
     uint16_t* h;            // gate/up out [P][F]
+    uint16_t* hs;           // gate/up out [M][Fs]
     float* part;            // down out [P][D]
+    float* sout;            // down out [M][D]
+    int M, kmax;            // tokens, longest K (LDS layout)
 };
 
 constexpr int kRoutedMp = 8;  // activation rows staged per descriptor (>= kMoeDescPairs)
@@ -88,16 +97,30 @@ __global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c16 = lane & 15;
-    const int4 wd = a.work[blockIdx.y];
-    const int e = __builtin_amdgcn_readfirstlane(wd.x);
-    if (e < 0) return;  // whole workgroup: an unused descriptor slot
-    const int first = __builtin_amdgcn_readfirstlane(wd.y), cnt = __builtin_amdgcn_readfirstlane(wd.z);
-    const int K = a.W0.K, N = a.W0.N;
+    // the shared expert's descriptors come first (they have the longest
+    // rows, so they start before the routed ones rather than trail them)
+    const int sdesc = a.S0.codes ? (a.M + kMoeDescPairs - 1) / kMoeDescPairs : 0;
+    const bool sh = (int)blockIdx.y < sdesc;
+    int e = 0, first, cnt;
+    if (!sh) {
+        const int4 wd = a.work[blockIdx.y - sdesc];
+        e = __builtin_amdgcn_readfirstlane(wd.x);
+        if (e < 0) return;  // whole workgroup: an unused descriptor slot
+        first = __builtin_amdgcn_readfirstlane(wd.y);
+        cnt = __builtin_amdgcn_readfirstlane(wd.z);
+    } else {
+        first = blockIdx.y * kMoeDescPairs;
+        cnt = min(kMoeDescPairs, a.M - first);
+    }
+    const GMat& W0 = sh ? a.S0 : a.W0;
+    const int K = W0.K, N = W0.N;
+    if ((int)blockIdx.x * (NT / 64) * 16 >= N) return;  // whole workgroup: past this matrix's rows
     const int groups = K / T::GROUP, steps = K / 128;
     int mp = 2;
     while (mp < cnt) mp *= 2;
-    float* xd = reinterpret_cast<float*>(lds + steps * 16 * kRoutedMp * 4);
-    uint32_t* sl = lds + steps * 16 * kRoutedMp * 4 + steps * GPS * 16 + wave * NM * 16 * (SGMAX + 1);
+    const int smax = a.kmax / 128;  // the LDS layout is the longest K's
+    float* xd = reinterpret_cast<float*>(lds + smax * 16 * kRoutedMp * 4);
+    uint32_t* sl = lds + smax * 16 * kRoutedMp * 4 + smax * GPS * 16 + wave * NM * 16 * (SGMAX + 1);
 
     const int row0 = (blockIdx.x * (NT / 64) + wave) * 16;  // N % (16 * wavefronts) == 0
     const uint8_t* crow[NM];
@@ -105,7 +128,7 @@ __global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
     const uint8_t* bil[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-        const GMat& W = m ? a.W1 : a.W0;
+        const GMat& W = sh ? (m ? a.S1 : a.S0) : (m ? a.W1 : a.W0);
         crow[m] = W.codes + (int64_t)e * W.stride_c + (int64_t)(row0 + c16) * (K / 2);
         scl[m] = W.scale + (int64_t)e * W.stride_s;
         bil[m] = T::AFFINE ? W.bias + (int64_t)e * W.stride_s : nullptr;
@@ -119,7 +142,8 @@ __global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
     const int gi0 = (int)threadIdx.x < GS * C ? (int)threadIdx.x / C : groups;
     const int t = c / NV, iv = c % NV;
     const bool live = t < cnt;
-    const uint16_t* xl = a.xin + (int64_t)(a.pairs[first + min(t, cnt - 1)] / a.k) * K + iv * 8;
+    const int xrow = sh ? first + min(t, cnt - 1) : a.pairs[first + min(t, cnt - 1)] / a.k;
+    const uint16_t* xl = (sh ? a.xsh : a.xin) + (int64_t)xrow * K + iv * 8;
     const int gg = GPS == 1 ? (iv >> 2) : ((iv >> 2) | (((iv >> 1) & 1) << 1));
     u32x4_t xr[U];
     auto stage_load = [&](int gb) {
@@ -268,11 +292,11 @@ __global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
     for (int r = 0; r < 4; ++r) {
         const int slot = 4 * g + r;
         if (slot < cnt) {
-            const int64_t pr = a.pairs[first + slot];
+            const int64_t pr = sh ? first + slot : a.pairs[first + slot];
             if constexpr (GU)
-                a.h[pr * N + n] = (uint16_t)f32_to_bf16_rne(gelu_tanh(acc[0][r]) * acc[1][r]);
+                (sh ? a.hs : a.h)[pr * N + n] = (uint16_t)f32_to_bf16_rne(gelu_tanh(acc[0][r]) * acc[1][r]);
             else
-                a.part[pr * N + n] = acc[0][r];
+                (sh ? a.sout : a.part)[pr * N + n] = acc[0][r];
         }
     }
 }
