@@ -181,14 +181,12 @@ hipError_t launch_route(int scheme, const void* codes, const void* scale, const 
 // ---------------------------------------------------------------- bucketing
 // One 1024-thread workgroup. Pair p = m * k + j (token m, slot j), P <=
 // kMoeMaxPairs, expert ids already in LDS (sid, -1 for ids outside [0, E)).
-// For every expert e, the pairs routed to it in increasing p; the experts with
-// at least one pair get work descriptors {e, first pair index, pair count},
-// one per kMoeDescPairs pairs (so a descriptor is one MFMA token tile), in
-// increasing e; the remaining descriptors up to `slots` are {-1, 0, 0} and
-// descriptor `slots` holds {number of descriptors in use, 0, 0}. Counts
-// use LDS integer atomics (exact in any order); a pair's place is the
-// expert's offset plus the number of earlier pairs of the same expert, so the
-// output is deterministic.
+// For every expert e, the pairs routed to it (in no fixed order); the experts
+// with at least one pair get work descriptors {e, first pair index, pair
+// count}, one per kMoeDescPairs pairs, in increasing e; the remaining
+// descriptors up to `slots` are {-1, 0, 0} and descriptor `slots` holds
+// {number of descriptors in use, 0, 0}. Counts use LDS integer atomics
+// (exact in any order).
 __device__ __forceinline__ void bucket_pairs(const int* sid, int P, int E, int slots,
                                              int4* __restrict__ work, int32_t* __restrict__ pairs) {
     __shared__ int cnt[1024], off[1024], act[1024];
@@ -230,19 +228,14 @@ __device__ __forceinline__ void bucket_pairs(const int* sid, int P, int E, int s
             for (int i = 0; i * kMoeDescPairs < cnt[e]; ++i)
                 work[act[e] + i] = make_int4(e, off[e] + i * kMoeDescPairs,
                                              min(kMoeDescPairs, cnt[e] - i * kMoeDescPairs), 0);
-    // rank among earlier pairs of the same expert: every lane of a wavefront
-    // reads the same sid words (LDS broadcast), four at a time
-    const int4* sid4 = reinterpret_cast<const int4*>(sid);
+    // a pair's place inside its expert's list comes from an LDS atomic, in
+    // no fixed order: the expert passes compute every pair's outputs from its
+    // own activation row alone, so the order changes no result bit
+    for (int e = t; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
     for (int p = t; p < P; p += blockDim.x) {
         const int e = sid[p];
-        if (e < 0) continue;
-        int rank = 0;
-        for (int q = 0; q < p / 4; ++q) {
-            const int4 v = sid4[q];
-            rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
-        }
-        for (int q = p & ~3; q < p; ++q) rank += sid[q] == e;
-        pairs[off[e] + rank] = p;
+        if (e >= 0) pairs[off[e] + atomicAdd(&cnt[e], 1)] = p;
     }
     for (int s = n_act + t; s < slots; s += blockDim.x) work[s] = make_int4(-1, 0, 0, 0);
     if (t == 0) work[slots] = make_int4(n_act, 0, 0, 0);
