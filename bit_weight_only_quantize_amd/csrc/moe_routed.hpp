@@ -53,10 +53,11 @@ __device__ __forceinline__ int gswz(int mp, int lr) {
 // h[pair][row] = bf16(gelu(g) * u), or part[pair][row]. A small LDS footprint
 // and few wavefronts (4) let several workgroups share a CU, so one
 // workgroup's staging overlaps the others' streaming.
-// The shared expert, when present (S0.codes set), comes first as
-// ceil(M / kMoeDescPairs) token descriptors of its own matrices (token t of
-// descriptor s is token s * kMoeDescPairs + t); the amax routed descriptor
-// slots follow.
+// A launch covers the shared expert (S0.codes set) as ceil(M /
+// kMoeDescPairs) token descriptors of its own matrices (token t of descriptor
+// s is token s * kMoeDescPairs + t), the routed descriptor slots (W0.codes
+// set), or both; one workgroup per (descriptor, row block), the shared
+// expert's first. Both kinds in one launch share its LDS layout (kmax).
 struct MoeRoutedArgs {
     GMat W0, W1;            // gate, up (gate/up pass) or down (W1 unused)
     GMat S0, S1;            // the shared expert's, same roles
@@ -97,24 +98,31 @@ __global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c16 = lane & 15;
-    // the shared expert's descriptors come first (they have the longest
-    // rows, so they start before the routed ones rather than trail them)
+    // workgroup b: the shared expert's (descriptor, row block) pairs first,
+    // then the routed ones
+    const int rows = (NT / 64) * 16;  // per workgroup
     const int sdesc = a.S0.codes ? (a.M + kMoeDescPairs - 1) / kMoeDescPairs : 0;
-    const bool sh = (int)blockIdx.y < sdesc;
-    int e = 0, first, cnt;
-    if (!sh) {
-        const int4 wd = a.work[blockIdx.y - sdesc];
+    const int rbs = a.S0.codes ? a.S0.N / rows : 0, rbr = a.W0.codes ? a.W0.N / rows : 0;
+    int b = blockIdx.x;
+    const bool sh = b < sdesc * rbs;
+    int e = 0, first, cnt, rb;
+    if (sh) {
+        const int j = b / rbs;
+        rb = b - j * rbs;
+        first = j * kMoeDescPairs;
+        cnt = min(kMoeDescPairs, a.M - first);
+    } else {
+        b -= sdesc * rbs;
+        const int j = b / rbr;
+        rb = b - j * rbr;
+        const int4 wd = a.work[j];
         e = __builtin_amdgcn_readfirstlane(wd.x);
         if (e < 0) return;  // whole workgroup: an unused descriptor slot
         first = __builtin_amdgcn_readfirstlane(wd.y);
         cnt = __builtin_amdgcn_readfirstlane(wd.z);
-    } else {
-        first = blockIdx.y * kMoeDescPairs;
-        cnt = min(kMoeDescPairs, a.M - first);
     }
     const GMat& W0 = sh ? a.S0 : a.W0;
     const int K = W0.K, N = W0.N;
-    if ((int)blockIdx.x * (NT / 64) * 16 >= N) return;  // whole workgroup: past this matrix's rows
     const int groups = K / T::GROUP, steps = K / 128;
     int mp = 2;
     while (mp < cnt) mp *= 2;
@@ -122,7 +130,7 @@ __global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
     float* xd = reinterpret_cast<float*>(lds + smax * 16 * kRoutedMp * 4);
     uint32_t* sl = lds + smax * 16 * kRoutedMp * 4 + smax * GPS * 16 + wave * NM * 16 * (SGMAX + 1);
 
-    const int row0 = (blockIdx.x * (NT / 64) + wave) * 16;  // N % (16 * wavefronts) == 0
+    const int row0 = rb * rows + wave * 16;  // N % rows == 0
     const uint8_t* crow[NM];
     const uint8_t* scl[NM];
     const uint8_t* bil[NM];
