@@ -182,7 +182,7 @@ def _dev_stack(E, N, K, seed, name, scheme):
     (1, 128, 768, 2048, 8),   # one token, E <= 128: selection inside the gate/up pass
     (1, 64, 256, 0, 3),       # same path, fewer slots, no shared expert
     (1, 256, 256, 512, 8),    # one token, E > 128: a top-k launch first
-    (2, 128, 256, 512, 8),    # several tokens: selection + bucketing in one workgroup, then the passes
+    (2, 128, 256, 512, 8),    # several tokens: top-k launch, then the bucketed passes
     (32, 128, 768, 2048, 8),  # the decode batch of the MoE bench
     (20, 256, 256, 512, 8),   # > 16 tokens (two per wavefront), E > 128
 ])
