@@ -310,8 +310,8 @@ def run_moe(c: Ctx, a):
     logits = torch.empty((M, E), dtype=torch.float32, device=c.dev)
     y = torch.empty((M, D), dtype=torch.float32, device=c.dev)
     # Router GEMV, then selection + experts in one call (one token: the
-    # selection runs inside the gate/up pass; several: selection and bucketing
-    # share one workgroup).
+    # selection runs inside the gate/up pass; several: a top-k launch with a
+    # workgroup per token, then one bucketing workgroup).
     one = M == 1
 
     def step():
@@ -334,12 +334,12 @@ def run_moe(c: Ctx, a):
                         "experts": E, "top_k": k, "d_model": D, "expert_ffn": F, "shared_ffn": Fs,
                         "scheme": "aff4_g64 experts/shared, aff8_g64 router",
                         "launches_per_layer": ("router gemv, gate/up with the top-k inside, down" if one else
-                                               "router gemv, top-k + bucketing, gate/up, down, combine")})
+                                               "router gemv, top-k, bucketing, gate/up, down, combine")})
     out["hbm_TBps"] = round(tbs, 4)
     out["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
     out["distinct_experts_per_layer"] = sum(distinct) / len(distinct)
     out["step_bytes"] = step_bytes
-    out["roofline"] = hbm_roofline(f"whole MoE layer ({3 if one else 5} launches)", step_bytes // layers,
+    out["roofline"] = hbm_roofline(f"whole MoE layer ({3 if one else 6} launches)", step_bytes // layers,
                                    ms * 1e3 / layers)
     return out
 
