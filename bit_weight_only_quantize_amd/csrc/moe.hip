@@ -394,23 +394,43 @@ __global__ __launch_bounds__(64 * WR * WK) void moe_down_kernel(MoeArgs a) {
     }
 }
 
-// y[m][n] = shared[m][n] + sum_j w[m][j] * part[m*k + j][n]   (fixed j order)
+// y[m][n] = shared[m][n] + sum_j w[m][j] * part[m*k + j][n]   (fixed j order;
+// slots with an id outside [0, E) are skipped). A thread owns 4 consecutive
+// outputs (D % 4 == 0); every slot's loads are issued before the first FMA,
+// eight slots at a time, and an unused slot's partial (never written: it may
+// hold anything) is dropped by a select, not multiplied by zero.
+constexpr int kCombineSlots = 8;
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ part,
                                                           const float* __restrict__ sout,
                                                           const float* __restrict__ wts,
                                                           const int32_t* __restrict__ ids, int M,
                                                           int k, int D, int E, int has_shared,
                                                           float* __restrict__ y) {
+    const int D4 = D / 4;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)M * D) return;
-    const int m = (int)(i / D), n = (int)(i % D);
-    float acc = has_shared ? sout[i] : 0.f;
-    for (int j = 0; j < k; ++j) {
-        const int e = ids[(int64_t)m * k + j];
-        if (e < 0 || e >= E) continue;
-        acc = fmaf(wts[(int64_t)m * k + j], part[((int64_t)m * k + j) * D + n], acc);
+    if (i >= (int64_t)M * D4) return;
+    const int m = (int)(i / D4), n4 = (int)(i % D4);
+    const f32x4_t* part4 = reinterpret_cast<const f32x4_t*>(part);
+    f32x4_t acc = has_shared ? reinterpret_cast<const f32x4_t*>(sout)[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < k; j0 += kCombineSlots) {
+        int e[kCombineSlots];
+        float w[kCombineSlots];
+        f32x4_t p[kCombineSlots];
+#pragma unroll
+        for (int u = 0; u < kCombineSlots; ++u) {
+            const int64_t pj = (int64_t)m * k + min(j0 + u, k - 1);
+            e[u] = ids[pj];
+            w[u] = wts[pj];
+            p[u] = part4[pj * D4 + n4];
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineSlots; ++u) {
+            const bool use = j0 + u < k && e[u] >= 0 && e[u] < E;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = use ? fmaf(w[u], p[u][r], acc[r]) : acc[r];
+        }
     }
-    y[i] = acc;
+    reinterpret_cast<f32x4_t*>(y)[i] = acc;
 }
 
 // ---------------------------------------------------------------- host side
@@ -482,30 +502,31 @@ static GMat gmat(const MoeMat& m) { return GMat{m.codes, m.scale, m.bias, m.stri
 // One launch of moe_routed_kernel over the routed descriptors and/or the
 // shared expert's token descriptors, where it applies (rows a multiple of 64,
 // K of 128, at most 128 groups per row): false otherwise.
-template <int S, bool GU>
-static bool moe_routed_launch(const MoeArgs& a, bool routed, bool shared, hipStream_t st) {
-    constexpr int nw = 4;  // wavefronts (16-row tiles) per workgroup: 4 measured 1% over 8, 4% over 16
+template <int S, bool GU, int RT>
+static bool moe_routed_launch_rt(const MoeArgs& a, bool routed, bool shared, hipStream_t st) {
+    constexpr int nw = 4;  // wavefronts per workgroup: 4 measured 1% over 8, 4% over 16
+    constexpr int rows = 16 * nw * RT;
     MoeRoutedArgs r{};
     int kmax = 0, blocks = 0;
     bool ok = true;
     if (shared) {
         r.S0 = gmat(GU ? a.sgate : a.sdown);
         if (GU) r.S1 = gmat(a.sup);
-        ok = ok && r.S0.N % (16 * nw) == 0 && r.S0.K % 128 == 0;
+        ok = ok && r.S0.N % rows == 0 && r.S0.K % 128 == 0;
         kmax = std::max(kmax, r.S0.K);
-        blocks += (a.M + kMoeDescPairs - 1) / kMoeDescPairs * (r.S0.N / (16 * nw));
+        blocks += (a.M + kMoeDescPairs - 1) / kMoeDescPairs * (r.S0.N / rows);
     }
     if (routed) {
         r.W0 = gmat(GU ? a.gate : a.down);
         if (GU) r.W1 = gmat(a.up);
-        ok = ok && r.W0.N % (16 * nw) == 0 && r.W0.K % 128 == 0;
+        ok = ok && r.W0.N % rows == 0 && r.W0.K % 128 == 0;
         kmax = std::max(kmax, r.W0.K);
-        blocks += a.amax * (r.W0.N / (16 * nw));
+        blocks += a.amax * (r.W0.N / rows);
     }
     const int groups = kmax / Traits<S>::GROUP;
     if (!ok || groups > 128) return false;
     const int sg = groups <= 16 ? 16 : groups <= 32 ? 32 : groups <= 64 ? 64 : 128;
-    const size_t lds = moe_routed_lds_bytes(kmax, Traits<S>::GROUP, sg, nw, GU ? 2 : 1);
+    const size_t lds = moe_routed_lds_bytes(kmax, Traits<S>::GROUP, sg, nw, GU ? 2 : RT);
     if (lds > 160 * 1024) return false;
     r.xin = GU ? a.x : a.h;
     r.xsh = GU ? a.x : a.hs;
@@ -525,12 +546,25 @@ static bool moe_routed_launch(const MoeArgs& a, bool routed, bool shared, hipStr
     };
     const bool deep = kmax / 128 >= 4;  // four steps in flight, two for shorter rows
     switch (sg) {
-        case 16: deep ? go(moe_routed_kernel<S, GU, 4, 16>) : go(moe_routed_kernel<S, GU, 2, 16>); break;
-        case 32: deep ? go(moe_routed_kernel<S, GU, 4, 32>) : go(moe_routed_kernel<S, GU, 2, 32>); break;
-        case 64: deep ? go(moe_routed_kernel<S, GU, 4, 64>) : go(moe_routed_kernel<S, GU, 2, 64>); break;
-        default: deep ? go(moe_routed_kernel<S, GU, 4, 128>) : go(moe_routed_kernel<S, GU, 2, 128>); break;
+        case 16: deep ? go(moe_routed_kernel<S, GU, 4, 16, RT>) : go(moe_routed_kernel<S, GU, 2, 16, RT>); break;
+        case 32: deep ? go(moe_routed_kernel<S, GU, 4, 32, RT>) : go(moe_routed_kernel<S, GU, 2, 32, RT>); break;
+        case 64: deep ? go(moe_routed_kernel<S, GU, 4, 64, RT>) : go(moe_routed_kernel<S, GU, 2, 64, RT>); break;
+        default: deep ? go(moe_routed_kernel<S, GU, 4, 128, RT>) : go(moe_routed_kernel<S, GU, 2, 128, RT>); break;
     }
     return true;
+}
+
+template <int S, bool GU>
+static bool moe_routed_launch(const MoeArgs& a, bool routed, bool shared, hipStream_t st) {
+    if constexpr (GU) {
+        return moe_routed_launch_rt<S, GU, 1>(a, routed, shared, st);
+    } else {
+        // down: two row tiles per wavefront (the Gemma-shaped layer at M = 32:
+        // 10.5k -> 10.9k tok/s; four hold 240 registers, one wavefront per SIMD,
+        // and measured 9.9k)
+        return moe_routed_launch_rt<S, GU, 2>(a, routed, shared, st) ||
+               moe_routed_launch_rt<S, GU, 1>(a, routed, shared, st);
+    }
 }
 
 // A pass: routed and shared descriptors in one launch where one LDS layout
@@ -720,7 +754,7 @@ static hipError_t moe_multi(int scheme, const MoeMats& W, const uint16_t* x, int
     if (e != hipSuccess) return e;
     e = scheme == SYM4_G128 ? moe_passes<SYM4_G128>(a, Fs, st) : moe_passes<AFF4_G64>(a, Fs, st);
     if (e != hipSuccess) return e;
-    const int64_t tot = M * D;
+    const int64_t tot = M * D / 4;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
                        a.part, a.sout, wts, ids, (int)M, k, (int)D, (int)E, a.has_shared, y);
     return hipGetLastError();

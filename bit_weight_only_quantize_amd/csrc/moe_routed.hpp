@@ -42,14 +42,15 @@ __device__ __forceinline__ int gswz(int mp, int lr) {
 
 
 // Routed expert passes for several tokens: one workgroup per (work
-// descriptor j, block of 16 rows per wavefront of the expert's matrices). The
+// descriptor j, block of 16 * RT rows per wavefront of the expert's
+// matrices). The
 // descriptor's pairs (at most kMoeDescPairs) are the MFMA tokens: their
 // activation rows -- x of the pair's token for gate/up, the pair's own h row
 // for down -- are gathered from L2 once per workgroup into LDS in the
 // A-operand layout (the skinny kernel's layout and swizzle, with every
-// (group, pair) activation sum). Wavefront w then streams row tile w of the
-// pass's matrices (gate and up, or down) over all K, its scales in a private
-// LDS block, DEPTH steps of code loads in flight, and writes its outputs:
+// (group, pair) activation sum). Wavefront w then streams its row tile of
+// gate and up, or its RT row tiles of down, over all K, its scales in a
+// private LDS block, DEPTH steps of code loads in flight, and writes its outputs:
 // h[pair][row] = bf16(gelu(g) * u), or part[pair][row]. A small LDS footprint
 // and few wavefronts (4) let several workgroups share a CU, so one
 // workgroup's staging overlaps the others' streaming.
@@ -84,12 +85,14 @@ __host__ __device__ inline size_t moe_routed_lds_bytes(int K, int group, int sgm
             (size_t)waves * nm * 16 * (sgmax + 1)) * 4;
 }
 
-template <int S, bool GU, int DEPTH, int SGMAX>
+template <int S, bool GU, int DEPTH, int SGMAX, int RT = 1>
 __global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
     using T = Traits<S>;
     using P = MfmaStep<S>;
     constexpr int GPS = P::GPS;
-    constexpr int NM = GU ? 2 : 1;
+    // matrices streamed per wavefront: gate and up, or RT row tiles of down
+    constexpr int NM = GU ? 2 : RT;
+    static_assert(!GU || RT == 1, "gate/up streams one row tile of each matrix");
     constexpr int NV = T::GROUP / 8;  // 16-byte activation vectors per group
     constexpr int U = 4;
     constexpr uint32_t ONE2 = 0x3F803F80u;
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
     const int g = lane >> 4, c16 = lane & 15;
     // workgroup b: the shared expert's (descriptor, row block) pairs first,
     // then the routed ones
-    const int rows = (NT / 64) * 16;  // per workgroup
+    const int rows = (NT / 64) * 16 * RT;  // per workgroup
     const int sdesc = a.S0.codes ? (a.M + kMoeDescPairs - 1) / kMoeDescPairs : 0;
     const int rbs = a.S0.codes ? a.S0.N / rows : 0, rbr = a.W0.codes ? a.W0.N / rows : 0;
     int b = blockIdx.x;
@@ -130,14 +133,14 @@ __global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
     float* xd = reinterpret_cast<float*>(lds + smax * 16 * kRoutedMp * 4);
     uint32_t* sl = lds + smax * 16 * kRoutedMp * 4 + smax * GPS * 16 + wave * NM * 16 * (SGMAX + 1);
 
-    const int row0 = rb * rows + wave * 16;  // N % rows == 0
+    const int row0 = rb * rows + wave * 16 * RT;  // N % rows == 0; tile m at row0 + 16 m
     const uint8_t* crow[NM];
     const uint8_t* scl[NM];
     const uint8_t* bil[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-        const GMat& W = sh ? (m ? a.S1 : a.S0) : (m ? a.W1 : a.W0);
-        crow[m] = W.codes + (int64_t)e * W.stride_c + (int64_t)(row0 + c16) * (K / 2);
+        const GMat& W = sh ? (GU && m ? a.S1 : a.S0) : (GU && m ? a.W1 : a.W0);
+        crow[m] = W.codes + (int64_t)e * W.stride_c + (int64_t)(row0 + (GU ? 0 : 16 * m) + c16) * (K / 2);
         scl[m] = W.scale + (int64_t)e * W.stride_s;
         bil[m] = T::AFFINE ? W.bias + (int64_t)e * W.stride_s : nullptr;
     }
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
             const int gl = min(lane + 64 * hh, groups - 1);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const uint32_t ei = (uint32_t)(row0 + r) * (uint32_t)groups + (uint32_t)gl;
+                const uint32_t ei = (uint32_t)(row0 + (GU ? 0 : 16 * m) + r) * (uint32_t)groups + (uint32_t)gl;
                 if constexpr (T::AFFINE)
                     sv[m][hh][r] = (uint32_t)gmem<uint16_t>(scl[m])[ei] | ((uint32_t)gmem<uint16_t>(bil[m])[ei] << 16);
                 else
@@ -301,10 +304,12 @@ __global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
         const int slot = 4 * g + r;
         if (slot < cnt) {
             const int64_t pr = sh ? first + slot : a.pairs[first + slot];
-            if constexpr (GU)
+            if constexpr (GU) {
                 (sh ? a.hs : a.h)[pr * N + n] = (uint16_t)f32_to_bf16_rne(gelu_tanh(acc[0][r]) * acc[1][r]);
-            else
-                (sh ? a.sout : a.part)[pr * N + n] = acc[0][r];
+            } else {
+#pragma unroll
+                for (int m = 0; m < NM; ++m) (sh ? a.sout : a.part)[pr * N + n + 16 * m] = acc[m][r];
+            }
         }
     }
 }
