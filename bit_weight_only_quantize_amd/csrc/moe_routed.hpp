@@ -185,24 +185,26 @@ __global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
     // 1. the first activation loads first (their waits then cover L2 only)
     stage_load(gi0);
     __builtin_amdgcn_sched_barrier(0);
-    // 2. the tile's scales (affine: bf16 scale low, bias high) for the
-    //    wavefront's LDS blocks, lanes over a row's groups
-    constexpr int SR = (SGMAX + 63) / 64;
-    uint32_t sv[NM][SR][16];
+    // 2. the tiles' scales: a tile's 16 rows are consecutive in the scale
+    //    (and bias) arrays, so 16-byte vectors over the lanes cover them in
+    //    SV loads per array (16 * groups elements, a multiple of a vector);
+    //    step 4 spreads them into the wavefront's LDS blocks
+    constexpr int EB = T::AFFINE ? 2 : 4;  // bytes per element
+    constexpr int EPV = 16 / EB;           // elements per vector
+    constexpr int SV = (16 * SGMAX / EPV + 63) / 64;
+    const int nvec = 16 * groups / EPV;
+    u32x4_t svs[NM][SV];
+    u32x4_t svb[T::AFFINE ? NM : 1][SV];
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int m = 0; m < NM; ++m) {
+        const int64_t e0 = (int64_t)(row0 + (GU ? 0 : 16 * m)) * groups * EB;
 #pragma unroll
-        for (int hh = 0; hh < SR; ++hh) {
-            const int gl = min(lane + 64 * hh, groups - 1);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const uint32_t ei = (uint32_t)(row0 + (GU ? 0 : 16 * m) + r) * (uint32_t)groups + (uint32_t)gl;
-                if constexpr (T::AFFINE)
-                    sv[m][hh][r] = (uint32_t)gmem<uint16_t>(scl[m])[ei] | ((uint32_t)gmem<uint16_t>(bil[m])[ei] << 16);
-                else
-                    sv[m][hh][r] = gmem<uint32_t>(scl[m])[ei];
-            }
+        for (int j = 0; j < SV; ++j) {
+            const int v = min(lane + 64 * j, nvec - 1);
+            svs[m][j] = *gmem<u32x4_t>(scl[m] + e0 + 16 * v);
+            if constexpr (T::AFFINE) svb[m][j] = *gmem<u32x4_t>(bil[m] + e0 + 16 * v);
         }
+    }
     __builtin_amdgcn_sched_barrier(0);
     // 3. the first DEPTH - 1 steps' codes, in the loop's order
     struct Buf {
@@ -225,13 +227,33 @@ __global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
         stage_load(gb);
         stage_store(gb);
     }
+    // element idx of a tile's block is row idx / groups, group idx % groups
+    // (the quotient from a float product: exact, as idx < 16 * 128 and the
+    // fraction stays at least 1/(2 groups) away from an integer); lanes past
+    // the block store into the padding column (unconditional stores keep the
+    // load waits exact). Affine words: bf16 scale low, bias high.
+    const float rg = 1.0f / (float)groups;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int hh = 0; hh < SR; ++hh)
+        for (int j = 0; j < SV; ++j) {
+            const int v = lane + 64 * j;
+            const bool ok = v < nvec;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                sl[(m * 16 + r) * (SGMAX + 1) + min(lane + 64 * hh, SGMAX)] = sv[m][hh][r];
+            for (int q = 0; q < EPV; ++q) {
+                const int idx = v * EPV + q;
+                const int r = (int)(((float)idx + 0.5f) * rg);
+                const int gi = idx - r * groups;
+                uint32_t w;
+                if constexpr (T::AFFINE) {
+                    const uint32_t s2 = svs[m][j][q / 2], b2 = svb[m][j][q / 2];
+                    w = (q & 1) ? ((s2 >> 16) | (b2 & 0xFFFF0000u)) : ((s2 & 0xFFFFu) | (b2 << 16));
+                } else {
+                    w = svs[m][j][q];
+                }
+                sl[(m * 16 + (ok ? r : 15)) * (SGMAX + 1) + (ok ? gi : SGMAX)] = w;
+            }
+        }
     __syncthreads();
 
     // 5. the tile's steps
