@@ -194,13 +194,17 @@ def decode_stack(c: Ctx, shapes, scheme, layers, M, head=None):
     xs = {K: v[1] for K, v in xh.items()}
     ys = {nm: c.torch.empty((M, N), dtype=c.torch.float32, device=c.dev) for nm, N, _ in shapes}
     yh = c.torch.empty((M, head[0]), dtype=c.torch.float32, device=c.dev) if head else None
+    # the down projection's activations outgrow one CU's LDS at M = 16 (7B) and
+    # M = 8 (13B): those launches split K across CUs through a workspace
+    need = w4.gemv_workspace_bytes(mats[0]["down"], M)
+    ws = c.torch.empty(need, dtype=c.torch.uint8, device=c.dev) if need else None
 
     def step():
         for m in mats:
             w4.gemv_multi_into([m["wq"], m["wk"], m["wv"]], xs[d], [ys["wq"], ys["wk"], ys["wv"]])
             w4.gemv_into(m["wo"], xs[d], ys["wo"])
             w4.gemv_multi_into([m["gate"], m["up"]], xs[d], [ys["gate"], ys["up"]])
-            w4.gemv_into(m["down"], xs[f], ys["down"])
+            w4.gemv_ws_into(m["down"], xs[f], ys["down"], ws)
         if hq is not None:
             w4.gemv_into(hq, xs[d], yh)
 
@@ -267,7 +271,8 @@ def run_llama(c: Ctx, a, big: bool):
     out = base_line(a, METRIC, round(tbs, 4), "TB/s", ms, {
         "workload": name, "layers": layers, "M": M, "scheme": scheme,
         "matrices": ", ".join(f"{nm} {N}x{K}" for nm, N, K in shapes) + (f", head {head[0]}x{head[1]}" if head else ""),
-        "launches_per_layer": "qkv (one launch), o, gate+up (one launch), down",
+        "launches_per_layer": "qkv (one launch), o, gate+up (one launch), down" + (
+            " (K parts on separate CUs, then a summing launch)" if c.w4.gemv_workspace_bytes(mats[0]["down"], M) else ""),
         "weights": "seeded N(0,0.02) drawn on device", "activations": "bf16 N(0,1)"})
     out["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
     out["tok_per_s"] = round(M / (ms * 1e-3), 1)

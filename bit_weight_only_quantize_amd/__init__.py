@@ -55,6 +55,8 @@ _SIGS = {
     "w4_quantize_pack": ([ctypes.c_int, _P, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "w4a16_gemv": ([ctypes.POINTER(_W4Matrix), _P, _I64, _P, _P], ctypes.c_int),
     "w4a16_gemm": ([ctypes.POINTER(_W4Matrix), _P, _I64, _P, _P], ctypes.c_int),
+    "w4_gemv_workspace_bytes": ([ctypes.POINTER(_W4Matrix), _I64], ctypes.c_size_t),
+    "w4a16_gemv_ws": ([ctypes.POINTER(_W4Matrix), _P, _I64, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "w4a16_gemv_multi": ([ctypes.POINTER(ctypes.POINTER(_W4Matrix)), ctypes.c_int, _P, _I64,
                           ctypes.POINTER(ctypes.c_void_p), _P], ctypes.c_int),
     "w4_moe_route": ([ctypes.POINTER(_W4Matrix), _P, _I64, ctypes.c_int, _P, _P, _P, _P], ctypes.c_int),
@@ -184,6 +186,23 @@ def gemv_into(W: QuantizedMatrix, x: torch.Tensor, y: torch.Tensor) -> torch.Ten
     M = x.shape[0] if x.dim() == 2 else 1
     d = W.desc()
     _check(lib().w4a16_gemv(ctypes.byref(d), _ptr(x), M, _ptr(y), _stream(x.device)))
+    return y
+
+
+def gemv_workspace_bytes(W: QuantizedMatrix, M: int) -> int:
+    """Workspace bytes with which gemv_ws_into splits K across CUs (0: no split)."""
+    d = W.desc()
+    return int(lib().w4_gemv_workspace_bytes(ctypes.byref(d), M))
+
+
+def gemv_ws_into(W: QuantizedMatrix, x: torch.Tensor, y: torch.Tensor,
+                 workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    """gemv_into with a device workspace (>= gemv_workspace_bytes(W, M) bytes, or None when 0)."""
+    x = _as_bf16_bits(x, "x")
+    M = x.shape[0] if x.dim() == 2 else 1
+    d = W.desc()
+    wp, wb = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+    _check(lib().w4a16_gemv_ws(ctypes.byref(d), _ptr(x), M, _ptr(y), wp, wb, _stream(x.device)))
     return y
 
 

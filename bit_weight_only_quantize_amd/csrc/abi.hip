@@ -109,6 +109,43 @@ int w4a16_gemv(const w4_matrix* W, const uint16_t* x, int64_t M, float* y, void*
                       "gemv launch");
 }
 
+size_t w4_gemv_workspace_bytes(const w4_matrix* W, int64_t M) {
+    if (!W || W->num_experts != 1 || W->N <= 0 || W->K <= 0 || M < 2 || M > 16) return 0;
+    if (W->scheme != W4_SYM4_G128 && W->scheme != W4_AFF4_G64) return 0;
+    const int64_t group = W->scheme == W4_SYM4_G128 ? 128 : 64;
+    if (W->K % group || W->K > w4::kMaxSkinnyK) return 0;
+    return w4::gemv_mfma_split_bytes(W->scheme, W->N, W->K, M);
+}
+
+int w4a16_gemv_ws(const w4_matrix* W, const uint16_t* x, int64_t M, float* y, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    int rc = check_matrix(W, "W", 1);
+    if (rc) return rc;
+    if (M < 0 || M > 64) return fail(W4_ESHAPE, "M=%lld out of range [0, 64]", (long long)M);
+    if (M == 0 || W->N == 0) return ok();
+    if (W->K > w4::kMaxSkinnyK)
+        return fail(W4_ESHAPE, "K=%lld exceeds the GEMV limit %lld", (long long)W->K,
+                    (long long)w4::kMaxSkinnyK);
+    if (!x || !y) return fail(W4_EINVAL, "null x or y");
+    if (!aligned16(x) || !aligned16(y)) return fail(W4_EALIGN, "x and y must be 16-byte aligned");
+    const size_t need = w4_gemv_workspace_bytes(W, M);
+    if (need == 0)
+        return hip_status(w4::launch_gemv(W->scheme, W->codes, W->scale, W->bias, W->N, W->K, x, M,
+                                          y, (hipStream_t)stream),
+                          "gemv launch");
+    if (!workspace || workspace_bytes < need)
+        return fail(W4_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(W4_EALIGN, "workspace must be 16-byte aligned");
+    const void* c = W->codes;
+    const void* sc = W->scale;
+    const void* b = W->bias;
+    const int64_t N = W->N;
+    return hip_status(w4::launch_gemv_mfma(W->scheme, 1, &c, &sc, &b, &N, W->K, x, M, &y,
+                                           (hipStream_t)stream, (float*)workspace),
+                      "gemv launch");
+}
+
 int w4a16_gemv_multi(const w4_matrix* const* Ws, int count, const uint16_t* x, int64_t M,
                      float* const* ys, void* stream) {
     if (!Ws || !ys) return fail(W4_EINVAL, "null Ws or ys");

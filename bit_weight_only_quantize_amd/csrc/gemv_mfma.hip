@@ -6,6 +6,21 @@
 
 namespace w4 {
 
+// y[i] = sum of the KP partial outputs part[p][i], p = 0 .. KP-1 in order
+// (all loads issued first; KP <= 8)
+__global__ __launch_bounds__(256) void ksplit_sum_kernel(const float* __restrict__ part, int KP,
+                                                         int64_t MN, float* __restrict__ y) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= MN) return;
+    float v[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) v[p] = part[(int64_t)min(p, KP - 1) * MN + i];
+    float s = v[0];
+#pragma unroll
+    for (int p = 1; p < 8; ++p) s = p < KP ? s + v[p] : s;
+    y[i] = s;
+}
+
 bool gemv_mfma_ok(int scheme, int64_t K, int64_t M) {
     if (scheme != SYM4_G128 && scheme != AFF4_G64) return false;
     const int group = scheme == SYM4_G128 ? 128 : 64;
@@ -43,11 +58,89 @@ static void pick_mfma(int RT, int WK, const GemvGroupArgs& a, int blocks, int K,
 // about 24 steps (KB) of code loads in flight per CU read fastest, more read
 // slower (16 wavefronts x 4 steps on one tile: 1.6 TB/s against 2.4 with 4
 // x 4). Launches of more than 16 tiles per CU take the split-K kernel.
+struct LdsPlan {
+    int KP = 1, TP = 0, WK = 1, CS = 0, SG = 16, spw = 0, grid = 0;
+    bool chunked = false;
+    size_t lds = 0;
+};
+
+template <int S>
+static bool plan_mfma_lds(int tiles, int64_t K, int64_t M, bool split, LdsPlan& P) {
+    constexpr int kCUs = 256, kWaves = 16;
+    constexpr size_t kLds = 160 * 1024;
+    if (tiles == 0) return false;
+    const MfmaLdsLayout<S> whole((int)K, (int)M, 1);
+    const int steps = whole.steps, GPS = whole.GPS;
+    // the staging lanes of one group of all tokens must fit the workgroup
+    if (64 * kWaves < whole.mp * (Traits<S>::GROUP / 8)) return false;
+    // a run of CS steps on TP tiles per workgroup: the K-slice split WK puts
+    // about 24 steps of code loads in flight per CU; returns the LDS bytes
+    // (activations, sums and scale blocks), 0 if they do not fit
+    auto fit = [&](LdsPlan& q) -> size_t {
+        const int depth = q.chunked ? 2 : 4;
+        int WK = (24 + q.TP * depth / 2) / (q.TP * depth);
+        WK = std::max(1, std::min({WK, kWaves / q.TP, q.CS}));
+        // every K-slice of a full run non-empty
+        while (WK > 1 && (WK - 1) * ((q.CS + WK - 1) / WK) >= q.CS) --WK;
+        q.WK = WK;
+        q.spw = (q.CS + WK - 1) / WK;
+        const int sgmax = std::min(q.spw * GPS, whole.groups);
+        if (sgmax > (q.chunked ? 64 : 128)) return 0;  // chunked: registers (see below)
+        q.SG = sgmax <= 16 ? 16 : sgmax <= 32 ? 32 : sgmax <= 64 ? 64 : 128;
+        size_t lds = MfmaLdsLayout<S>((int)K, (int)M, q.CS).bytes() + (size_t)q.TP * WK * 16 * (q.SG + 1) * 4;
+        lds = std::max(lds, WK > 1 ? (size_t)q.TP * WK * 64 * 16 : (size_t)0);
+        return lds <= kLds ? lds : 0;
+    };
+    const int TP1 = (tiles + kCUs - 1) / kCUs;
+    if (TP1 > kWaves) return false;
+    LdsPlan q;
+    q.TP = TP1;
+    q.CS = steps;
+    if ((q.lds = fit(q))) {
+        q.grid = (tiles + TP1 - 1) / TP1;
+        P = q;
+        return true;
+    }
+    // x does not fit. With room for partial outputs: K parts on different
+    // CUs, each part's x one chunk; the plan with the fewest code steps per
+    // CU (TP x part steps), the fewest parts on a tie, all in one round of
+    // workgroups
+    if (split) {
+        LdsPlan best;
+        for (int KP = 2; KP <= 8; ++KP) {
+            LdsPlan c;
+            c.KP = KP;
+            c.CS = (steps + KP - 1) / KP;
+            if ((KP - 1) * c.CS >= steps) continue;  // an empty last part
+            c.TP = (tiles + kCUs / KP - 1) / (kCUs / KP);
+            if (c.TP > kWaves) continue;
+            if (!(c.lds = fit(c))) continue;
+            c.grid = KP * ((tiles + c.TP - 1) / c.TP);
+            if (best.KP == 1 || c.TP * c.CS < best.TP * best.CS) best = c;
+        }
+        if (best.KP > 1) {
+            P = best;
+            return true;
+        }
+    }
+    // else the fewest chunks whose activations, sums and scale blocks fit
+    q.chunked = true;
+    for (int chunks = 2; chunks <= steps; ++chunks) {
+        q.CS = (steps + chunks - 1) / chunks;
+        if ((q.lds = fit(q))) {
+            q.grid = (tiles + TP1 - 1) / TP1;
+            P = q;
+            return true;
+        }
+    }
+    return false;
+}
+
 template <int S>
 static bool try_mfma_lds(int count, const void* const* codes, const void* const* scale,
                          const void* const* bias, const int64_t* N, int64_t K,
-                         const uint16_t* x, int64_t M, float* const* y, hipStream_t st) {
-    constexpr int kCUs = 256, kWaves = 16;
+                         const uint16_t* x, int64_t M, float* const* y, float* part,
+                         hipStream_t st) {
     constexpr size_t kLds = 160 * 1024;
     GemvGroupArgs a{};
     int tiles = 0;
@@ -62,39 +155,13 @@ static bool try_mfma_lds(int count, const void* const* codes, const void* const*
     }
     a.tile_start[count] = tiles;
     a.count = count;
-    if (tiles == 0) return false;
-    const int TP = (tiles + kCUs - 1) / kCUs;
-    if (TP > kWaves) return false;
-    const MfmaLdsLayout<S> whole((int)K, (int)M, 1);
-    const int steps = whole.steps, GPS = whole.GPS;
-    // the staging lanes of one group of all tokens must fit the workgroup
-    if (64 * kWaves < whole.mp * (Traits<S>::GROUP / 8)) return false;
-    // fewest chunks whose activations, sums and scale blocks fit in LDS; the
-    // tile split WK puts about 24 steps of code loads in flight per CU
-    int CS = 0, SG = 0, spw = 0, WK = 1;
-    size_t lds = 0;
-    for (int chunks = 1; chunks <= steps; ++chunks) {
-        CS = (steps + chunks - 1) / chunks;
-        const int depth = chunks > 1 ? 2 : 4;
-        WK = (24 + TP * depth / 2) / (TP * depth);
-        WK = std::max(1, std::min({WK, kWaves / TP, CS}));
-        // every K-slice of a full chunk non-empty
-        while (WK > 1 && (WK - 1) * ((CS + WK - 1) / WK) >= CS) --WK;
-        spw = (CS + WK - 1) / WK;
-        const int sgmax = std::min(spw * GPS, whole.groups);
-        if (sgmax > (chunks > 1 ? 64 : 128)) continue;  // chunked: registers (see below)
-        SG = sgmax <= 16 ? 16 : sgmax <= 32 ? 32 : sgmax <= 64 ? 64 : 128;
-        lds = MfmaLdsLayout<S>((int)K, (int)M, CS).bytes() + (size_t)TP * WK * 16 * (SG + 1) * 4;
-        lds = std::max(lds, WK > 1 ? (size_t)TP * WK * 64 * 16 : (size_t)0);
-        if (lds <= kLds) break;
-        lds = 0;
-    }
-    if (lds == 0) return false;
-    const int grid = (tiles + TP - 1) / TP;
+    LdsPlan P;
+    if (!plan_mfma_lds<S>(tiles, K, M, part != nullptr && count == 1, P)) return false;
     auto go = [&](auto kern) {
-        if (lds > 64 * 1024)
+        if (P.lds > 64 * 1024)
             (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWaves), lds, st, a, (int)K, (int)M, x, tiles, TP, WK, CS);
+        hipLaunchKernelGGL(kern, dim3(P.grid), dim3(1024), P.lds, st, a, (int)K, (int)M, x, tiles,
+                           P.TP, P.WK, P.CS, P.KP, part);
     };
     // four steps in flight (eight read slower, see above); slices under four
     // steps take two. The chunk loop costs the registers of two more steps in
@@ -102,27 +169,46 @@ static bool try_mfma_lds(int count, const void* const* codes, const void* const*
     auto by_depth = [&](auto sgc) {
         constexpr int G = decltype(sgc)::value;
         if constexpr (G <= 64) {
-            if (CS < steps) {
+            if (P.chunked) {
                 go(gemv_mfma_lds_kernel<S, 2, G, true>);
                 return;
             }
         }
-        if (spw >= 4) go(gemv_mfma_lds_kernel<S, 4, G, false>);
-        else go(gemv_mfma_lds_kernel<S, 2, G, false>);
+        if (P.KP > 1) {
+            if (P.spw >= 4) go(gemv_mfma_lds_kernel<S, 4, G, false, true>);
+            else go(gemv_mfma_lds_kernel<S, 2, G, false, true>);
+        } else {
+            if (P.spw >= 4) go(gemv_mfma_lds_kernel<S, 4, G, false>);
+            else go(gemv_mfma_lds_kernel<S, 2, G, false>);
+        }
     };
-    if (SG == 16) by_depth(std::integral_constant<int, 16>{});
-    else if (SG == 32) by_depth(std::integral_constant<int, 32>{});
-    else if (SG == 64) by_depth(std::integral_constant<int, 64>{});
+    if (P.SG == 16) by_depth(std::integral_constant<int, 16>{});
+    else if (P.SG == 32) by_depth(std::integral_constant<int, 32>{});
+    else if (P.SG == 64) by_depth(std::integral_constant<int, 64>{});
     else by_depth(std::integral_constant<int, 128>{});
+    if (P.KP > 1) {
+        const int64_t MN = M * N[0];
+        hipLaunchKernelGGL(ksplit_sum_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, st,
+                           (const float*)part, P.KP, MN, y[0]);
+    }
     return true;
+}
+
+size_t gemv_mfma_split_bytes(int scheme, int64_t N, int64_t K, int64_t M) {
+    if (!gemv_mfma_ok(scheme, K, M) || N <= 0) return 0;
+    const int tiles = (int)((N + 15) / 16);
+    LdsPlan P;
+    const bool ok = scheme == SYM4_G128 ? plan_mfma_lds<SYM4_G128>(tiles, K, M, true, P)
+                                        : plan_mfma_lds<AFF4_G64>(tiles, K, M, true, P);
+    return ok && P.KP > 1 ? (size_t)P.KP * (size_t)(M * N) * sizeof(float) : 0;
 }
 
 hipError_t launch_gemv_mfma(int scheme, int count, const void* const* codes,
                             const void* const* scale, const void* const* bias, const int64_t* N,
                             int64_t K, const uint16_t* x, int64_t M, float* const* y,
-                            hipStream_t st) {
-    if (scheme == SYM4_G128 ? try_mfma_lds<SYM4_G128>(count, codes, scale, bias, N, K, x, M, y, st)
-                            : try_mfma_lds<AFF4_G64>(count, codes, scale, bias, N, K, x, M, y, st))
+                            hipStream_t st, float* part) {
+    if (scheme == SYM4_G128 ? try_mfma_lds<SYM4_G128>(count, codes, scale, bias, N, K, x, M, y, part, st)
+                            : try_mfma_lds<AFF4_G64>(count, codes, scale, bias, N, K, x, M, y, part, st))
         return hipGetLastError();
     int64_t total_rows = 0;
     for (int i = 0; i < count; ++i) total_rows += N[i];

@@ -405,10 +405,16 @@ __device__ __forceinline__ int lds_swz(int mp, int lr) {
 // stage activations. DEPTH steps of code loads in flight per streaming
 // wavefront. SGMAX (at most 128) bounds the groups of a slice: the scale
 // block's row stride. CHUNKED: x goes in several chunks (CS < steps).
-template <int S, int DEPTH, int SGMAX, bool CHUNKED>
+// PARTS (K parts: KP > 1, one matrix, not CHUNKED): the grid is KP runs of
+// gridDim.x / KP workgroups; run p covers steps [p * CS, p * CS + CS) of every
+// tile, as one chunk, and writes its partial outputs to part + p * M * N
+// ([M][N]). A template switch, so that the other launches keep constant
+// chunk offsets.
+template <int S, int DEPTH, int SGMAX, bool CHUNKED, bool PARTS = false>
 __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, int K, int M,
                                                               const uint16_t* x, int tiles,
-                                                              int TP, int WK, int CS) {
+                                                              int TP, int WK, int CS, int KP,
+                                                              float* part) {
     using T = Traits<S>;
     using P = MfmaStep<S>;
     constexpr int GPS = P::GPS;
@@ -431,7 +437,9 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
     // and store nothing); the others only help stage the activations
     const bool comp = wave < TP * WK;
     const int tw = wave % TP, ks = min(wave / TP, WK - 1);
-    const int tile_raw = blockIdx.x * TP + tw;
+    const int gpp = PARTS ? (int)gridDim.x / KP : 0;  // workgroups per K part
+    const int kp = PARTS ? (int)blockIdx.x / gpp : 0;
+    const int tile_raw = ((int)blockIdx.x - kp * gpp) * TP + tw;
     const int tile = min(tile_raw, tiles - 1);
     int i = 0;
 #pragma unroll
@@ -472,17 +480,19 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
     };
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    // one pass when x fits (CHUNKED false: no loop for the compiler to hoist
-    // lane constants out of, which would cost registers the ring needs)
-    const int c_end = CHUNKED ? steps : 1;
-    for (int c0 = 0; c0 < c_end; c0 += CHUNKED ? CS : 1) {
+    // one pass when x (or the K part's x) fits (CHUNKED false: no loop for
+    // the compiler to hoist lane constants out of, which would cost registers
+    // the ring needs)
+    const int cbeg = kp * CS;
+    const int c_end = CHUNKED ? steps : cbeg + 1;
+    for (int c0 = cbeg; c0 < c_end; c0 += CHUNKED ? CS : 1) {
         const int cn = min(CS, steps - c0);                        // chunk steps
         const int cg0 = c0 * GPS, cgn = min(groups, (c0 + cn) * GPS) - cg0;  // chunk groups
         const int spw = (cn + WK - 1) / WK;
         const int lb = ks * spw;                   // slice start (chunk step)
         const int ns = min(cn, lb + spw) - lb;     // slice steps, <= 0 if empty
         const int lbl = min(lb, cn - 1), nsl = max(ns, 1);  // addresses of an empty slice
-        if (c0 > 0) __syncthreads();               // the previous chunk's LDS reads are done
+        if (c0 > cbeg) __syncthreads();            // the previous chunk's LDS reads are done
 
         u32x4_t xr[U];
         auto stage_load = [&](int gb) {
@@ -664,7 +674,7 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
         }
     }
     if (tile_raw >= tiles) return;
-    float* y = a.y[i];
+    float* y = PARTS ? part + (int64_t)kp * M * N : a.y[i];
     const int nn = row0 + c16;
     if (nn < N) {
 #pragma unroll

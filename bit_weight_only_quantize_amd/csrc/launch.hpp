@@ -28,10 +28,15 @@ hipError_t launch_gemv_wave(int scheme, int count, const void* const* codes,
 
 // 2 <= M <= 16, 4-bit schemes: unpacked codes feed bf16 MFMA from registers.
 bool gemv_mfma_ok(int scheme, int64_t K, int64_t M);
+// part: room for K-part partial outputs (gemv_mfma_split_bytes of them) or
+// null; with it, a single matrix whose activations do not fit LDS takes K
+// parts on different CUs and a summing launch instead of chunks
 hipError_t launch_gemv_mfma(int scheme, int count, const void* const* codes,
                             const void* const* scale, const void* const* bias, const int64_t* N,
                             int64_t K, const uint16_t* x, int64_t M, float* const* y,
-                            hipStream_t st);
+                            hipStream_t st, float* part = nullptr);
+// bytes of partial outputs the K-part plan needs (0: no K parts for this shape)
+size_t gemv_mfma_split_bytes(int scheme, int64_t N, int64_t K, int64_t M);
 
 // 2 <= M <= 64, same design with token tiles staged in LDS.
 bool gemv_wave_mt_ok(int scheme, int64_t K, int64_t M);

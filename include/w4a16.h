@@ -121,6 +121,31 @@ int w4a16_gemv_multi(const w4_matrix* const* Ws, int count, const uint16_t* x, i
                      float* const* ys, void* stream);
 
 /*
+ * Host-only. Bytes of device workspace with which w4a16_gemv_ws splits the
+ * reduction over K of W (one matrix) across CUs for M tokens; 0 when it does
+ * not (then w4a16_gemv_ws runs w4a16_gemv's path and needs no workspace). A
+ * split applies to the 4-bit schemes at 2 <= M <= 16 when the activations
+ * (M * K bf16) do not fit one CU's LDS, e.g. K = 11008 at M = 16 or
+ * K = 13824 at M = 8. Invalid arguments give 0.
+ */
+size_t w4_gemv_workspace_bytes(const w4_matrix* W, int64_t M);
+
+/*
+ * w4a16_gemv (same operation, arguments and limits) with a caller-provided
+ * workspace: device memory of at least w4_gemv_workspace_bytes(W, M) bytes
+ * (W4_EWORKSPACE otherwise; may be NULL when that is 0); its contents on entry
+ * do not matter and on return are unspecified. Decode is memory-bound
+ * ([airllm] §3.3): where x does not fit a CU's LDS, w4a16_gemv stages it in
+ * chunks that each drain the weight stream, while here K is cut into parts
+ * whose activations each fit, every part's tiles stream on their own CUs into
+ * partial outputs in the workspace, and a second launch adds the parts in a
+ * fixed order. Deterministic; the sums are ordered differently from
+ * w4a16_gemv's, so the two agree to the error bound, not bit for bit.
+ */
+int w4a16_gemv_ws(const w4_matrix* W, const uint16_t* x, int64_t M, float* y, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
  * Prefill GEMM ([airllm] §3.3: prefill is compute-dense): Y = X * dequant(W)^T with
  * bf16 inputs, fp32 accumulation and bf16 output (round to nearest even).
  * X: bf16 [M][K]; Y: bf16 [M][N]; any M >= 0. W: single matrix, 4-bit scheme.

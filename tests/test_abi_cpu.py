@@ -67,6 +67,37 @@ def test_gemv_argument_validation_without_a_device():
     assert L.w4a16_gemv(ctypes.byref(_desc(E=2)), 16, 1, 16, None) == -2
 
 
+def test_gemv_workspace_bytes_on_the_host():
+    L = w4.lib()
+
+    def need(scheme, N, K, M):
+        return L.w4_gemv_workspace_bytes(ctypes.byref(_desc(scheme=scheme, N=N, K=K)), M)
+
+    # activations that fit one CU's LDS, one token, 8-bit codes, > 16 tokens: no K parts
+    assert need(0, 4096, 4096, 16) == 0 and need(0, 4096, 11008, 4) == 0
+    assert need(0, 4096, 11008, 1) == 0 and need(2, 4096, 11008, 16) == 0
+    assert need(0, 4096, 11008, 17) == 0 and need(1, 5120, 5120, 8) == 0
+    assert L.w4_gemv_workspace_bytes(None, 16) == 0
+    # the 7B and 13B down projections at M = 16 / 8: K parts, partial outputs [parts][M][N] fp32
+    for scheme, N, K, M in ((0, 4096, 11008, 16), (1, 5120, 13824, 8), (0, 40, 28672, 16)):
+        b = need(scheme, N, K, M)
+        assert b % (M * N * 4) == 0 and 2 <= b // (M * N * 4) <= 8, (scheme, N, K, M, b)
+
+
+def test_gemv_ws_argument_validation_without_a_device():
+    L = w4.lib()
+    d = _desc(scheme=0, N=4096, K=11008)
+    need = L.w4_gemv_workspace_bytes(ctypes.byref(d), 16)
+    assert need > 0
+    assert L.w4a16_gemv_ws(ctypes.byref(d), 16, 0, 16, None, 0, None) == 0        # M == 0: no-op
+    assert L.w4a16_gemv_ws(ctypes.byref(d), 16, 16, 16, None, 0, None) == -5      # no workspace
+    assert L.w4a16_gemv_ws(ctypes.byref(d), 16, 16, 16, 16, need - 16, None) == -5  # too small
+    assert b"workspace" in L.w4_last_error()
+    assert L.w4a16_gemv_ws(ctypes.byref(d), 16, 16, 16, 8, need, None) == -3      # misaligned
+    assert L.w4a16_gemv_ws(ctypes.byref(d), 16, 65, 16, 16, need, None) == -2
+    assert L.w4a16_gemv_ws(ctypes.byref(_desc(E=2)), 16, 16, 16, 16, need, None) == -2
+
+
 def test_quantize_argument_validation_without_a_device():
     L = w4.lib()
     assert L.w4_quantize_pack(0, 16, 0, 128, 16, 16, None, None) == 0   # N == 0: no-op

@@ -58,6 +58,48 @@ def test_gemv_matches_oracle(scheme, N, K, M):
     _run(scheme, N, K, M, f"small.{scheme}.{N}x{K}")
 
 
+@pytest.mark.parametrize("scheme,N,K,M", [
+    ("sym4_g128", 300, 11008, 16),    # K in parts, ragged rows
+    ("aff4_g64", 600, 13888, 8),      # odd group count: the last part ends in a half step
+    ("aff4_g64", 200, 13824, 16),
+    ("sym4_g128", 40, 28672, 16),     # the most parts (8)
+    ("sym4_g128", 4096, 11008, 16),   # the 7B down projection as the decode stack runs it
+    ("aff4_g64", 5120, 13824, 8),     # the 13B down projection
+])
+def test_gemv_ws_k_parts_match_oracle(scheme, N, K, M):
+    name = f"ws.{scheme}.{N}x{K}"
+    print(f"[gemv_ws] {name} M={M}", flush=True)
+    W = synth.weights(N, K, 0.02, seed=0, name=name)
+    x = synth.activations_bf16(M, K, seed=0, name=name + ".x")
+    c, s, b = oracle.quantize_pack(W, scheme)
+    q = upload(c, s, b, scheme)
+    need = w4.gemv_workspace_bytes(q, M)
+    assert need > 0 and need % (M * N * 4) == 0 and 2 <= need // (M * N * 4) <= 8
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN bits: contents do not matter
+    xd = dev_bf16(x)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    w4.gemv_ws_into(q, xd, y, ws)
+    yr, S = oracle.gemv_reference(c, s, b, scheme, x)
+    r = tolerance_ratio(y.cpu().numpy(), yr, S)
+    assert r <= 1.0, f"worst error is {r:.3f} x tolerance"
+    y2 = torch.empty_like(y)
+    w4.gemv_ws_into(q, xd, y2, ws)
+    assert torch.equal(y, y2)                       # deterministic
+    with pytest.raises(w4.W4Error) as e:
+        w4.gemv_ws_into(q, xd, y2, ws[: need - 16])
+    assert e.value.code == -5
+
+
+def test_gemv_ws_without_k_parts_is_gemv():
+    W = synth.weights(4096, 4096, 0.02, seed=0, name="ws.none")
+    x = dev_bf16(synth.activations_bf16(4, 4096, seed=0, name="ws.none.x"))
+    q = w4.quantize_pack(dev_f32(W), "sym4_g128")
+    assert w4.gemv_workspace_bytes(q, 4) == 0
+    y = torch.empty((4, 4096), dtype=torch.float32, device="cuda")
+    w4.gemv_ws_into(q, x, y, None)
+    assert torch.equal(y, w4.gemv(q, x))
+
+
 @pytest.mark.parametrize("M", [1, 4, 16])
 @pytest.mark.parametrize("N,K,mat", [(4096, 4096, "wq"), (11008, 4096, "gate"), (4096, 11008, "down")])
 def test_gemv_llama7b_shapes(N, K, mat, M):
