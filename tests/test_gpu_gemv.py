@@ -63,6 +63,7 @@ def test_gemv_matches_oracle(scheme, N, K, M):
     ("aff4_g64", 600, 13888, 8),      # odd group count: the last part ends in a half step
     ("aff4_g64", 200, 13824, 16),
     ("sym4_g128", 40, 28672, 16),     # the most parts (8)
+    ("sym4_g128", 77, 11008, 9),      # ragged token tile (9 of 16), ragged rows
     ("sym4_g128", 4096, 11008, 16),   # the 7B down projection as the decode stack runs it
     ("aff4_g64", 5120, 13824, 8),     # the 13B down projection
 ])
