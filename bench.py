@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--workload", default="llama7b",
                     choices=["llama7b", "moe26b", "prefill", "llama13b", "gemv1024"])
     ap.add_argument("--M", type=int, default=None, help="decode tokens per step")
+    ap.add_argument("--scheme", default=None, choices=["sym4_g128", "aff4_g64", "aff8_g64"],
+                    help="weight scheme of the llama7b/llama13b stacks (default: sym4_g128 / aff4_g64)")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU oracle time budget")
@@ -250,6 +252,7 @@ def cpu_baseline(layer, xs_host, M, budget_s, shapes, scheme, layers):
 
 def run_llama(c: Ctx, a, big: bool):
     shapes, scheme = (LLAMA13B, "aff4_g64") if big else (LLAMA7B, "sym4_g128")
+    scheme = a.scheme or scheme
     layers = a.layers or (40 if big else 32)
     M = a.M or 1
     head = (152064, 5120) if big else None
@@ -278,7 +281,7 @@ def run_llama(c: Ctx, a, big: bool):
     out["tok_per_s"] = round(M / (ms * 1e-3), 1)
     out["step_bytes"] = step_bytes
     traffic = None
-    if not big and M == 1 and layers == 32:
+    if not big and M == 1 and layers == 32 and scheme == "sym4_g128":
         traffic = measured_traffic("gemv_wave_gate_up_llama7b_counters.md", GEMV_WAVE_SOURCES)
     out["roofline"] = hbm_roofline(f"gemv_wave_kernel (gate+up, 2 x {f}x{d} {scheme}, one launch)",
                                    dom_bytes, us_dom, traffic)

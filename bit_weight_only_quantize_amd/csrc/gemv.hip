@@ -175,18 +175,22 @@ static hipError_t pick_mt(const GemvPlan& p, const void* c, const void* s, const
 
 // ---------------------------------------------------------------- M = 1, wave per row
 // Instantiated code-vector counts per lane (ceil(VR / 64) rounded up to one of these).
-static int wave_nv(int64_t VR) {
+// 16-byte code vectors per lane for rows of VR vectors; 0 if too many. The
+// one-token kernel also takes 11 and 14 per lane (rows of up to 896 vectors:
+// the 8-bit scheme at K = 11008 or 13824, the 4-bit ones up to K = 28672),
+// the multi-token kernel, which keeps more per lane, at most 8.
+static int wave_nv(int64_t VR, bool one_token = false) {
     const int64_t need = (VR + 63) / 64;
-    const int nvs[] = {1, 2, 3, 4, 6, 7, 8};
+    const int nvs[] = {1, 2, 3, 4, 6, 7, 8, 11, 14};
     for (int nv : nvs)
-        if (nv >= need) return nv;
+        if (nv >= need && (nv <= 8 || one_token)) return nv;
     return 0;
 }
 
 bool gemv_wave_ok(int scheme, int64_t K) {
     const int kv = scheme == AFF8_G64 ? 16 : 32;
     const int64_t VR = K / kv;
-    return VR >= 64 && wave_nv(VR) > 0;
+    return VR >= 64 && wave_nv(VR, true) > 0;
 }
 
 // Row wavefronts stage the activations themselves (no staging wavefronts): a
@@ -210,7 +214,13 @@ static void pick_nv(int nv, const GemvGroupArgs& a, int blocks, int K, const uin
         case 4: go_wave<S, 4, R, RW>(a, blocks, K, x, lds, st); break;
         case 6: go_wave<S, 6, R, RW>(a, blocks, K, x, lds, st); break;
         case 7: go_wave<S, 7, R, RW>(a, blocks, K, x, lds, st); break;
-        default: go_wave<S, 8, R, RW>(a, blocks, K, x, lds, st); break;
+        case 8: go_wave<S, 8, R, RW>(a, blocks, K, x, lds, st); break;
+        default:  // 11 or 14: one row per wavefront only (two take nv <= 4)
+            if constexpr (R == 1) {
+                if (nv == 11) go_wave<S, 11, R, RW>(a, blocks, K, x, lds, st);
+                else go_wave<S, 14, R, RW>(a, blocks, K, x, lds, st);
+            }
+            break;
     }
 }
 
@@ -228,7 +238,7 @@ hipError_t launch_gemv_wave(int scheme, int count, const void* const* codes,
                             int64_t K, const uint16_t* x, float* const* y, hipStream_t st) {
     const int kv = scheme == AFF8_G64 ? 16 : 32;
     const int64_t VR = K / kv;
-    const int nv = wave_nv(VR);
+    const int nv = wave_nv(VR, true);
     int64_t total_rows = 0;
     for (int i = 0; i < count; ++i) total_rows += N[i];
     // Measured on the decode shapes: two rows per wavefront pay off once a

@@ -53,6 +53,9 @@ def _run(scheme, N, K, M, name, rows=None, quantize_on_gpu=True):
     ("aff4_g64", 600, 13888, 8),      # activations staged in chunks; odd group count
     ("aff8_g64", 128, 2048, 32),      # router shape, several tokens: token tiles split over workgroups
     ("sym4_g128", 40, 4096, 37),      # > 16 tokens (VALU multi-token path), ragged token split
+    ("aff8_g64", 96, 13824, 1),       # one token, long rows: 14 code vectors per lane
+    ("aff4_g64", 50, 20480, 1),       # 11 per lane, ragged last vector column
+    ("sym4_g128", 70, 28672, 1),      # the longest rows (14 per lane)
 ])
 def test_gemv_matches_oracle(scheme, N, K, M):
     _run(scheme, N, K, M, f"small.{scheme}.{N}x{K}")
@@ -105,6 +108,13 @@ def test_gemv_ws_without_k_parts_is_gemv():
 @pytest.mark.parametrize("N,K,mat", [(4096, 4096, "wq"), (11008, 4096, "gate"), (4096, 11008, "down")])
 def test_gemv_llama7b_shapes(N, K, mat, M):
     _run("sym4_g128", N, K, M, f"llama7b.{mat}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("N,K,mat", [(4096, 4096, "wq"), (11008, 4096, "gate"), (4096, 11008, "down")])
+def test_gemv_w8a16_llama7b_shapes(N, K, mat, M):
+    """Whole layers in the router's 8-bit affine g64 scheme (W8A16)."""
+    _run("aff8_g64", N, K, M, f"w8.llama7b.{mat}")
 
 
 @pytest.mark.parametrize("M", [1, 8])
