@@ -111,7 +111,6 @@ int w4a16_gemv(const w4_matrix* W, const uint16_t* x, int64_t M, float* y, void*
 
 size_t w4_gemv_workspace_bytes(const w4_matrix* W, int64_t M) {
     if (!W || W->num_experts != 1 || W->N <= 0 || W->K <= 0 || M < 2 || M > 16) return 0;
-    if (W->scheme != W4_SYM4_G128 && W->scheme != W4_AFF4_G64) return 0;
     const int64_t group = W->scheme == W4_SYM4_G128 ? 128 : 64;
     if (W->K % group || W->K > w4::kMaxSkinnyK) return 0;
     return w4::gemv_mfma_split_bytes(W->scheme, W->N, W->K, M);
@@ -143,7 +142,7 @@ int w4a16_gemv_ws(const w4_matrix* W, const uint16_t* x, int64_t M, float* y, vo
     const int64_t N = W->N;
     return hip_status(w4::launch_gemv_mfma(W->scheme, 1, &c, &sc, &b, &N, W->K, x, M, &y,
                                            (hipStream_t)stream, (float*)workspace),
-                      "gemv launch");
+                      "gemv launch");  // need > 0: the K-part plan exists, so it launches
 }
 
 int w4a16_gemv_multi(const w4_matrix* const* Ws, int count, const uint16_t* x, int64_t M,
@@ -187,9 +186,10 @@ int w4a16_gemv_multi(const w4_matrix* const* Ws, int count, const uint16_t* x, i
     if (M == 1 && w4::gemv_wave_ok(scheme, K))
         return hip_status(w4::launch_gemv_wave(scheme, n, c, sc, b, N, K, x, y, st),
                           "gemv_multi launch");
-    if (w4::gemv_mfma_ok(scheme, K, M))
-        return hip_status(w4::launch_gemv_mfma(scheme, n, c, sc, b, N, K, x, M, y, st),
-                          "gemv_multi launch");
+    if (w4::gemv_mfma_ok(scheme, K, M)) {
+        const hipError_t e = w4::launch_gemv_mfma(scheme, n, c, sc, b, N, K, x, M, y, st);
+        if (e != hipErrorNotSupported) return hip_status(e, "gemv_multi launch");
+    }
     if (w4::gemv_wave_mt_ok(scheme, K, M))
         return hip_status(w4::launch_gemv_wave_mt(scheme, n, c, sc, b, N, K, x, M, y, st),
                           "gemv_multi launch");

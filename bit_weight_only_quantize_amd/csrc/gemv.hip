@@ -380,8 +380,10 @@ hipError_t launch_gemv(int scheme, const void* codes, const void* scale, const v
                        hipStream_t st) {
     if (M == 1 && gemv_wave_ok(scheme, K))
         return launch_gemv_wave(scheme, 1, &codes, &scale, &bias, &N, K, x, &y, st);
-    if (gemv_mfma_ok(scheme, K, M))
-        return launch_gemv_mfma(scheme, 1, &codes, &scale, &bias, &N, K, x, M, &y, st);
+    if (gemv_mfma_ok(scheme, K, M)) {
+        const hipError_t e = launch_gemv_mfma(scheme, 1, &codes, &scale, &bias, &N, K, x, M, &y, st);
+        if (e != hipErrorNotSupported) return e;  // else nothing was launched
+    }
     if (gemv_wave_mt_ok(scheme, K, M))
         return launch_gemv_wave_mt(scheme, 1, &codes, &scale, &bias, &N, K, x, M, &y, st);
     const GemvPlan p = plan_gemv(scheme, N, K, M);

@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void ksplit_sum_kernel(const float* __restrict
 }
 
 bool gemv_mfma_ok(int scheme, int64_t K, int64_t M) {
-    if (scheme != SYM4_G128 && scheme != AFF4_G64) return false;
+    if (scheme != SYM4_G128 && scheme != AFF4_G64 && scheme != AFF8_G64) return false;
     const int group = scheme == SYM4_G128 ? 128 : 64;
     return M >= 2 && M <= 16 && K >= group && K / group <= kMfmaMaxGroups;
 }
@@ -198,8 +198,9 @@ size_t gemv_mfma_split_bytes(int scheme, int64_t N, int64_t K, int64_t M) {
     if (!gemv_mfma_ok(scheme, K, M) || N <= 0) return 0;
     const int tiles = (int)((N + 15) / 16);
     LdsPlan P;
-    const bool ok = scheme == SYM4_G128 ? plan_mfma_lds<SYM4_G128>(tiles, K, M, true, P)
-                                        : plan_mfma_lds<AFF4_G64>(tiles, K, M, true, P);
+    const bool ok = scheme == SYM4_G128  ? plan_mfma_lds<SYM4_G128>(tiles, K, M, true, P)
+                    : scheme == AFF4_G64 ? plan_mfma_lds<AFF4_G64>(tiles, K, M, true, P)
+                                         : plan_mfma_lds<AFF8_G64>(tiles, K, M, true, P);
     return ok && P.KP > 1 ? (size_t)P.KP * (size_t)(M * N) * sizeof(float) : 0;
 }
 
@@ -207,6 +208,13 @@ hipError_t launch_gemv_mfma(int scheme, int count, const void* const* codes,
                             const void* const* scale, const void* const* bias, const int64_t* N,
                             int64_t K, const uint16_t* x, int64_t M, float* const* y,
                             hipStream_t st, float* part) {
+    if (scheme == AFF8_G64) {
+        // 8-bit codes: the LDS kernel only (the split-K kernel has no 8-bit
+        // step); NotSupported sends the caller to the VALU paths
+        if (try_mfma_lds<AFF8_G64>(count, codes, scale, bias, N, K, x, M, y, part, st))
+            return hipGetLastError();
+        return hipErrorNotSupported;
+    }
     if (scheme == SYM4_G128 ? try_mfma_lds<SYM4_G128>(count, codes, scale, bias, N, K, x, M, y, part, st)
                             : try_mfma_lds<AFF4_G64>(count, codes, scale, bias, N, K, x, M, y, part, st))
         return hipGetLastError();

@@ -39,7 +39,12 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 template <int S>
 struct MfmaStep {
-    static constexpr int GPS = S == SYM4_G128 ? 1 : 2;  // groups per 128-weight step
+    // A step is 16 bytes of codes per lane: 128 weights of 16 rows for the
+    // 4-bit schemes, 64 for the 8-bit one. Groups per step; activation
+    // pieces (MFMAs) per step: 4, or 2 for 8-bit codes, whose bytes are
+    // converted exactly (two per MFMA operand word pair)
+    static constexpr int GPS = S == AFF4_G64 ? 2 : 1;
+    static constexpr int PPS = S == AFF8_G64 ? 2 : 4;
     // k offset of activation piece d (8 weights, A operand of word d after the
     // regrouping) for lane group g, relative to the step's first k
     __device__ __forceinline__ static int xpiece(int g, int d) {
@@ -375,13 +380,14 @@ __global__ __launch_bounds__(64 * WK) void gemv_mfma_kernel(GemvGroupArgs a, int
 template <int S>
 struct MfmaLdsLayout {
     static constexpr int GPS = MfmaStep<S>::GPS;
+    static constexpr int RPS = 4 * MfmaStep<S>::PPS;  // A rows per step
     int groups, steps, mp, aw, sw;  // whole-K groups and steps; A and sums words of a chunk
     __host__ __device__ MfmaLdsLayout(int K, int M, int CS) {
         groups = K / Traits<S>::GROUP;
         steps = (groups + GPS - 1) / GPS;
         mp = 2;
         while (mp < M) mp *= 2;
-        aw = CS * 16 * mp * 4;
+        aw = CS * RPS * mp * 4;
         sw = CS * GPS * 16;
     }
     // bytes of A and sums for a chunk of CS steps
@@ -427,6 +433,7 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c16 = lane & 15;
     const MfmaLdsLayout<S> Lo(K, M, CS);
+    constexpr int RPS = MfmaLdsLayout<S>::RPS, PPS = P::PPS;
     const int groups = Lo.groups, steps = Lo.steps, mp = Lo.mp;
     const bool odd = GPS == 2 && (groups & 1);
     float* xd = reinterpret_cast<float*>(lds + Lo.aw);
@@ -451,7 +458,7 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
     const uint8_t* scale = a.scale[i];
     const uint8_t* bias = a.bias[i];
     const int n = min(row0 + c16, N - 1);
-    const uint8_t* crow = codes + (int64_t)n * (K / 2);
+    const uint8_t* crow = codes + (int64_t)n * (K * T::BITS / 8);
     const int tm = min(c16, M - 1);  // tokens past M read token M-1; their outputs are dropped
 
     // staging lanes: a lane keeps one token t and one 16-byte vector iv of a
@@ -468,7 +475,7 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
     const uint16_t* xl = x + (int64_t)min(t, M - 1) * K + iv * 8;
     // vector iv of a group is piece d of lane group gg (the inverse of the
     // codes' piece order); for GPS = 2, d also depends on q
-    const int gg = GPS == 1 ? (iv >> 2) : ((iv >> 2) | (((iv >> 1) & 1) << 1));
+    const int gg = S == AFF8_G64 ? (iv >> 1) : GPS == 1 ? (iv >> 2) : ((iv >> 2) | (((iv >> 1) & 1) << 1));
 
     const uint32_t MASK = opaque(0x000F000Fu);
     const uint32_t MAGIC = unpack_magic<S>();
@@ -510,13 +517,15 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
                 const int gi = gb + j * GS;
                 if (live && gi < cgn) {
                     const int st = gi / GPS, q = gi - st * GPS;
-                    const int d = GPS == 1 ? (iv & 3) : (2 * q + (iv & 1));
-                    const u32x4_t o = {__builtin_amdgcn_perm(xr[j][2], xr[j][0], 0x05040100u),
+                    const int d = S == AFF8_G64 ? (iv & 1) : GPS == 1 ? (iv & 3) : (2 * q + (iv & 1));
+                    // 4-bit: the (k, k + 4) pair order of the nibble unpack;
+                    // 8-bit: bytes convert in order, the vector stays as loaded
+                    const u32x4_t o = S == AFF8_G64 ? xr[j] : u32x4_t{__builtin_amdgcn_perm(xr[j][2], xr[j][0], 0x05040100u),
                                        __builtin_amdgcn_perm(xr[j][2], xr[j][0], 0x07060302u),
                                        __builtin_amdgcn_perm(xr[j][3], xr[j][1], 0x05040100u),
                                        __builtin_amdgcn_perm(xr[j][3], xr[j][1], 0x07060302u)};
                     const int lr = d * 4 + gg;
-                    *reinterpret_cast<u32x4_t*>(lds + 4 * ((st * 16 + lr) * mp + (t ^ lds_swz(mp, lr)))) = o;
+                    *reinterpret_cast<u32x4_t*>(lds + 4 * ((st * RPS + lr) * mp + (t ^ lds_swz(mp, lr)))) = o;
                     if (iv == 0) xd[(st * GPS + q) * 16 + t] = sum;
                 }
             }
@@ -598,12 +607,40 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
         auto compute = [&](const Buf& B, int ls) {
             const int sc_ = lb + ls;  // chunk step
             const bool half = odd && c0 + sc_ == steps - 1;
-            bf16x8_t A[4];
+            bf16x8_t A[PPS];
 #pragma unroll
-            for (int d = 0; d < 4; ++d)
+            for (int d = 0; d < PPS; ++d)
                 A[d] = *reinterpret_cast<const bf16x8_t*>(
-                    lds + 4 * ((sc_ * 16 + d * 4 + g) * mp + (tm ^ lds_swz(mp, d * 4 + g))));
+                    lds + 4 * ((sc_ * RPS + d * 4 + g) * mp + (tm ^ lds_swz(mp, d * 4 + g))));
             uint32_t w[4] = {B[0], B[1], B[2], B[3]};
+            if constexpr (S == AFF8_G64) {
+                // one group per step, two MFMAs over the byte codes converted
+                // exactly (v_cvt_f32_ubyte, then a bf16 pair): D = sum x * q,
+                // so w = s q + b adds b times the activation sum
+                f32x4_t D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    uint32_t o[4];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t c = w[2 * d + h];
+#pragma unroll
+                        for (int b = 0; b < 2; ++b) {
+                            const bf16x2_t pr = {(__bf16)(float)((c >> (16 * b)) & 0xFFu),
+                                                 (__bf16)(float)((c >> (16 * b + 8)) & 0xFFu)};
+                            o[2 * h + b] = __builtin_bit_cast(uint32_t, pr);
+                        }
+                    }
+                    D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[d], as_bf16x8(o[0], o[1], o[2], o[3]), D, 0, 0, 0);
+                }
+                const f32x4_t DX = *reinterpret_cast<const f32x4_t*>(xd + sc_ * 16 + 4 * g);
+                const uint32_t swd = sl[c16 * (SGMAX + 1) + min(ls, sg - 1)];
+                const float sc = bf16_bits_to_f32(swd & 0xFFFFu);
+                const float corr = __uint_as_float(swd & 0xFFFF0000u);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = fmaf(corr, DX[r], fmaf(sc, D[r], acc[r]));
+                return;
+            }
             if constexpr (GPS == 2) {
                 // lanes 0-31 hold group A, lanes 32-63 group B: swap the upper
                 // half of words 0/1 with the lower half of words 2/3
@@ -617,7 +654,7 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
                 if (q == 1 && half) continue;
                 f32x4_t D = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int d = 4 / GPS * q; d < 4 / GPS * (q + 1); ++d)
+                for (int d = PPS / GPS * q; d < PPS / GPS * (q + 1); ++d)
                     D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[d], unpack(w[d]), D, 0, 0, 0);
                 const f32x4_t DX = *reinterpret_cast<const f32x4_t*>(xd + (sc_ * GPS + q) * 16 + 4 * g);
                 const uint32_t swd = sl[c16 * (SGMAX + 1) + min(ls * GPS + q, sg - 1)];

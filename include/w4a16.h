@@ -124,7 +124,7 @@ int w4a16_gemv_multi(const w4_matrix* const* Ws, int count, const uint16_t* x, i
  * Host-only. Bytes of device workspace with which w4a16_gemv_ws splits the
  * reduction over K of W (one matrix) across CUs for M tokens; 0 when it does
  * not (then w4a16_gemv_ws runs w4a16_gemv's path and needs no workspace). A
- * split applies to the 4-bit schemes at 2 <= M <= 16 when the activations
+ * split applies at 2 <= M <= 16 when the activations
  * (M * K bf16) do not fit one CU's LDS, e.g. K = 11008 at M = 16 or
  * K = 13824 at M = 8. Invalid arguments give 0.
  */

@@ -73,13 +73,13 @@ def test_gemv_workspace_bytes_on_the_host():
     def need(scheme, N, K, M):
         return L.w4_gemv_workspace_bytes(ctypes.byref(_desc(scheme=scheme, N=N, K=K)), M)
 
-    # activations that fit one CU's LDS, one token, 8-bit codes, > 16 tokens: no K parts
+    # activations that fit one CU's LDS, one token, > 16 tokens: no K parts
     assert need(0, 4096, 4096, 16) == 0 and need(0, 4096, 11008, 4) == 0
-    assert need(0, 4096, 11008, 1) == 0 and need(2, 4096, 11008, 16) == 0
+    assert need(0, 4096, 11008, 1) == 0 and need(2, 4096, 4096, 16) == 0
     assert need(0, 4096, 11008, 17) == 0 and need(1, 5120, 5120, 8) == 0
     assert L.w4_gemv_workspace_bytes(None, 16) == 0
     # the 7B and 13B down projections at M = 16 / 8: K parts, partial outputs [parts][M][N] fp32
-    for scheme, N, K, M in ((0, 4096, 11008, 16), (1, 5120, 13824, 8), (0, 40, 28672, 16)):
+    for scheme, N, K, M in ((0, 4096, 11008, 16), (1, 5120, 13824, 8), (0, 40, 28672, 16), (2, 4096, 11008, 16)):
         b = need(scheme, N, K, M)
         assert b % (M * N * 4) == 0 and 2 <= b // (M * N * 4) <= 8, (scheme, N, K, M, b)
 

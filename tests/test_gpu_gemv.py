@@ -56,6 +56,9 @@ def _run(scheme, N, K, M, name, rows=None, quantize_on_gpu=True):
     ("aff8_g64", 96, 13824, 1),       # one token, long rows: 14 code vectors per lane
     ("aff4_g64", 50, 20480, 1),       # 11 per lane, ragged last vector column
     ("sym4_g128", 70, 28672, 1),      # the longest rows (14 per lane)
+    ("aff8_g64", 333, 4160, 16),      # 8-bit codes on the matrix cores: odd group count, ragged rows
+    ("aff8_g64", 50, 64, 3),          # one group
+    ("aff8_g64", 12370, 512, 4),      # > 256 row tiles
 ])
 def test_gemv_matches_oracle(scheme, N, K, M):
     _run(scheme, N, K, M, f"small.{scheme}.{N}x{K}")
@@ -69,6 +72,7 @@ def test_gemv_matches_oracle(scheme, N, K, M):
     ("sym4_g128", 77, 11008, 9),      # ragged token tile (9 of 16), ragged rows
     ("sym4_g128", 4096, 11008, 16),   # the 7B down projection as the decode stack runs it
     ("aff4_g64", 5120, 13824, 8),     # the 13B down projection
+    ("aff8_g64", 300, 11008, 16),     # 8-bit codes
 ])
 def test_gemv_ws_k_parts_match_oracle(scheme, N, K, M):
     name = f"ws.{scheme}.{N}x{K}"
@@ -133,8 +137,8 @@ def test_gemv_head_sampled_rows():
 def test_gemv_exact_on_dyadic_toy(scheme, ngroups):
     """8 x 64/128 toy with dyadic scales/biases and small-integer activations:
     every partial sum is exactly representable, so the fp32 result is exact.
-    Two tokens take the matrix-core path for the 4-bit schemes; an odd group
-    count covers its half step."""
+    Two tokens take the matrix-core path; an odd group count covers the
+    4-bit affine half step."""
     rng = np.random.default_rng(21)
     g = 128 if scheme == "sym4_g128" else 64
     K, N = ngroups * g, 8
