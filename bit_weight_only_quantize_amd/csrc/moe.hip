@@ -502,9 +502,9 @@ static GMat gmat(const MoeMat& m) { return GMat{m.codes, m.scale, m.bias, m.stri
 // One launch of moe_routed_kernel over the routed descriptors and/or the
 // shared expert's token descriptors, where it applies (rows a multiple of 64,
 // K of 128, at most 128 groups per row): false otherwise.
-template <int S, bool GU, int RT>
+// nw wavefronts per workgroup (gate/up: 4 measured 0.5% over 8)
+template <int S, bool GU, int RT, int nw = 4>
 static bool moe_routed_launch_rt(const MoeArgs& a, bool routed, bool shared, hipStream_t st) {
-    constexpr int nw = 4;  // wavefronts per workgroup: 4 measured 1% over 8, 4% over 16
     constexpr int rows = 16 * nw * RT;
     MoeRoutedArgs r{};
     int kmax = 0, blocks = 0;
@@ -546,10 +546,10 @@ static bool moe_routed_launch_rt(const MoeArgs& a, bool routed, bool shared, hip
     };
     const bool deep = kmax / 128 >= 4;  // four steps in flight, two for shorter rows
     switch (sg) {
-        case 16: deep ? go(moe_routed_kernel<S, GU, 4, 16, RT>) : go(moe_routed_kernel<S, GU, 2, 16, RT>); break;
-        case 32: deep ? go(moe_routed_kernel<S, GU, 4, 32, RT>) : go(moe_routed_kernel<S, GU, 2, 32, RT>); break;
-        case 64: deep ? go(moe_routed_kernel<S, GU, 4, 64, RT>) : go(moe_routed_kernel<S, GU, 2, 64, RT>); break;
-        default: deep ? go(moe_routed_kernel<S, GU, 4, 128, RT>) : go(moe_routed_kernel<S, GU, 2, 128, RT>); break;
+        case 16: deep ? go(moe_routed_kernel<S, GU, 4, 16, RT, nw>) : go(moe_routed_kernel<S, GU, 2, 16, RT, nw>); break;
+        case 32: deep ? go(moe_routed_kernel<S, GU, 4, 32, RT, nw>) : go(moe_routed_kernel<S, GU, 2, 32, RT, nw>); break;
+        case 64: deep ? go(moe_routed_kernel<S, GU, 4, 64, RT, nw>) : go(moe_routed_kernel<S, GU, 2, 64, RT, nw>); break;
+        default: deep ? go(moe_routed_kernel<S, GU, 4, 128, RT, nw>) : go(moe_routed_kernel<S, GU, 2, 128, RT, nw>); break;
     }
     return true;
 }
@@ -559,10 +559,12 @@ static bool moe_routed_launch(const MoeArgs& a, bool routed, bool shared, hipStr
     if constexpr (GU) {
         return moe_routed_launch_rt<S, GU, 1>(a, routed, shared, st);
     } else {
-        // down: two row tiles per wavefront (the Gemma-shaped layer at M = 32:
-        // 10.5k -> 10.9k tok/s; four hold 240 registers, one wavefront per SIMD,
-        // and measured 9.9k)
-        return moe_routed_launch_rt<S, GU, 2>(a, routed, shared, st) ||
+        // down: two row tiles per wavefront and eight wavefronts per
+        // workgroup, 256 rows (the Gemma-shaped layer at M = 32: one tile,
+        // four wavefronts 10.5k tok/s; two tiles 10.9k, then 11.3k with the
+        // later changes; eight wavefronts 11.45k; four tiles hold 240
+        // registers, one wavefront per SIMD, 9.9k; sixteen wavefronts 11.1k)
+        return moe_routed_launch_rt<S, GU, 2, 8>(a, routed, shared, st) ||
                moe_routed_launch_rt<S, GU, 1>(a, routed, shared, st);
     }
 }

@@ -52,8 +52,8 @@ __device__ __forceinline__ int gswz(int mp, int lr) {
 // gate and up, or its RT row tiles of down, over all K, its scales in a
 // private LDS block, DEPTH steps of code loads in flight, and writes its outputs:
 // h[pair][row] = bf16(gelu(g) * u), or part[pair][row]. A small LDS footprint
-// and few wavefronts (4) let several workgroups share a CU, so one
-// workgroup's staging overlaps the others' streaming.
+// and few wavefronts (NW: 4 for gate/up, 8 for down) let several workgroups
+// share a CU, so one workgroup's staging overlaps the others' streaming.
 // A launch covers the shared expert (S0.codes set) as ceil(M /
 // kMoeDescPairs) token descriptors of its own matrices (token t of descriptor
 // s is token s * kMoeDescPairs + t), the routed descriptor slots (W0.codes
@@ -85,8 +85,8 @@ __host__ __device__ inline size_t moe_routed_lds_bytes(int K, int group, int sgm
             (size_t)waves * nm * 16 * (sgmax + 1)) * 4;
 }
 
-template <int S, bool GU, int DEPTH, int SGMAX, int RT = 1>
-__global__ __launch_bounds__(256) void moe_routed_kernel(MoeRoutedArgs a) {
+template <int S, bool GU, int DEPTH, int SGMAX, int RT = 1, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void moe_routed_kernel(MoeRoutedArgs a) {
     using T = Traits<S>;
     using P = MfmaStep<S>;
     constexpr int GPS = P::GPS;
