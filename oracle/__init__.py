@@ -15,17 +15,19 @@ Sources (cited by page title and section; see each function):
 Parity status: every function here is pinned by tests/test_oracle_*.py against
 closed forms, exhaustive enumeration, exact rational arithmetic or an
 independent library routine, except the choices the pages leave open (the
-affine min/max rule, the FFN activation), which are pinned only by invariants
-and stated as readings.
+affine min/max rule, the FFN activation, the KV codec's all-zero vector), which
+are pinned only by invariants and stated as readings.
 """
 from .quant import (SCHEMES, GROUP, BITS, bf16_round, bf16_to_f32, quantize, quantize_sym4,
                     quantize_affine, pack, unpack, dequantize, quantize_pack, packed_nbytes)
 from .matmul import matmul_f64, abs_matmul_f64, gemv_reference
 from .moe import route, gelu_tanh, ffn, moe_sparse, moe_dense_masked
+from .kv import kv_quantize, kv_unpack, kv_dequant, kv_scores, kv_weighted_sum
 
 __all__ = [
     "SCHEMES", "GROUP", "BITS", "bf16_round", "bf16_to_f32", "quantize", "quantize_sym4",
     "quantize_affine", "pack", "unpack", "dequantize", "quantize_pack", "packed_nbytes",
     "matmul_f64", "abs_matmul_f64", "gemv_reference", "route", "gelu_tanh", "ffn",
-    "moe_sparse", "moe_dense_masked",
+    "moe_sparse", "moe_dense_masked", "kv_quantize", "kv_unpack", "kv_dequant", "kv_scores",
+    "kv_weighted_sum",
 ]
