@@ -56,6 +56,11 @@ _SIGS = {
     "w4a16_gemv": ([ctypes.POINTER(_W4Matrix), _P, _I64, _P, _P], ctypes.c_int),
     "w4a16_gemm": ([ctypes.POINTER(_W4Matrix), _P, _I64, _P, _P], ctypes.c_int),
     "w4_gemv_workspace_bytes": ([ctypes.POINTER(_W4Matrix), _I64], ctypes.c_size_t),
+    "w4_kv_quantize": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "w4_kv_scores": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
+    "w4_kv_weighted_sum_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
+    "w4_kv_weighted_sum": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P],
+                           ctypes.c_int),
     "w4a16_gemv_ws": ([ctypes.POINTER(_W4Matrix), _P, _I64, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "w4a16_gemv_multi": ([ctypes.POINTER(ctypes.POINTER(_W4Matrix)), ctypes.c_int, _P, _I64,
                           ctypes.POINTER(ctypes.c_void_p), _P], ctypes.c_int),
@@ -306,3 +311,57 @@ def moe_gemv(gate: QuantizedMatrix, up: QuantizedMatrix, down: QuantizedMatrix, 
     _check(lib().w4a16_moe_gemv(*refs, _ptr(x), M, _ptr(ids), _ptr(weights), top_k, _ptr(workspace),
                                 workspace.numel(), _ptr(y), _stream(x.device)))
     return y
+
+
+# ---------------------------------------------------------------- INT4 KV cache
+KV_HEAD_DIM = 128
+
+
+def kv_cache(Hkv: int, T_max: int, device="cuda"):
+    """An empty INT4 KV cache for one of K or V: (codes uint8 [Hkv][T_max][64], scales fp32 [Hkv][T_max])."""
+    codes = torch.empty((Hkv, T_max, KV_HEAD_DIM // 2), dtype=torch.uint8, device=device)
+    scales = torch.empty((Hkv, T_max), dtype=torch.float32, device=device)
+    return codes, scales
+
+
+def kv_quantize(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, pos: int) -> None:
+    """Quantize x fp32 [n][Hkv][128] (or [Hkv][128]) into the cache at positions pos .. pos+n-1."""
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("x must be contiguous fp32")
+    n = 1 if x.dim() == 2 else x.shape[0]
+    Hkv, T_max = scales.shape
+    _check(lib().w4_kv_quantize(_ptr(x), n, Hkv, pos, T_max, _ptr(codes), _ptr(scales),
+                                _stream(x.device)))
+
+
+def kv_scores(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, T: int,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """scores fp32 [Hq][T] = q [Hq][128] . dequant(K cache)[head group][t] for t < T."""
+    Hq = q.shape[0]
+    Hkv, T_max = scales.shape
+    if out is None:
+        out = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    _check(lib().w4_kv_scores(_ptr(q), Hq, Hkv, T, T_max, _ptr(codes), _ptr(scales), _ptr(out),
+                              _stream(q.device)))
+    return out
+
+
+def kv_weighted_sum_workspace_bytes(Hq: int, T: int) -> int:
+    return int(lib().w4_kv_weighted_sum_workspace_bytes(Hq, T))
+
+
+def kv_weighted_sum(p: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                    workspace: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out fp32 [Hq][128] = sum_t p[h][t] * dequant(V cache)[head group][t], t < p.shape[1]."""
+    Hq, T = p.shape
+    Hkv, T_max = scales.shape
+    if out is None:
+        out = torch.empty((Hq, KV_HEAD_DIM), dtype=torch.float32, device=p.device)
+    need = kv_weighted_sum_workspace_bytes(Hq, T)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=p.device)
+    _check(lib().w4_kv_weighted_sum(_ptr(p), Hq, Hkv, T, T_max, _ptr(codes), _ptr(scales), _ptr(out),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(p.device)))
+    return out

@@ -343,4 +343,65 @@ int w4a16_moe_gemv_logits(const w4_matrix* gate, const w4_matrix* up, const w4_m
                       "moe_gemv_logits launch");
 }
 
+// ---------------------------------------------------------------- INT4 KV cache
+static int kv_check_cache(int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max, const void* codes,
+                          const void* scales) {
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv)
+        return fail(W4_ESHAPE, "Hq=%lld must be a positive multiple of Hkv=%lld", (long long)Hq,
+                    (long long)Hkv);
+    if (T < 0 || T > T_max || T_max > 0x7fffffffLL || Hq * w4::kv_chunks(T_max) > 0x7fffffffLL)
+        return fail(W4_ESHAPE, "T=%lld, T_max=%lld out of range", (long long)T, (long long)T_max);
+    if (!codes || !scales) return fail(W4_EINVAL, "null codes or scales");
+    if (!aligned16(codes) || !aligned16(scales)) return fail(W4_EALIGN, "codes and scales must be 16-byte aligned");
+    return W4_OK;
+}
+
+int w4_kv_quantize(const float* x, int64_t n, int64_t Hkv, int64_t pos, int64_t T_max,
+                   uint8_t* codes, float* scales, void* stream) {
+    if (n < 0 || Hkv < 1 || pos < 0 || T_max < 1 || pos + n > T_max || T_max > 0x7fffffffLL ||
+        n * Hkv > 0x7fffffffLL)
+        return fail(W4_ESHAPE, "n=%lld Hkv=%lld pos=%lld T_max=%lld out of range", (long long)n,
+                    (long long)Hkv, (long long)pos, (long long)T_max);
+    if (n == 0) return ok();
+    if (!x || !codes || !scales) return fail(W4_EINVAL, "null x, codes or scales");
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
+        return fail(W4_EALIGN, "x, codes and scales must be 16-byte aligned");
+    return hip_status(w4::launch_kv_quantize(x, n, Hkv, pos, T_max, codes, scales, (hipStream_t)stream),
+                      "kv_quantize launch");
+}
+
+int w4_kv_scores(const float* q, int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max,
+                 const uint8_t* codes, const float* scales, float* scores, void* stream) {
+    int rc = kv_check_cache(Hq, Hkv, T, T_max, codes, scales);
+    if (rc) return rc;
+    if (T == 0) return ok();
+    if (!q || !scores) return fail(W4_EINVAL, "null q or scores");
+    if (!aligned16(q) || !aligned16(scores)) return fail(W4_EALIGN, "q and scores must be 16-byte aligned");
+    return hip_status(w4::launch_kv_scores(q, Hq, Hkv, T, T_max, codes, scales, scores, (hipStream_t)stream),
+                      "kv_scores launch");
+}
+
+size_t w4_kv_weighted_sum_workspace_bytes(int64_t Hq, int64_t T) {
+    if (Hq < 1 || T < 1 || T > 0x7fffffffLL) return 0;
+    return (size_t)Hq * (size_t)w4::kv_chunks(T) * w4::kKvHeadDim * sizeof(float);
+}
+
+int w4_kv_weighted_sum(const float* p, int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max,
+                       const uint8_t* codes, const float* scales, float* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    int rc = kv_check_cache(Hq, Hkv, T, T_max, codes, scales);
+    if (rc) return rc;
+    if (T < 1) return fail(W4_ESHAPE, "T=%lld: the weighted sum needs at least one position", (long long)T);
+    if (!p || !out) return fail(W4_EINVAL, "null p or out");
+    if (!aligned16(p) || !aligned16(out)) return fail(W4_EALIGN, "p and out must be 16-byte aligned");
+    const size_t need = w4_kv_weighted_sum_workspace_bytes(Hq, T);
+    if (!workspace || workspace_bytes < need)
+        return fail(W4_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(W4_EALIGN, "workspace must be 16-byte aligned");
+    return hip_status(w4::launch_kv_weighted_sum(p, Hq, Hkv, T, T_max, codes, scales, out,
+                                                 (float*)workspace, (hipStream_t)stream),
+                      "kv_weighted_sum launch");
+}
+
 }  // extern "C"

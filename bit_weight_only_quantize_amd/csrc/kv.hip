@@ -1,0 +1,243 @@
+// INT4 KV cache: the per-head-vector codec and the two products that read the
+// cache with the dequantization fused in.
+//
+// Shimmy article, §3.2 (TurboShimmy INT4 KV): every head vector is quantized
+// on its own with scale = max|v| / 7.5 (f32) and integers round(v / scale)
+// clamped to [-8, 7], stored plus 8 as nibbles (element 2j low); attention
+// dequantizes (nibble - 8) * scale on the GPU while it computes. Rounding is
+// the page's f32::round (halves away from zero); an all-zero vector gets
+// scale 0 and nibbles 8.
+//
+// Cache layout: codes [Hkv][T_max][D / 2] bytes and scales [Hkv][T_max] f32,
+// one head's positions contiguous, so both products stream a head's cache as
+// contiguous memory. D = 128.
+//
+// Products (query head h reads kv head h / (Hq / Hkv)):
+//   scores[h][t] = sum_i q[h][i] * k[t][i]         (kv_scores_kernel)
+//   out[h][i]    = sum_t p[h][t] * v[t][i]         (kv_wsum_kernel + kv_wsum_add_kernel)
+// Both are HBM-bound: 68 bytes of codes and scale per cached vector.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace w4 {
+
+// ---------------------------------------------------------------- quantize
+// One wavefront per head vector: lane l holds elements 2l and 2l + 1, the
+// wavefront's max |v| comes from a butterfly, and lane l writes byte l.
+__global__ __launch_bounds__(256) void kv_quantize_kernel(const float* __restrict__ x, int nvec,
+                                                          int H, int64_t pos, int64_t T_max,
+                                                          uint8_t* __restrict__ codes,
+                                                          float* __restrict__ scales) {
+    const int lane = threadIdx.x & 63;
+    const int v = blockIdx.x * 4 + (threadIdx.x >> 6);  // vector index n * H + h
+    if (v >= nvec) return;                                // whole wavefront
+    const float2 e = reinterpret_cast<const float2*>(x + (int64_t)v * kKvHeadDim)[lane];
+    float m = fmaxf(fabsf(e.x), fabsf(e.y));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float s = m / 7.5f;  // f32 division, correctly rounded
+    auto code = [&](float a) -> uint32_t {
+        const float q = s > 0.f ? fminf(fmaxf(roundf(a / s), -8.f), 7.f) : 0.f;  // roundf: halves away
+        return (uint32_t)((int)q + 8);
+    };
+    const int n = v / H, h = v - n * H;
+    const int64_t row = (int64_t)h * T_max + pos + n;
+    codes[row * (kKvHeadDim / 2) + lane] = (uint8_t)(code(e.x) | (code(e.y) << 4));
+    if (lane == 0) scales[row] = s;
+}
+
+// ---------------------------------------------------------------- scores
+// A wavefront takes one query head and a chunk of positions, 16 cached keys per
+// load instruction (1 KB contiguous): lane (key j = lane / 4, part c = lane %
+// 4) holds 32 elements of key j, i.e. bytes 16c..16c+15 of its row. The
+// nibbles convert exactly (v_cvt_f32_ubyte of the masked bytes) and meet the
+// query in f32 FMAs: sum q (u - 8) = sum q u - 8 sum q, the second sum taken
+// once. Four lanes of a key add their parts by cross-lane steps; the key's
+// scale multiplies the total.
+constexpr int kKvChunk = 128;   // positions per wavefront
+constexpr int kKvDepth = 4;     // 16-key loads in flight per wavefront
+
+__device__ __forceinline__ float kv_dot32(const u32x4_t c, const float* qe, const float* qo) {
+    float acc = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint32_t lo = c[d] & 0x0F0F0F0Fu, hi = (c[d] >> 4) & 0x0F0F0F0Fu;
+        // keep the byte masks: one v_cvt_f32_ubyte per nibble afterwards
+        asm("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            acc = fmaf(qe[4 * d + b], (float)((lo >> (8 * b)) & 0xFFu), acc);
+            acc = fmaf(qo[4 * d + b], (float)((hi >> (8 * b)) & 0xFFu), acc);
+        }
+    }
+    return acc;
+}
+
+__global__ __launch_bounds__(256) void kv_scores_kernel(const float* __restrict__ q, int Hq,
+                                                        int group, int T, int64_t T_max,
+                                                        const uint8_t* __restrict__ codes,
+                                                        const float* __restrict__ scales,
+                                                        float* __restrict__ scores, int nch) {
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);  // (chunk, head) with heads fastest
+    if (w >= nch * Hq) return;                           // whole wavefront
+    const int h = w % Hq, ch = w / Hq;
+    const int g = h / group;
+    const int j = lane >> 2, c = lane & 3;
+    // this lane's 32 query elements, even and odd
+    float qe[16], qo[16];
+    const float2* qp = reinterpret_cast<const float2*>(q + (int64_t)h * kKvHeadDim + 32 * c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float2 e = qp[i];
+        qe[i] = e.x;
+        qo[i] = e.y;
+    }
+    float qs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qs += qe[i] + qo[i];
+    const int t0 = ch * kKvChunk;
+    const uint8_t* base = codes + (int64_t)g * T_max * (kKvHeadDim / 2) + 16 * c;
+    const float* sbase = scales + (int64_t)g * T_max;
+    constexpr int IT = kKvChunk / 16;
+    u32x4_t cb[kKvDepth];
+    float sb[kKvDepth];
+    auto load = [&](int it, int slot) {  // clamped: keys past T reload T - 1
+        const int t = min(t0 + 16 * min(it, IT - 1) + j, T - 1);
+        cb[slot] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)t * (kKvHeadDim / 2));
+        sb[slot] = sbase[t];
+    };
+#pragma unroll
+    for (int p = 0; p < kKvDepth; ++p) load(p, p);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int slot = it % kKvDepth;
+        float d = kv_dot32(cb[slot], qe, qo) - 8.f * qs;
+        const float s = sb[slot];
+        if (it + kKvDepth < IT) load(it + kKvDepth, slot);
+        d += __shfl_xor(d, 1);
+        d += __shfl_xor(d, 2);
+        // every lane stores (no branch in the load pipeline): the 4 lanes of a
+        // key store the same value, keys past T rewrite the score of T - 1
+        scores[(int64_t)h * T + min(t0 + 16 * it + j, T - 1)] = s * d;
+    }
+}
+
+// ---------------------------------------------------------------- weighted sum
+// The same lane layout over the values: a lane accumulates p_t * scale_t times
+// its 32 nibbles (as 0..15) and the weight sum W = sum p_t scale_t, so its
+// elements are acc - 8 W. After the chunk the 16 lanes of each part add their
+// accumulators (cross-lane steps over lane bits 2..5, a fixed order), and the
+// chunk's 128 partial outputs go to part[h][chunk][128]; kv_wsum_add_kernel
+// adds the chunks in order.
+__global__ __launch_bounds__(256) void kv_wsum_kernel(const float* __restrict__ pw, int Hq,
+                                                      int group, int T, int64_t T_max,
+                                                      const uint8_t* __restrict__ codes,
+                                                      const float* __restrict__ scales,
+                                                      float* __restrict__ part, int nch) {
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w >= nch * Hq) return;
+    const int h = w % Hq, ch = w / Hq;
+    const int g = h / group;
+    const int j = lane >> 2, c = lane & 3;
+    const int t0 = ch * kKvChunk;
+    const uint8_t* base = codes + (int64_t)g * T_max * (kKvHeadDim / 2) + 16 * c;
+    const float* sbase = scales + (int64_t)g * T_max;
+    const float* prow = pw + (int64_t)h * T;
+    constexpr int IT = kKvChunk / 16;
+    u32x4_t cb[kKvDepth];
+    float wb[kKvDepth];
+    auto load = [&](int it, int slot) {  // keys past T get weight 0
+        const int tt = t0 + 16 * min(it, IT - 1) + j;
+        const int t = min(tt, T - 1);
+        cb[slot] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)t * (kKvHeadDim / 2));
+        wb[slot] = tt < T ? prow[t] * sbase[t] : 0.f;
+    };
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+    float W = 0.f;
+#pragma unroll
+    for (int p = 0; p < kKvDepth; ++p) load(p, p);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int slot = it % kKvDepth;
+        const u32x4_t cw = cb[slot];
+        const float wt = wb[slot];
+        if (it + kKvDepth < IT) load(it + kKvDepth, slot);
+        W += wt;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t lo = cw[d] & 0x0F0F0F0Fu, hi = (cw[d] >> 4) & 0x0F0F0F0Fu;
+            asm("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                acc[8 * d + 2 * b] = fmaf(wt, (float)((lo >> (8 * b)) & 0xFFu), acc[8 * d + 2 * b]);
+                acc[8 * d + 2 * b + 1] = fmaf(wt, (float)((hi >> (8 * b)) & 0xFFu), acc[8 * d + 2 * b + 1]);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = fmaf(-8.f, W, acc[i]);
+    // lanes c, c + 4, ..., c + 60 hold part c of 16 keys: add them
+#pragma unroll
+    for (int o = 4; o <= 32; o <<= 1)
+#pragma unroll
+        for (int i = 0; i < 32; ++i) acc[i] += __shfl_xor(acc[i], o);
+    if (j == 0) {
+        float4* dst = reinterpret_cast<float4*>(part + ((int64_t)h * nch + ch) * kKvHeadDim + 32 * c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[i] = make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
+    }
+}
+
+__global__ __launch_bounds__(256) void kv_wsum_add_kernel(const float* __restrict__ part, int Hq,
+                                                          int nch, float* __restrict__ out) {
+    const int i = blockIdx.x * 256 + threadIdx.x;  // h * 128 + element
+    if (i >= Hq * kKvHeadDim) return;
+    const int h = i / kKvHeadDim, e = i - h * kKvHeadDim;
+    const float* p = part + (int64_t)h * nch * kKvHeadDim + e;
+    float s = 0.f;
+    for (int ch = 0; ch < nch; ++ch) s += p[(int64_t)ch * kKvHeadDim];
+    out[i] = s;
+}
+
+// ---------------------------------------------------------------- host side
+int kv_chunks(int64_t T) { return (int)((T + kKvChunk - 1) / kKvChunk); }
+
+hipError_t launch_kv_quantize(const float* x, int64_t n, int64_t H, int64_t pos, int64_t T_max,
+                              uint8_t* codes, float* scales, hipStream_t st) {
+    const int nvec = (int)(n * H);
+    hipLaunchKernelGGL(kv_quantize_kernel, dim3((unsigned)((nvec + 3) / 4)), dim3(256), 0, st, x,
+                       nvec, (int)H, pos, T_max, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_scores(const float* q, int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max,
+                            const uint8_t* codes, const float* scales, float* scores,
+                            hipStream_t st) {
+    const int nch = kv_chunks(T);
+    const int64_t waves = (int64_t)nch * Hq;
+    hipLaunchKernelGGL(kv_scores_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, q,
+                       (int)Hq, (int)(Hq / Hkv), (int)T, T_max, codes, scales, scores, nch);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_weighted_sum(const float* p, int64_t Hq, int64_t Hkv, int64_t T,
+                                  int64_t T_max, const uint8_t* codes, const float* scales,
+                                  float* out, float* part, hipStream_t st) {
+    const int nch = kv_chunks(T);
+    const int64_t waves = (int64_t)nch * Hq;
+    hipLaunchKernelGGL(kv_wsum_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p,
+                       (int)Hq, (int)(Hq / Hkv), (int)T, T_max, codes, scales, part, nch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kv_wsum_add_kernel, dim3((unsigned)((Hq * kKvHeadDim + 255) / 256)),
+                       dim3(256), 0, st, part, (int)Hq, nch, out);
+    return hipGetLastError();
+}
+
+}  // namespace w4

@@ -12,6 +12,7 @@ hipError_t launch_quantize_pack(int scheme, const float* W, int64_t N, int64_t K
 
 // Largest K the skinny kernels can stage in LDS for one token.
 constexpr int64_t kMaxSkinnyK = 28672;
+constexpr int kKvHeadDim = 128;  // INT4 KV cache: values per head vector
 
 struct GemvPlan {
     int lpr, v, r, mt;
@@ -88,5 +89,16 @@ hipError_t launch_moe(int scheme, const MoeMats& W, const uint16_t* x, int64_t M
 hipError_t launch_moe_logits(int scheme, const MoeMats& W, const uint16_t* x, int64_t M,
                              const float* logits, int k, int32_t* ids, float* wts, void* ws,
                              float* y, hipStream_t st);
+
+// ---- INT4 KV cache (head vectors of kKvHeadDim values)
+int kv_chunks(int64_t T);  // position chunks of the weighted sum (partials per head)
+hipError_t launch_kv_quantize(const float* x, int64_t n, int64_t H, int64_t pos, int64_t T_max,
+                              uint8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_kv_scores(const float* q, int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max,
+                            const uint8_t* codes, const float* scales, float* scores,
+                            hipStream_t st);
+hipError_t launch_kv_weighted_sum(const float* p, int64_t Hq, int64_t Hkv, int64_t T,
+                                  int64_t T_max, const uint8_t* codes, const float* scales,
+                                  float* out, float* part, hipStream_t st);
 
 }  // namespace w4

@@ -211,6 +211,53 @@ int w4a16_moe_gemv_logits(const w4_matrix* gate, const w4_matrix* up, const w4_m
                           int32_t* ids, float* weights, void* workspace, size_t workspace_bytes,
                           float* y, void* stream);
 
+/*
+ * INT4 KV cache ([Shimmy] §3.2, TurboShimmy INT4 KV): each head vector of
+ * W4_KV_HEAD_DIM fp32 values is quantized on its own: scale = max|v| / 7.5
+ * (fp32), integers round(v / scale) (halves away from zero, as the page's
+ * f32::round) clamped to [-8, 7], stored plus 8 as nibbles, element 2j in the
+ * low nibble of byte j; an all-zero vector gets scale 0 and every nibble 8. A
+ * cached value reads back as (nibble - 8) * scale.
+ * Cache layout (caller-allocated, [Shimmy] §3.1 sizes it per layer): codes
+ * uint8 [Hkv][T_max][W4_KV_HEAD_DIM / 2], scales fp32 [Hkv][T_max]; one head's
+ * positions are contiguous. Query head h reads key/value head h / (Hq / Hkv).
+ */
+#define W4_KV_HEAD_DIM 128
+
+/*
+ * Quantize n new positions of Hkv head vectors into the cache: x fp32
+ * [n][Hkv][W4_KV_HEAD_DIM] -> codes/scales at positions pos .. pos + n - 1.
+ * 0 <= pos, pos + n <= T_max (W4_ESHAPE otherwise). n == 0 is a no-op.
+ */
+int w4_kv_quantize(const float* x, int64_t n, int64_t Hkv, int64_t pos, int64_t T_max,
+                   uint8_t* codes, float* scales, void* stream);
+
+/*
+ * scores[h][t] = sum_i q[h][i] * k[t][i] for the first T cached positions, with
+ * the dequantization fused into the product ([Shimmy] §3.2: the shader
+ * dequantizes while it computes the attention scores). q fp32 [Hq][D]; scores
+ * fp32 [Hq][T]. Scaling by 1/sqrt(D), masking and the softmax are the caller's.
+ * 1 <= T <= T_max; Hq a multiple of Hkv (W4_ESHAPE otherwise). Deterministic.
+ */
+int w4_kv_scores(const float* q, int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max,
+                 const uint8_t* codes, const float* scales, float* scores, void* stream);
+
+/* Host-only. Workspace bytes w4_kv_weighted_sum needs for Hq heads over T positions. */
+size_t w4_kv_weighted_sum_workspace_bytes(int64_t Hq, int64_t T);
+
+/*
+ * out[h][i] = sum_t p[h][t] * v[t][i] over the first T cached positions (the
+ * value side of attention, dequantization fused in). p fp32 [Hq][T] (e.g. the
+ * softmax of the scores); out fp32 [Hq][D]. Positions are summed in chunks whose
+ * partial outputs go to the workspace (device memory of at least
+ * w4_kv_weighted_sum_workspace_bytes(Hq, T) bytes, W4_EWORKSPACE otherwise;
+ * contents on entry do not matter, on return unspecified), then added in a fixed
+ * order. Shapes and errors as for w4_kv_scores.
+ */
+int w4_kv_weighted_sum(const float* p, int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max,
+                       const uint8_t* codes, const float* scales, float* out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char* w4_last_error(void);
 

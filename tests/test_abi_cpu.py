@@ -98,6 +98,26 @@ def test_gemv_ws_argument_validation_without_a_device():
     assert L.w4a16_gemv_ws(ctypes.byref(_desc(E=2)), 16, 16, 16, 16, need, None) == -2
 
 
+def test_kv_argument_validation_without_a_device():
+    L = w4.lib()
+    assert L.w4_kv_weighted_sum_workspace_bytes(32, 8192) == 32 * 64 * 128 * 4   # 64 chunks of 128
+    assert L.w4_kv_weighted_sum_workspace_bytes(3, 129) == 3 * 2 * 128 * 4
+    assert L.w4_kv_weighted_sum_workspace_bytes(0, 10) == 0
+    assert L.w4_kv_quantize(16, 0, 4, 0, 8, 16, 16, None) == 0                   # n == 0: no-op
+    assert L.w4_kv_quantize(16, 2, 4, 7, 8, 16, 16, None) == -2                  # past T_max
+    assert L.w4_kv_quantize(None, 1, 4, 0, 8, 16, 16, None) == -1
+    assert L.w4_kv_quantize(8, 1, 4, 0, 8, 16, 16, None) == -3
+    assert L.w4_kv_scores(16, 6, 4, 10, 16, 16, 16, 16, None) == -2              # 6 heads over 4
+    assert L.w4_kv_scores(16, 8, 4, 17, 16, 16, 16, 16, None) == -2              # T > T_max
+    assert L.w4_kv_scores(16, 8, 4, 0, 16, 16, 16, 16, None) == 0                # T == 0: no-op
+    assert L.w4_kv_scores(16, 8, 4, 4, 16, 16, 24, 16, None) == -3
+    need = L.w4_kv_weighted_sum_workspace_bytes(8, 10)
+    assert L.w4_kv_weighted_sum(16, 8, 4, 10, 16, 16, 16, 16, None, 0, None) == -5
+    assert L.w4_kv_weighted_sum(16, 8, 4, 10, 16, 16, 16, 16, 16, need - 16, None) == -5
+    assert L.w4_kv_weighted_sum(16, 8, 4, 0, 16, 16, 16, 16, 16, need, None) == -2   # no position
+    assert L.w4_kv_weighted_sum(16, 8, 4, 10, 16, 16, 16, 16, 8, need, None) == -3
+
+
 def test_quantize_argument_validation_without_a_device():
     L = w4.lib()
     assert L.w4_quantize_pack(0, 16, 0, 128, 16, 16, None, None) == 0   # N == 0: no-op
