@@ -62,7 +62,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b",
-                    choices=["llama7b", "moe26b", "prefill", "llama13b", "gemv1024"])
+                    choices=["llama7b", "moe26b", "prefill", "llama13b", "gemv1024", "kv"])
+    ap.add_argument("--context", type=int, default=8192, help="kv: cached positions per layer")
     ap.add_argument("--M", type=int, default=None, help="decode tokens per step")
     ap.add_argument("--scheme", default=None, choices=["sym4_g128", "aff4_g64", "aff8_g64"],
                     help="weight scheme of the llama7b/llama13b stacks (default: sym4_g128 / aff4_g64)")
@@ -352,6 +353,101 @@ def run_moe(c: Ctx, a):
     return out
 
 
+# ---------------------------------------------------------------- INT4 KV cache
+def run_kv(c: Ctx, a):
+    """Decode over an INT4 KV cache (Shimmy article §3.2, TurboShimmy): per layer,
+    append the new token's K and V vectors (quantize), then the fused-dequant
+    scores over the T + 1 cached keys and the weighted sum over the T + 1 cached
+    values. The weights are a fixed softmax of random logits: the softmax itself
+    is not a library operation. Llama-7B-shaped: 32 layers, 32 heads of 128."""
+    torch, w4 = c.torch, c.w4
+    layers = a.layers or 32
+    Hq = Hkv = 32
+    D = w4.KV_HEAD_DIM
+    T = a.context
+    Tn = T + 1
+    gen = torch.Generator(device=c.dev)
+    gen.manual_seed(0)
+    L = []
+    for _ in range(layers):
+        kc, ks = w4.kv_cache(Hkv, Tn, c.dev)
+        vc, vs = w4.kv_cache(Hkv, Tn, c.dev)
+        for codes, scales in ((kc, ks), (vc, vs)):
+            x = torch.randn((T, Hkv, D), generator=gen, device=c.dev)
+            w4.kv_quantize(x, codes, scales, 0)
+        L.append((kc, ks, vc, vs))
+    knew = torch.randn((1, Hkv, D), generator=gen, device=c.dev)
+    vnew = torch.randn((1, Hkv, D), generator=gen, device=c.dev)
+    q = torch.randn((Hq, D), generator=gen, device=c.dev)
+    p = torch.softmax(torch.randn((Hq, Tn), generator=gen, device=c.dev), dim=1).contiguous()
+    scores = torch.empty((Hq, Tn), dtype=torch.float32, device=c.dev)
+    out = torch.empty((Hq, D), dtype=torch.float32, device=c.dev)
+    ws = torch.empty(w4.kv_weighted_sum_workspace_bytes(Hq, Tn), dtype=torch.uint8, device=c.dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for kc, ks, vc, vs in L:
+            w4.kv_quantize(knew, kc, ks, T)
+            w4.kv_quantize(vnew, vc, vs, T)
+            w4.kv_scores(q, kc, ks, Tn, out=scores)
+            w4.kv_weighted_sum(p, vc, vs, workspace=ws, out=out)
+
+    def dominant():
+        for kc, ks, _, _ in L:
+            w4.kv_scores(q, kc, ks, Tn, out=scores)
+
+    cache_b = Hkv * Tn * (D // 2 + 4)                  # one of K or V: codes + scales
+    scores_b = cache_b + Hq * D * 4 + Hq * Tn * 4        # + q read + scores written
+    wsum_b = cache_b + Hq * Tn * 4 + Hq * D * 4          # + weights read + out written
+    quant_b = 2 * Hkv * (D * 4 + D // 2 + 4)             # new K, V: fp32 in, codes + scale out
+    step_bytes = layers * (scores_b + wsum_b + quant_b)
+    g = c.graph(step)
+    ms = c.time_graph(g, a.steps, a.warmup)
+    g_dom = c.graph(dominant)
+    us_dom = c.time_graph(g_dom, max(4, a.steps // 2), 2) * 1e3 / layers
+    tbs = step_bytes / (ms * 1e-3) / 1e12
+    res = base_line(a, "INT4 KV decode (append + scores + weighted sum) HBM TB/s over the cache bytes read",
+                    round(tbs, 4), "TB/s", ms, {
+                        "workload": "llama7b-shaped INT4 KV cache decode, 32 layers", "layers": layers,
+                        "heads_q": Hq, "heads_kv": Hkv, "head_dim": D, "context": Tn,
+                        "cache_bytes": layers * 2 * cache_b,
+                        "launches_per_layer": "quantize K, quantize V, scores, weighted sum (+ chunk add)"},
+                    dtype="f32")
+    res["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
+    res["tok_per_s"] = round(1 / (ms * 1e-3), 1)
+    res["step_bytes"] = step_bytes
+    res["roofline"] = hbm_roofline(f"kv_scores_kernel ({Hq} heads x {Tn} positions, INT4 keys)", scores_b, us_dom)
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = kv_cpu_baseline(L[0], q, p, a.cpu_seconds, Tn)
+    return res
+
+
+def kv_cpu_baseline(layer, q, p, budget_s, Tn):
+    """The oracle as it stands on layer 0's cache (host copies): scores and
+    weighted sum repeated until the budget."""
+    import oracle
+    kc, ks, vc, vs = (t.cpu().numpy() for t in layer)
+    qh, ph = q.cpu().numpy(), p.cpu().numpy()
+    threads = os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        pass
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.kv_scores(qh, kc, ks)
+        oracle.kv_weighted_sum(ph, vc, vs)
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = n * 2 * (kc.nbytes + ks.nbytes)
+    return {"value": nbytes / dt / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer 0's K and V caches ({Tn} positions x 32 heads): numpy fp64 dequantize + "
+                      f"matrix products, {n} passes in {dt:.1f} s"}
+
+
 # ---------------------------------------------------------------- prefill
 def run_prefill(c: Ctx, a):
     torch, w4 = c.torch, c.w4
@@ -437,6 +533,8 @@ def main():
         out = run_moe(c, a)
     elif a.workload == "prefill":
         out = run_prefill(c, a)
+    elif a.workload == "kv":
+        out = run_kv(c, a)
     else:
         out = run_gemv1024(c, a)
     print(json.dumps(out), flush=True)

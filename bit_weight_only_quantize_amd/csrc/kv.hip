@@ -56,8 +56,11 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const float* __restric
 // query in f32 FMAs: sum q (u - 8) = sum q u - 8 sum q, the second sum taken
 // once. Four lanes of a key add their parts by cross-lane steps; the key's
 // scale multiplies the total.
-constexpr int kKvChunk = 128;   // positions per wavefront
-constexpr int kKvDepth = 4;     // 16-key loads in flight per wavefront
+// Positions per wavefront, 4 of its 16-key loads in flight. Measured on the
+// 7B-shaped cache (32 heads, 8193 positions): chunks of 64, 256 or 512 and 8
+// loads in flight were all slower or the same, for both products.
+constexpr int kKvChunk = 128;
+constexpr int kKvDepth = 4;
 
 __device__ __forceinline__ float kv_dot32(const u32x4_t c, const float* qe, const float* qo) {
     float acc = 0.f;
@@ -75,6 +78,7 @@ __device__ __forceinline__ float kv_dot32(const u32x4_t c, const float* qe, cons
     return acc;
 }
 
+template <int CHUNK, int DEPTH>
 __global__ __launch_bounds__(256) void kv_scores_kernel(const float* __restrict__ q, int Hq,
                                                         int group, int T, int64_t T_max,
                                                         const uint8_t* __restrict__ codes,
@@ -98,25 +102,25 @@ __global__ __launch_bounds__(256) void kv_scores_kernel(const float* __restrict_
     float qs = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) qs += qe[i] + qo[i];
-    const int t0 = ch * kKvChunk;
+    const int t0 = ch * CHUNK;
     const uint8_t* base = codes + (int64_t)g * T_max * (kKvHeadDim / 2) + 16 * c;
     const float* sbase = scales + (int64_t)g * T_max;
-    constexpr int IT = kKvChunk / 16;
-    u32x4_t cb[kKvDepth];
-    float sb[kKvDepth];
+    constexpr int IT = CHUNK / 16;
+    u32x4_t cb[DEPTH];
+    float sb[DEPTH];
     auto load = [&](int it, int slot) {  // clamped: keys past T reload T - 1
         const int t = min(t0 + 16 * min(it, IT - 1) + j, T - 1);
         cb[slot] = *reinterpret_cast<const u32x4_t*>(base + (int64_t)t * (kKvHeadDim / 2));
         sb[slot] = sbase[t];
     };
 #pragma unroll
-    for (int p = 0; p < kKvDepth; ++p) load(p, p);
+    for (int p = 0; p < DEPTH; ++p) load(p, p);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int slot = it % kKvDepth;
+        const int slot = it % DEPTH;
         float d = kv_dot32(cb[slot], qe, qo) - 8.f * qs;
         const float s = sb[slot];
-        if (it + kKvDepth < IT) load(it + kKvDepth, slot);
+        if (it + DEPTH < IT) load(it + DEPTH, slot);
         d += __shfl_xor(d, 1);
         d += __shfl_xor(d, 2);
         // every lane stores (no branch in the load pipeline): the 4 lanes of a
@@ -131,7 +135,8 @@ __global__ __launch_bounds__(256) void kv_scores_kernel(const float* __restrict_
 // elements are acc - 8 W. After the chunk the 16 lanes of each part add their
 // accumulators (cross-lane steps over lane bits 2..5, a fixed order), and the
 // chunk's 128 partial outputs go to part[h][chunk][128]; kv_wsum_add_kernel
-// adds the chunks in order.
+// adds the chunks in a fixed order.
+template <int CHUNK, int DEPTH>
 __global__ __launch_bounds__(256) void kv_wsum_kernel(const float* __restrict__ pw, int Hq,
                                                       int group, int T, int64_t T_max,
                                                       const uint8_t* __restrict__ codes,
@@ -143,13 +148,13 @@ __global__ __launch_bounds__(256) void kv_wsum_kernel(const float* __restrict__ 
     const int h = w % Hq, ch = w / Hq;
     const int g = h / group;
     const int j = lane >> 2, c = lane & 3;
-    const int t0 = ch * kKvChunk;
+    const int t0 = ch * CHUNK;
     const uint8_t* base = codes + (int64_t)g * T_max * (kKvHeadDim / 2) + 16 * c;
     const float* sbase = scales + (int64_t)g * T_max;
     const float* prow = pw + (int64_t)h * T;
-    constexpr int IT = kKvChunk / 16;
-    u32x4_t cb[kKvDepth];
-    float wb[kKvDepth];
+    constexpr int IT = CHUNK / 16;
+    u32x4_t cb[DEPTH];
+    float wb[DEPTH];
     auto load = [&](int it, int slot) {  // keys past T get weight 0
         const int tt = t0 + 16 * min(it, IT - 1) + j;
         const int t = min(tt, T - 1);
@@ -161,13 +166,13 @@ __global__ __launch_bounds__(256) void kv_wsum_kernel(const float* __restrict__ 
     for (int i = 0; i < 32; ++i) acc[i] = 0.f;
     float W = 0.f;
 #pragma unroll
-    for (int p = 0; p < kKvDepth; ++p) load(p, p);
+    for (int p = 0; p < DEPTH; ++p) load(p, p);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int slot = it % kKvDepth;
+        const int slot = it % DEPTH;
         const u32x4_t cw = cb[slot];
         const float wt = wb[slot];
-        if (it + kKvDepth < IT) load(it + kKvDepth, slot);
+        if (it + DEPTH < IT) load(it + DEPTH, slot);
         W += wt;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -194,15 +199,32 @@ __global__ __launch_bounds__(256) void kv_wsum_kernel(const float* __restrict__ 
     }
 }
 
+// out[h][e] = the sum of part[h][ch][e] over the chunks: 16 lanes per output,
+// lane k taking chunks k, k + 16, ... (eight loads in flight, added in chunk
+// order), then the 16 lane sums added by cross-lane steps in a fixed order.
 __global__ __launch_bounds__(256) void kv_wsum_add_kernel(const float* __restrict__ part, int Hq,
                                                           int nch, float* __restrict__ out) {
-    const int i = blockIdx.x * 256 + threadIdx.x;  // h * 128 + element
-    if (i >= Hq * kKvHeadDim) return;
-    const int h = i / kKvHeadDim, e = i - h * kKvHeadDim;
+    const int i = blockIdx.x * 16 + (threadIdx.x >> 4);  // h * 128 + element
+    const int k = threadIdx.x & 15;
+    const bool live = i < Hq * kKvHeadDim;
+    const int ic = live ? i : 0;
+    const int h = ic / kKvHeadDim, e = ic - h * kKvHeadDim;
     const float* p = part + (int64_t)h * nch * kKvHeadDim + e;
     float s = 0.f;
-    for (int ch = 0; ch < nch; ++ch) s += p[(int64_t)ch * kKvHeadDim];
-    out[i] = s;
+    for (int c0 = k; c0 < nch; c0 += 16 * 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int ch = c0 + 16 * u;
+            v[u] = p[(int64_t)min(ch, nch - 1) * kKvHeadDim];
+            v[u] = ch < nch ? v[u] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+    if (live && k == 0) out[i] = s;
 }
 
 // ---------------------------------------------------------------- host side
@@ -221,8 +243,9 @@ hipError_t launch_kv_scores(const float* q, int64_t Hq, int64_t Hkv, int64_t T, 
                             hipStream_t st) {
     const int nch = kv_chunks(T);
     const int64_t waves = (int64_t)nch * Hq;
-    hipLaunchKernelGGL(kv_scores_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, q,
-                       (int)Hq, (int)(Hq / Hkv), (int)T, T_max, codes, scales, scores, nch);
+    hipLaunchKernelGGL((kv_scores_kernel<kKvChunk, kKvDepth>), dim3((unsigned)((waves + 3) / 4)),
+                       dim3(256), 0, st, q, (int)Hq, (int)(Hq / Hkv), (int)T, T_max, codes, scales,
+                       scores, nch);
     return hipGetLastError();
 }
 
@@ -231,11 +254,12 @@ hipError_t launch_kv_weighted_sum(const float* p, int64_t Hq, int64_t Hkv, int64
                                   float* out, float* part, hipStream_t st) {
     const int nch = kv_chunks(T);
     const int64_t waves = (int64_t)nch * Hq;
-    hipLaunchKernelGGL(kv_wsum_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p,
-                       (int)Hq, (int)(Hq / Hkv), (int)T, T_max, codes, scales, part, nch);
+    hipLaunchKernelGGL((kv_wsum_kernel<kKvChunk, kKvDepth>), dim3((unsigned)((waves + 3) / 4)),
+                       dim3(256), 0, st, p, (int)Hq, (int)(Hq / Hkv), (int)T, T_max, codes, scales,
+                       part, nch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kv_wsum_add_kernel, dim3((unsigned)((Hq * kKvHeadDim + 255) / 256)),
+    hipLaunchKernelGGL(kv_wsum_add_kernel, dim3((unsigned)((Hq * kKvHeadDim + 15) / 16)),
                        dim3(256), 0, st, part, (int)Hq, nch, out);
     return hipGetLastError();
 }
