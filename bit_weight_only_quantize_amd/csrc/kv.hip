@@ -62,6 +62,12 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const float* __restric
 constexpr int kKvChunk = 128;
 constexpr int kKvDepth = 4;
 
+// value of the lane N places along in the same row of 16 (DPP row_ror:N)
+template <int N>
+__device__ __forceinline__ float dpp_row_ror(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float kv_dot32(const u32x4_t c, const float* qe, const float* qo) {
     float acc = 0.f;
 #pragma unroll
@@ -187,15 +193,31 @@ __global__ __launch_bounds__(256) void kv_wsum_kernel(const float* __restrict__ 
     }
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = fmaf(-8.f, W, acc[i]);
-    // lanes c, c + 4, ..., c + 60 hold part c of 16 keys: add them
+    // lanes c, c + 4, ..., c + 60 hold part c of 16 keys: add them. Inside a
+    // row of 16 lanes, rotations by 4 and by 8 (DPP, no LDS) leave every lane
+    // with its row's sum for its part; across the 4 rows, lane (row R, r =
+    // lane / 4 % 4) then adds only elements 8r .. 8r + 7 of its part (two
+    // cross-lane steps on 8 values instead of four on 32), and row 0 stores.
+    // Each output comes from one fixed lane: deterministic.
 #pragma unroll
-    for (int o = 4; o <= 32; o <<= 1)
+    for (int i = 0; i < 32; ++i) {
+        acc[i] += dpp_row_ror<4>(acc[i]);
+        acc[i] += dpp_row_ror<8>(acc[i]);
+    }
+    const int r = (lane >> 2) & 3;
+    float o8[8];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] += __shfl_xor(acc[i], o);
-    if (j == 0) {
-        float4* dst = reinterpret_cast<float4*>(part + ((int64_t)h * nch + ch) * kKvHeadDim + 32 * c);
+    for (int i = 0; i < 8; ++i)
+        o8[i] = r == 0 ? acc[i] : r == 1 ? acc[8 + i] : r == 2 ? acc[16 + i] : acc[24 + i];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
+    for (int i = 0; i < 8; ++i) {
+        o8[i] += __shfl_xor(o8[i], 16);
+        o8[i] += __shfl_xor(o8[i], 32);
+    }
+    if (lane < 16) {
+        float4* dst = reinterpret_cast<float4*>(part + ((int64_t)h * nch + ch) * kKvHeadDim + 32 * c + 8 * r);
+        dst[0] = make_float4(o8[0], o8[1], o8[2], o8[3]);
+        dst[1] = make_float4(o8[4], o8[5], o8[6], o8[7]);
     }
 }
 
