@@ -57,6 +57,7 @@ _SIGS = {
     "w4a16_gemm": ([ctypes.POINTER(_W4Matrix), _P, _I64, _P, _P], ctypes.c_int),
     "w4_gemv_workspace_bytes": ([ctypes.POINTER(_W4Matrix), _I64], ctypes.c_size_t),
     "w4_kv_quantize": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "w4_kv_append": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "w4_kv_scores": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "w4_kv_weighted_sum_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
     "w4_kv_weighted_sum": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P],
@@ -332,6 +333,17 @@ def kv_quantize(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, pos:
     Hkv, T_max = scales.shape
     _check(lib().w4_kv_quantize(_ptr(x), n, Hkv, pos, T_max, _ptr(codes), _ptr(scales),
                                 _stream(x.device)))
+
+
+def kv_append(k: torch.Tensor, v: torch.Tensor, k_cache, v_cache, pos: int) -> None:
+    """Quantize k and v fp32 [n][Hkv][128] into their caches ((codes, scales) pairs) at pos, one launch."""
+    for t in (k, v):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("k and v must be contiguous fp32")
+    n = 1 if k.dim() == 2 else k.shape[0]
+    Hkv, T_max = k_cache[1].shape
+    _check(lib().w4_kv_append(_ptr(k), _ptr(v), n, Hkv, pos, T_max, _ptr(k_cache[0]), _ptr(k_cache[1]),
+                              _ptr(v_cache[0]), _ptr(v_cache[1]), _stream(k.device)))
 
 
 def kv_scores(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, T: int,

@@ -356,18 +356,43 @@ static int kv_check_cache(int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max, con
     return W4_OK;
 }
 
-int w4_kv_quantize(const float* x, int64_t n, int64_t Hkv, int64_t pos, int64_t T_max,
-                   uint8_t* codes, float* scales, void* stream) {
+static int kv_check_append(int64_t n, int64_t Hkv, int64_t pos, int64_t T_max) {
     if (n < 0 || Hkv < 1 || pos < 0 || T_max < 1 || pos + n > T_max || T_max > 0x7fffffffLL ||
-        n * Hkv > 0x7fffffffLL)
+        2 * n * Hkv > 0x7fffffffLL)
         return fail(W4_ESHAPE, "n=%lld Hkv=%lld pos=%lld T_max=%lld out of range", (long long)n,
                     (long long)Hkv, (long long)pos, (long long)T_max);
+    return W4_OK;
+}
+
+int w4_kv_quantize(const float* x, int64_t n, int64_t Hkv, int64_t pos, int64_t T_max,
+                   uint8_t* codes, float* scales, void* stream) {
+    int rc = kv_check_append(n, Hkv, pos, T_max);
+    if (rc) return rc;
     if (n == 0) return ok();
     if (!x || !codes || !scales) return fail(W4_EINVAL, "null x, codes or scales");
     if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
         return fail(W4_EALIGN, "x, codes and scales must be 16-byte aligned");
-    return hip_status(w4::launch_kv_quantize(x, n, Hkv, pos, T_max, codes, scales, (hipStream_t)stream),
+    return hip_status(w4::launch_kv_quantize(&x, 1, n, Hkv, pos, T_max, &codes, &scales,
+                                             (hipStream_t)stream),
                       "kv_quantize launch");
+}
+
+int w4_kv_append(const float* k, const float* v, int64_t n, int64_t Hkv, int64_t pos,
+                 int64_t T_max, uint8_t* k_codes, float* k_scales, uint8_t* v_codes,
+                 float* v_scales, void* stream) {
+    int rc = kv_check_append(n, Hkv, pos, T_max);
+    if (rc) return rc;
+    if (n == 0) return ok();
+    if (!k || !v || !k_codes || !k_scales || !v_codes || !v_scales)
+        return fail(W4_EINVAL, "null k, v, codes or scales");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_codes) || !aligned16(k_scales) ||
+        !aligned16(v_codes) || !aligned16(v_scales))
+        return fail(W4_EALIGN, "k, v, codes and scales must be 16-byte aligned");
+    const float* x[2] = {k, v};
+    uint8_t* c[2] = {k_codes, v_codes};
+    float* s[2] = {k_scales, v_scales};
+    return hip_status(w4::launch_kv_quantize(x, 2, n, Hkv, pos, T_max, c, s, (hipStream_t)stream),
+                      "kv_append launch");
 }
 
 int w4_kv_scores(const float* q, int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max,

@@ -25,14 +25,25 @@ namespace w4 {
 
 // ---------------------------------------------------------------- quantize
 // One wavefront per head vector: lane l holds elements 2l and 2l + 1, the
-// wavefront's max |v| comes from a butterfly, and lane l writes byte l.
-__global__ __launch_bounds__(256) void kv_quantize_kernel(const float* __restrict__ x, int nvec,
-                                                          int H, int64_t pos, int64_t T_max,
-                                                          uint8_t* __restrict__ codes,
-                                                          float* __restrict__ scales) {
+// wavefront's max |v| comes from a butterfly, and lane l writes byte l. A
+// launch serves one cache, or two (the keys' and the values' of the same
+// positions: vectors nvec .. 2 nvec - 1 go to the second).
+struct KvAppend {
+    const float* x[2];
+    uint8_t* codes[2];
+    float* scales[2];
+};
+
+__global__ __launch_bounds__(256) void kv_quantize_kernel(KvAppend a, int ncache, int nvec, int H,
+                                                          int64_t pos, int64_t T_max) {
     const int lane = threadIdx.x & 63;
-    const int v = blockIdx.x * 4 + (threadIdx.x >> 6);  // vector index n * H + h
-    if (v >= nvec) return;                                // whole wavefront
+    int v = blockIdx.x * 4 + (threadIdx.x >> 6);  // vector index (cache, n * H + h)
+    if (v >= ncache * nvec) return;               // whole wavefront
+    const int cache = v >= nvec ? 1 : 0;
+    v -= cache * nvec;
+    const float* __restrict__ x = a.x[cache];
+    uint8_t* __restrict__ codes = a.codes[cache];
+    float* __restrict__ scales = a.scales[cache];
     const float2 e = reinterpret_cast<const float2*>(x + (int64_t)v * kKvHeadDim)[lane];
     float m = fmaxf(fabsf(e.x), fabsf(e.y));
 #pragma unroll
@@ -252,11 +263,19 @@ __global__ __launch_bounds__(256) void kv_wsum_add_kernel(const float* __restric
 // ---------------------------------------------------------------- host side
 int kv_chunks(int64_t T) { return (int)((T + kKvChunk - 1) / kKvChunk); }
 
-hipError_t launch_kv_quantize(const float* x, int64_t n, int64_t H, int64_t pos, int64_t T_max,
-                              uint8_t* codes, float* scales, hipStream_t st) {
+hipError_t launch_kv_quantize(const float* const* x, int ncache, int64_t n, int64_t H,
+                              int64_t pos, int64_t T_max, uint8_t* const* codes,
+                              float* const* scales, hipStream_t st) {
     const int nvec = (int)(n * H);
-    hipLaunchKernelGGL(kv_quantize_kernel, dim3((unsigned)((nvec + 3) / 4)), dim3(256), 0, st, x,
-                       nvec, (int)H, pos, T_max, codes, scales);
+    KvAppend a{};
+    for (int i = 0; i < ncache; ++i) {
+        a.x[i] = x[i];
+        a.codes[i] = codes[i];
+        a.scales[i] = scales[i];
+    }
+    const int total = ncache * nvec;
+    hipLaunchKernelGGL(kv_quantize_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, st, a,
+                       ncache, nvec, (int)H, pos, T_max);
     return hipGetLastError();
 }
 

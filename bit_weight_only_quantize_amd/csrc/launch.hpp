@@ -92,8 +92,9 @@ hipError_t launch_moe_logits(int scheme, const MoeMats& W, const uint16_t* x, in
 
 // ---- INT4 KV cache (head vectors of kKvHeadDim values)
 int kv_chunks(int64_t T);  // position chunks of the weighted sum (partials per head)
-hipError_t launch_kv_quantize(const float* x, int64_t n, int64_t H, int64_t pos, int64_t T_max,
-                              uint8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_kv_quantize(const float* const* x, int ncache, int64_t n, int64_t H,
+                              int64_t pos, int64_t T_max, uint8_t* const* codes,
+                              float* const* scales, hipStream_t st);
 hipError_t launch_kv_scores(const float* q, int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max,
                             const uint8_t* codes, const float* scales, float* scores,
                             hipStream_t st);

@@ -233,6 +233,16 @@ int w4_kv_quantize(const float* x, int64_t n, int64_t Hkv, int64_t pos, int64_t 
                    uint8_t* codes, float* scales, void* stream);
 
 /*
+ * The same for the keys and the values of the same positions in one launch
+ * ([Shimmy] §3.2: K and V are quantized on append): k, v fp32
+ * [n][Hkv][W4_KV_HEAD_DIM] into their own caches of one shape. Results equal two
+ * w4_kv_quantize calls bit for bit.
+ */
+int w4_kv_append(const float* k, const float* v, int64_t n, int64_t Hkv, int64_t pos,
+                 int64_t T_max, uint8_t* k_codes, float* k_scales, uint8_t* v_codes,
+                 float* v_scales, void* stream);
+
+/*
  * scores[h][t] = sum_i q[h][i] * k[t][i] for the first T cached positions, with
  * the dequantization fused into the product ([Shimmy] §3.2: the shader
  * dequantizes while it computes the attention scores). q fp32 [Hq][D]; scores

@@ -107,6 +107,10 @@ def test_kv_argument_validation_without_a_device():
     assert L.w4_kv_quantize(16, 2, 4, 7, 8, 16, 16, None) == -2                  # past T_max
     assert L.w4_kv_quantize(None, 1, 4, 0, 8, 16, 16, None) == -1
     assert L.w4_kv_quantize(8, 1, 4, 0, 8, 16, 16, None) == -3
+    assert L.w4_kv_append(16, 16, 0, 4, 0, 8, 16, 16, 16, 16, None) == 0         # n == 0: no-op
+    assert L.w4_kv_append(16, 16, 2, 4, 7, 8, 16, 16, 16, 16, None) == -2
+    assert L.w4_kv_append(16, None, 1, 4, 0, 8, 16, 16, 16, 16, None) == -1
+    assert L.w4_kv_append(16, 16, 1, 4, 0, 8, 16, 16, 24, 16, None) == -3
     assert L.w4_kv_scores(16, 6, 4, 10, 16, 16, 16, 16, None) == -2              # 6 heads over 4
     assert L.w4_kv_scores(16, 8, 4, 17, 16, 16, 16, 16, None) == -2              # T > T_max
     assert L.w4_kv_scores(16, 8, 4, 0, 16, 16, 16, 16, None) == 0                # T == 0: no-op

@@ -84,6 +84,25 @@ def test_kv_scores_and_weighted_sum_match_oracle(Hq, Hkv, T, T_max):
     assert np.array_equal(out, out2) and np.array_equal(sc, sc2)      # deterministic
 
 
+def test_kv_append_equals_two_quantize_calls():
+    n, Hkv, pos, T_max = 3, 8, 5, 12
+    k = _vectors((n, Hkv, D), "kva.k")
+    v = _vectors((n, Hkv, D), "kva.v", seed=1)
+    kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    kc, vc = w4.kv_cache(Hkv, T_max), w4.kv_cache(Hkv, T_max)
+    kc2, vc2 = w4.kv_cache(Hkv, T_max), w4.kv_cache(Hkv, T_max)
+    for t in kc + vc + kc2 + vc2:
+        t.zero_()
+    w4.kv_append(kd, vd, kc, vc, pos)
+    w4.kv_quantize(kd, kc2[0], kc2[1], pos)
+    w4.kv_quantize(vd, vc2[0], vc2[1], pos)
+    for a, b in zip(kc + vc, kc2 + vc2):
+        assert torch.equal(a, b)
+    c_ref, s_ref = oracle.kv_quantize(np.ascontiguousarray(v.transpose(1, 0, 2)))
+    assert np.array_equal(vc[0].cpu().numpy()[:, pos:pos + n], c_ref)
+    assert np.array_equal(vc[1].cpu().numpy()[:, pos:pos + n].view(np.uint32), s_ref.view(np.uint32))
+
+
 def test_kv_quantize_then_read_back():
     """The device codec feeds the device products: quantize K on the GPU, score
     one-hot queries, and read the dequantized cache back element by element."""
