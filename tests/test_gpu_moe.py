@@ -102,6 +102,15 @@ def test_moe_gemma_shaped_layer(M):
     _moe_case(M, 128, 2048, 768, 2048, 8, "aff4_g64", 0, "gemma")
 
 
+@pytest.mark.parametrize("M,E,D,F,Fs,k", [
+    (256, 64, 512, 256, 512, 8),    # the most tokens: 2048 pairs, experts with > 8 pairs in several descriptors
+    (256, 32, 256, 128, 0, 32),     # the most slots: 8192 pairs (the bucketing limit), no shared expert
+    (64, 128, 2048, 768, 2048, 8),  # Gemma-shaped, twice the bench's decode batch
+])
+def test_moe_largest_batches(M, E, D, F, Fs, k):
+    _moe_case(M, E, D, F, Fs, k, "aff4_g64", 5, f"big.{M}.{E}.{k}")
+
+
 @pytest.mark.parametrize("scheme", ["sym4_g128", "aff4_g64"])
 def test_moe_small_ragged_and_edge_ids(scheme):
     E, D, F, M, k = 16, 256, 384, 5, 3
