@@ -113,7 +113,7 @@ __global__ __launch_bounds__(64 * RW) void moe1_gate_up_kernel(Moe1Args a) {
             }
             __syncthreads();
             e = sel_id[slot];
-            if (bid == 0 && threadIdx.x < a.k) {
+            if (bid == 0 && (int)threadIdx.x < a.k) {
                 a.ids_out[threadIdx.x] = sel_id[threadIdx.x];
                 a.wts_out[threadIdx.x] = sel_w[threadIdx.x];
             }
