@@ -38,6 +38,7 @@ LLAMA13B = [("wq", 5120, 5120), ("wk", 5120, 5120), ("wv", 5120, 5120), ("wo", 5
 
 
 GEMV_WAVE_SOURCES = ("common.hpp", "launch.hpp", "skinny.hpp", "gemv_wave.hpp", "gemv.hip")
+GEMM_SOURCES = ("common.hpp", "launch.hpp", "gemm.hip")
 
 
 def weight_bytes(scheme: str, N: int, K: int) -> int:
@@ -495,7 +496,24 @@ def run_prefill(c: Ctx, a):
                        "achieved": round(f / (t * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(f / (t * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                        "traffic": None, "flops_per_launch": f, "avg_launch_us": round(t * 1e3, 3)}
+    busy = measured_mfma_busy("gemm_prefill_2048_mfma_counters.md", GEMM_SOURCES)
+    if busy is not None:
+        out["roofline"]["mfma_busy"] = busy
     return out
+
+
+def measured_mfma_busy(profile, files):
+    """Fraction of SIMD-cycles the matrix cores were busy in the gate/up GEMM, from a
+    committed counter summary (`mfma_busy_gate_up: <f> sources_sha256: <hex>`), or
+    None when it is missing or the kernel has changed since."""
+    try:
+        text = open(os.path.join(ROOT, "profiles", profile)).read()
+    except OSError:
+        return None
+    m = __import__("re").search(r"mfma_busy_gate_up:\s*([0-9.]+)\s+sources_sha256:\s*([0-9a-f]{64})", text)
+    if not m or m.group(2) != kernel_sources_digest(files):
+        return None
+    return float(m.group(1))
 
 
 # ---------------------------------------------------------------- single GEMV
