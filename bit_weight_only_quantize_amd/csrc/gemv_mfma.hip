@@ -174,6 +174,22 @@ static bool try_mfma_lds(int count, const void* const* codes, const void* const*
                 return;
             }
         }
+        // 12 or more tokens: 8 staging loads in flight per lane (the 7B stack
+        // at M = 16: +3.6%; at M = 4 it cost 2%). The registers only allow it
+        // with scale blocks of up to 32 groups and without the affine 4-bit
+        // regrouping (those variants spill)
+        if constexpr (G <= 32 && S != AFF4_G64) {
+            if (M >= 12) {
+                if (P.KP > 1) {
+                    if (P.spw >= 4) go(gemv_mfma_lds_kernel<S, 4, G, false, true, 8>);
+                    else go(gemv_mfma_lds_kernel<S, 2, G, false, true, 8>);
+                } else {
+                    if (P.spw >= 4) go(gemv_mfma_lds_kernel<S, 4, G, false, false, 8>);
+                    else go(gemv_mfma_lds_kernel<S, 2, G, false, false, 8>);
+                }
+                return;
+            }
+        }
         if (P.KP > 1) {
             if (P.spw >= 4) go(gemv_mfma_lds_kernel<S, 4, G, false, true>);
             else go(gemv_mfma_lds_kernel<S, 2, G, false, true>);

@@ -416,7 +416,7 @@ __device__ __forceinline__ int lds_swz(int mp, int lr) {
 // tile, as one chunk, and writes its partial outputs to part + p * M * N
 // ([M][N]). A template switch, so that the other launches keep constant
 // chunk offsets.
-template <int S, int DEPTH, int SGMAX, bool CHUNKED, bool PARTS = false>
+template <int S, int DEPTH, int SGMAX, bool CHUNKED, bool PARTS = false, int UW = 4>
 __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, int K, int M,
                                                               const uint16_t* x, int tiles,
                                                               int TP, int WK, int CS, int KP,
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
     using P = MfmaStep<S>;
     constexpr int GPS = P::GPS;
     constexpr int NV = T::GROUP / 8;  // 16-byte activation vectors per group
-    constexpr int U = CHUNKED ? 2 : 4;  // staging vectors in flight per lane (registers)
+    constexpr int U = CHUNKED ? 2 : UW;  // staging vectors in flight per lane (registers)
     constexpr uint32_t ONE2 = 0x3F803F80u;
     const int NT = blockDim.x;
     extern __shared__ __align__(16) uint32_t lds[];
