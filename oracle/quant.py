@@ -18,7 +18,7 @@ Readings where the pages are silent (each a single line below):
   * zero-range guard: scale >= 1e-8 for both schemes ([airllm] §4.2 clamps sym).
   * groups run along K inside one row of W[N][K] ([airllm] §2.1 "consecutive").
   * packing: element 2j in the low nibble of byte j, element 2j+1 in the high
-    nibble ([airllm] §4.2 packs q[0::2] low and q[1::2] high).
+    nibble ([airllm] §4.2 puts the even-indexed code of a pair low).
 """
 from __future__ import annotations
 
@@ -48,56 +48,71 @@ def bf16_to_f32(bits) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- quantizers
-def _groups(W: np.ndarray, g: int) -> np.ndarray:
+def _check(W: np.ndarray, g: int) -> np.ndarray:
     W = np.asarray(W)
-    if W.dtype != np.float32:
-        raise TypeError("weights must be fp32")
-    N, K = W.shape
-    if K % g != 0:
-        raise ValueError(f"K={K} is not a multiple of the group size {g}")
-    return W.reshape(N, K // g, g)
+    if W.dtype != np.float32 or W.ndim != 2:
+        raise TypeError("weights must be a 2-D fp32 array")
+    if W.shape[1] % g != 0:
+        raise ValueError(f"K={W.shape[1]} is not a multiple of the group size {g}")
+    return W
 
 
 def quantize_sym4(W: np.ndarray):
-    """Symmetric 4-bit, group 128, following [airllm] §4.2 (group_quantize, bits=4).
+    """Symmetric 4-bit codes with one fp32 scale per 128 consecutive weights of a
+    row ([airllm] §2.1 group size, §4.2 symmetric rule with bits = 4).
 
-    Per group of 128 consecutive weights of a row:
-      absmax a = max |w|               (exact)
-      s = a / 7                        (fp32, correctly rounded; 7 = 2^(bits-1) - 1)
-      s = max(s, 1e-8)                 (the page's clamp_min)
-      q = clamp(round_half_even(w / s), -7, 7)   (fp32 division)
+    The rule, applied to each group on its own (every row at once):
+      the scale is the group's largest magnitude divided by 7 (the largest
+      positive 4-bit code), in fp32 with correct rounding, and never below
+      1e-8 (the page's floor, which keeps an all-zero group finite);
+      a weight's code is its quotient by that scale (fp32 division), rounded
+      to the nearest integer with halves to even, then limited to [-7, 7].
     Returns (q int8 [N][K], s fp32 [N][K/128])."""
-    G = _groups(W, 128)
-    a = np.abs(G).max(axis=2)
-    s = a / np.float32(7.0)
-    s = np.maximum(s, SCALE_FLOOR).astype(np.float32)
-    q = np.rint(G / s[:, :, None])
-    q = np.clip(q, -7, 7).astype(np.int8)
-    return q.reshape(W.shape), s
+    W = _check(W, 128)
+    N, K = W.shape
+    q = np.empty((N, K), dtype=np.int8)
+    s = np.empty((N, K // 128), dtype=np.float32)
+    for j in range(K // 128):
+        cols = slice(128 * j, 128 * (j + 1))
+        grp = W[:, cols]                                    # group j of every row
+        peak = np.max(np.abs(grp), axis=1)                  # exact in fp32
+        sj = np.maximum(peak / np.float32(7.0), SCALE_FLOOR).astype(np.float32)
+        codes = np.rint(grp / sj[:, None])                  # fp32 quotient, halves to even
+        q[:, cols] = np.clip(codes, -7, 7)
+        s[:, j] = sj
+    return q, s
 
 
 def quantize_affine(W: np.ndarray, bits: int):
-    """Affine b-bit, group 64, bf16 scale + bf16 bias ([TurboFieldfare] "量化和精度").
+    """Affine b-bit codes with one bf16 scale and one bf16 bias per 64 weights of a
+    row ([TurboFieldfare] "量化和精度": 4-bit, group 64, bf16 scale + bf16 bias;
+    the router uses 8 bits).
 
-    The page fixes only the format; the rule is the plain min/max reading:
-      mn, mx = min w, max w            (exact)
-      s32 = max((mx - mn) / (2^b - 1), 1e-8)   (fp32 subtract, fp32 divide)
-      s = bf16(s32), b = bf16(mn)      (round to nearest even)
-      q = clamp(round_half_even((w - b) / s), 0, 2^b - 1)  (fp32, using the stored bf16 values)
-    so that w is approximated by s*q + b.
+    The page fixes only the format; the rule is the plain min/max reading, per group:
+      the scale spans the group's range over the 2^b - 1 code steps
+      ((max - min) / (2^b - 1) in fp32, floored at 1e-8) and the bias is the
+      group minimum; both are stored as bf16 (nearest, ties to even);
+      a weight's code is (w - bias) / scale computed in fp32 from the STORED
+      bf16 values, rounded half to even and limited to [0, 2^b - 1],
+    so that a weight reads back as scale * code + bias.
     Returns (q uint8 [N][K], s bf16 bits [N][K/64], b bf16 bits [N][K/64])."""
-    G = _groups(W, 64)
-    levels = np.float32(2 ** bits - 1)
-    mn = G.min(axis=2)
-    mx = G.max(axis=2)
-    s32 = np.maximum((mx - mn) / levels, SCALE_FLOOR).astype(np.float32)
-    s_b = bf16_round(s32)
-    b_b = bf16_round(mn)
-    sf = bf16_to_f32(s_b)[:, :, None]
-    bf = bf16_to_f32(b_b)[:, :, None]
-    q = np.rint((G - bf) / sf)
-    q = np.clip(q, 0, 2 ** bits - 1).astype(np.uint8)
-    return q.reshape(W.shape), s_b, b_b
+    W = _check(W, 64)
+    N, K = W.shape
+    top = np.float32(2 ** bits - 1)
+    q = np.empty((N, K), dtype=np.uint8)
+    s_b = np.empty((N, K // 64), dtype=np.uint16)
+    b_b = np.empty((N, K // 64), dtype=np.uint16)
+    for j in range(K // 64):
+        cols = slice(64 * j, 64 * (j + 1))
+        grp = W[:, cols]
+        lo, hi = grp.min(axis=1), grp.max(axis=1)
+        step = np.maximum((hi - lo) / top, SCALE_FLOOR).astype(np.float32)
+        s_b[:, j] = bf16_round(step)
+        b_b[:, j] = bf16_round(lo)
+        sf = bf16_to_f32(s_b[:, j])[:, None]
+        bf = bf16_to_f32(b_b[:, j])[:, None]
+        q[:, cols] = np.clip(np.rint((grp - bf) / sf), 0, 2 ** bits - 1)
+    return q, s_b, b_b
 
 
 def quantize(W: np.ndarray, scheme: str):
@@ -116,14 +131,17 @@ def quantize(W: np.ndarray, scheme: str):
 def pack(q: np.ndarray, bits: int) -> np.ndarray:
     """Integer codes [N][K] -> bytes.
 
-    4-bit: byte j of a row = (code[2j] & 0xF) | (code[2j+1] & 0xF) << 4, the
-    nibble of a negative code being its two's complement ([airllm] §4.2).
+    4-bit: two codes share a byte; of the pair (element 2j, element 2j + 1) the
+    first goes to the low nibble and the second to the high nibble, a negative
+    code being stored as its 4-bit two's complement ([airllm] §4.2).
     8-bit: one code per byte."""
     q = np.asarray(q)
     if bits == 8:
         return q.astype(np.uint8).copy()
-    nib = (q.astype(np.int16) & 0xF).astype(np.uint8)
-    return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    N, K = q.shape
+    pairs = (q.astype(np.int16) & 0xF).astype(np.uint8).reshape(N, K // 2, 2)
+    first, second = pairs[:, :, 0], pairs[:, :, 1]
+    return (first | (second << 4)).astype(np.uint8)
 
 
 def unpack(packed: np.ndarray, bits: int, signed: bool) -> np.ndarray:

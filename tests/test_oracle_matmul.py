@@ -96,3 +96,47 @@ def test_linearity_and_tolerance_scale():
     assert np.array_equal(abs_matmul_f64(x, Wd), S)
     yr, _ = gemv_reference(c, s, b, "sym4_g128", x, rows=[3, 17])
     assert np.array_equal(yr, y[:, [3, 17]])
+
+
+def _toy(scheme, seed):
+    """Mixed-sign dyadic toy: integer codes, power-of-two scales, dyadic biases
+    (affine), signed small-integer activations; every product and partial sum is
+    exact in fp64."""
+    rng = np.random.default_rng(seed)
+    if scheme == "sym4_g128":
+        g, K = 128, 256
+        q = rng.integers(-7, 8, size=(8, K))
+        s = np.array([[2.0 ** -(3 + (n + j) % 4) for j in range(K // g)] for n in range(8)], np.float32)
+        return q, s, None, rng.integers(-3, 4, size=(2, K)), g
+    g, K = 64, 192
+    q = rng.integers(0, 16, size=(8, K))
+    s = np.array([[2.0 ** -(4 + (n + j) % 3) for j in range(K // g)] for n in range(8)], np.float32)
+    b = np.array([[(n - 3 - j) * 2.0 ** -5 for j in range(K // g)] for n in range(8)], np.float32)
+    return q, s, b, rng.integers(-4, 5, size=(2, K)), g
+
+
+@pytest.mark.parametrize("scheme", ["sym4_g128", "aff4_g64"])
+def test_tolerance_scale_is_the_exact_sum_of_absolute_products(scheme):
+    """S[m][n] = sum_k |w'[n][k]| |x[m][k]|, computed here in exact rationals from
+    the integer codes, scales and biases. A mistaken S such as (sum|x|)(sum|w|),
+    sum|w x| without the absolute values, or a transposed product fails."""
+    q, s, b, x, g = _toy(scheme, 31)
+    if scheme == "sym4_g128":
+        codes, sc, bi = pack(q, 4), s, None
+    else:
+        codes = pack(q, 4)
+        sc = (s.view(np.uint32) >> 16).astype(np.uint16)
+        bi = (b.view(np.uint32) >> 16).astype(np.uint16)
+    xb = _bf16_bits_of_small_ints(x)
+    y, S = gemv_reference(codes, sc, bi, scheme, xb)
+    for m in range(2):
+        for n in range(8):
+            exact = Fraction(0)
+            for k in range(q.shape[1]):
+                w = Fraction(float(s[n][k // g])) * int(q[n][k])
+                if b is not None:
+                    w += Fraction(float(b[n][k // g]))
+                exact += abs(w) * abs(int(x[m][k]))
+            assert Fraction(float(S[m, n])) == exact, (m, n)
+    # the scale of a product with cancelling terms exceeds |y| strictly
+    assert np.any(S > np.abs(y))

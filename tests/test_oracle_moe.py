@@ -122,3 +122,40 @@ def test_ffn_h_is_bf16_of_gelu_gate_times_up():
     exact = gelu_tanh(g) * u
     assert np.all(np.abs(hv - exact) <= np.abs(exact) * 2.0 ** -8 + 1e-30)
     assert np.allclose(y, matmul_f64(h, dequantize(*trip[2], "aff4_g64")), rtol=0, atol=0)
+
+
+def test_moe_tolerance_scale_is_the_weighted_sum_of_each_down_product():
+    """moe_sparse's S[m][n] = sum_j p[m][j] sum_f |W_down[e_j][n][f]| |h_j[f]| plus the
+    shared expert's sum_f |W_sd[n][f]| |hs[f]|, recomputed here in exact rationals
+    from the dequantized down matrices and the bf16 h of each (token, expert).
+    Fixed ids and dyadic p; an expert id outside [0, E) adds nothing."""
+    from fractions import Fraction
+    E, D, F, Fs, M = 3, 64, 64, 64, 2
+    gate, up, down = _stack(E, F, D, 5, "sg"), _stack(E, F, D, 5, "su"), _stack(E, D, F, 5, "sd")
+    shared = tuple(quantize_pack(synth.weights(n, kk, 0.02, 5, nm), "aff4_g64")
+                   for n, kk, nm in ((Fs, D, "ssg"), (Fs, D, "ssu"), (D, Fs, "ssd")))
+    x = synth.activations_bf16(M, D, 5, "sx")
+    ids = np.array([[2, 0, -1], [1, 2, 5]], dtype=np.int32)
+    p = np.array([[0.5, 0.25, 0.125], [0.375, 0.0625, 0.5]])
+    y, S = moe_sparse(x, ids, p, gate, up, down, shared)
+    for m in range(M):
+        terms = []                      # (weight, dequantized down matrix, h row)
+        for j in range(3):
+            e = int(ids[m, j])
+            if not 0 <= e < E:
+                continue
+            g_e = (gate[0][e], gate[1][e], gate[2][e])
+            u_e = (up[0][e], up[1][e], up[2][e])
+            d_e = (down[0][e], down[1][e], down[2][e])
+            _, _, h = ffn(x[m:m + 1], g_e, u_e, d_e, "aff4_g64")
+            terms.append((Fraction(float(p[m, j])), dequantize(*d_e, "aff4_g64"), h[0]))
+        _, _, hs = ffn(x[m:m + 1], *shared, "aff4_g64")
+        terms.append((Fraction(1), dequantize(*shared[2], "aff4_g64"), hs[0]))
+        for n in range(0, D, 7):
+            exact = Fraction(0)
+            for w, Wd, h in terms:
+                hv = bf16_to_f32(h).astype(np.float64)
+                exact += w * sum(abs(Fraction(float(Wd[n, f]))) * abs(Fraction(float(hv[f])))
+                                 for f in range(Wd.shape[1]))
+            assert abs(Fraction(float(S[m, n])) - exact) <= exact * Fraction(1, 10 ** 12), (m, n)
+            assert S[m, n] >= abs(y[m, n])

@@ -1,8 +1,8 @@
 """Pins for the oracle's packing (CPU only).
 
 Low-nibble-first packing of two 4-bit codes per byte follows the airllm
-article §4.2 (q[0::2] into the low nibble, q[1::2] shifted into the high one);
-negative codes are stored as their two's-complement nibble (& 0x0F)."""
+article §4.2: of each pair of neighbouring codes the even-indexed one takes the
+low nibble; negative codes are stored as their 4-bit two's complement."""
 import numpy as np
 import pytest
 
