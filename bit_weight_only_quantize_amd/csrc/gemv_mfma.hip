@@ -38,19 +38,6 @@ static void go_mfma(const GemvGroupArgs& a, int blocks, int K, int M, const uint
     }
 }
 
-template <int S>
-static void pick_mfma(int RT, int WK, const GemvGroupArgs& a, int blocks, int K, int M,
-                      const uint16_t* x, hipStream_t st) {
-    if (RT == 2) {
-        if (WK == 8) go_mfma<S, 2, 8>(a, blocks, K, M, x, st);
-        else if (WK == 4) go_mfma<S, 2, 4>(a, blocks, K, M, x, st);
-        else go_mfma<S, 2, 2>(a, blocks, K, M, x, st);
-    } else {
-        if (WK == 8) go_mfma<S, 1, 8>(a, blocks, K, M, x, st);
-        else go_mfma<S, 1, 4>(a, blocks, K, M, x, st);
-    }
-}
-
 // Activations in LDS (gemv_mfma_lds_kernel): one workgroup per CU holds TP =
 // ceil(tiles / CUs) tiles; 16 wavefronts stage x (in as few chunks of steps
 // as LDS allows), and TP * WK of them stream codes, each tile's steps split
@@ -234,18 +221,12 @@ hipError_t launch_gemv_mfma(int scheme, int count, const void* const* codes,
     if (scheme == SYM4_G128 ? try_mfma_lds<SYM4_G128>(count, codes, scale, bias, N, K, x, M, y, part, st)
                             : try_mfma_lds<AFF4_G64>(count, codes, scale, bias, N, K, x, M, y, part, st))
         return hipGetLastError();
-    int64_t total_rows = 0;
-    for (int i = 0; i < count; ++i) total_rows += N[i];
     // The split-K kernel takes what the LDS kernel does not: more than 16 row
-    // tiles per CU (the 13B tied head) and launches too small for one
-    // workgroup of staging lanes. Measured on the 7B (sym) and 13B (affine)
-    // decode shapes at M = 4, 8, 16: two row tiles per wavefront amortize the
-    // activation loads once a launch has many rows (four do not pay); such
-    // launches run best with fewer split-K wavefronts (sym 2, affine 4),
-    // while eight give the smaller launches enough loads in flight.
-    const bool big = scheme == AFF4_G64 || total_rows >= 16384;
-    const int RT = big ? 2 : 1;
-    const int WK = big ? (scheme == SYM4_G128 ? 2 : 4) : 8;
+    // tiles per CU, i.e. more than 65536 rows (the 13B tied head). Measured on
+    // the 13B head and the 7B/13B decode shapes at M = 4, 8, 16: two row tiles
+    // per wavefront amortize the activation loads over that many rows (four do
+    // not pay), with two split-K wavefronts for sym and four for affine.
+    constexpr int RT = 2;
     GemvGroupArgs a{};
     int blocks = 0;
     for (int i = 0; i < count; ++i) {
@@ -260,8 +241,8 @@ hipError_t launch_gemv_mfma(int scheme, int count, const void* const* codes,
     a.tile_start[count] = blocks;
     a.count = count;
     if (blocks == 0) return hipSuccess;
-    if (scheme == SYM4_G128) pick_mfma<SYM4_G128>(RT, WK, a, blocks, (int)K, (int)M, x, st);
-    else pick_mfma<AFF4_G64>(RT, WK, a, blocks, (int)K, (int)M, x, st);
+    if (scheme == SYM4_G128) go_mfma<SYM4_G128, RT, 2>(a, blocks, (int)K, (int)M, x, st);
+    else go_mfma<AFF4_G64, RT, 4>(a, blocks, (int)K, (int)M, x, st);
     return hipGetLastError();
 }
 

@@ -42,3 +42,15 @@ def tolerance_ratio(y_gpu: np.ndarray, y_ref: np.ndarray, S: np.ndarray) -> floa
     """max over elements of |err| / (2e-3 S + 1e-5); <= 1 passes."""
     err = np.abs(y_gpu.astype(np.float64) - y_ref)
     return float((err / (TOL_REL * S + TOL_ABS)).max()) if err.size else 0.0
+
+
+U_BF16 = 2.0 ** -8   # unit roundoff of bf16 (8 significant bits, round to nearest even)
+
+
+def tolerance_ratio_bf16_out(y_gpu: np.ndarray, y_ref: np.ndarray, S: np.ndarray) -> float:
+    """The same check for a result stored as bf16. Rounding the result y^ to bf16
+    moves it by at most U_BF16 |y^|, and |y^| <= |y| + e with e within the fp32
+    bound, so |bf16(y^) - y| <= (1 + U_BF16)(2e-3 S + 1e-5) + U_BF16 |y|; <= 1 passes."""
+    err = np.abs(y_gpu.astype(np.float64) - y_ref)
+    bound = (1 + U_BF16) * (TOL_REL * S + TOL_ABS) + U_BF16 * np.abs(y_ref)
+    return float((err / bound).max()) if err.size else 0.0

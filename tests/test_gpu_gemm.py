@@ -1,7 +1,9 @@
 """GPU parity for the prefill GEMM (airllm article §3.3: prefill is the
 compute-dense phase): Y = X · dequant(W)^T with bf16 output, per element within
-2e-3·sum|w||x| + 1e-5 of the oracle's fp64 product, on ragged small shapes and
-on sampled rows and columns of the two prefill shapes."""
+2e-3·sum|w||x| + 1e-5 of the oracle's fp64 product plus the rounding of the
+bf16 result itself (2^-8 of its magnitude), on ragged small shapes, same-sign
+inputs (where |y| = sum|w||x|) and sampled rows and columns of the two prefill
+shapes."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +11,7 @@ import torch
 import bit_weight_only_quantize_amd as w4
 import oracle
 import synth
-from gpu_util import dev_bf16, dev_f32, host_bits16, tolerance_ratio
+from gpu_util import dev_bf16, dev_f32, host_bits16, tolerance_ratio_bf16_out
 
 pytestmark = pytest.mark.gpu
 
@@ -18,10 +20,15 @@ def _bf16_to_f64(bits):
     return oracle.bf16_to_f32(bits).astype(np.float64)
 
 
-def _case(scheme, M, N, K, name, rows=None, cols=None):
-    print(f"[gemm] {name} {scheme} M={M} N={N} K={K}", flush=True)
+def _case(scheme, M, N, K, name, rows=None, cols=None, same_sign=False):
+    print(f"[gemm] {name} {scheme} M={M} N={N} K={K} same_sign={same_sign}", flush=True)
     W = synth.weights(N, K, 0.02, seed=0, name=name)
     X = synth.activations_bf16(M, K, seed=0, name=name + ".X")
+    if same_sign:
+        # |x| and |w| + 0.01: every product is >= 0 (affine biases are then
+        # positive too), so y = sum|w||x| and no cancellation hides an error
+        X = X & np.uint16(0x7FFF)
+        W = np.abs(W) + np.float32(0.01)
     c, s, b = oracle.quantize_pack(W, scheme)
     q = w4.quantize_pack(dev_f32(W), scheme)
     Y = _bf16_to_f64(host_bits16(w4.gemm(q, dev_bf16(X))))
@@ -29,13 +36,13 @@ def _case(scheme, M, N, K, name, rows=None, cols=None):
     worst = 0.0
     if rows is None and cols is None:
         yr, S = oracle.gemv_reference(c, s, b, scheme, X)
-        worst = tolerance_ratio(Y, yr, S)
+        worst = tolerance_ratio_bf16_out(Y, yr, S)
     if rows is not None:
         yr, S = oracle.gemv_reference(c, s, b, scheme, X[rows])
-        worst = max(worst, tolerance_ratio(Y[rows], yr, S))
+        worst = max(worst, tolerance_ratio_bf16_out(Y[rows], yr, S))
     if cols is not None:
         yr, S = oracle.gemv_reference(c, s, b, scheme, X, rows=cols)
-        worst = max(worst, tolerance_ratio(Y[:, cols], yr, S))
+        worst = max(worst, tolerance_ratio_bf16_out(Y[:, cols], yr, S))
     assert worst <= 1.0, f"worst error {worst:.3f} x tolerance"
     return q, X, Y
 
@@ -48,6 +55,12 @@ def test_gemm_small_and_ragged(scheme, M, N, K):
     if K % (128 if scheme == "sym4_g128" else 64):
         pytest.skip("K not a multiple of the group")
     _case(scheme, M, N, K, f"gemm.{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("scheme", ["sym4_g128", "aff4_g64"])
+@pytest.mark.parametrize("M,N,K", [(300, 200, 512), (256, 256, 4096), (33, 130, 1152)])
+def test_gemm_same_sign_inputs(scheme, M, N, K):
+    _case(scheme, M, N, K, f"gemm.pos.{M}x{N}x{K}", same_sign=True)
 
 
 def _samples(n, k, seed):

@@ -47,7 +47,7 @@ def _run(scheme, N, K, M, name, rows=None, quantize_on_gpu=True):
     ("aff4_g64", 520, 13824, 2),
     ("sym4_g128", 1000, 4096, 16),    # skinny MFMA path: full token tile, ragged rows
     ("aff4_g64", 333, 768, 13),
-    ("aff4_g64", 17, 64, 6),          # one k step: most split-K wavefronts get none
+    ("aff4_g64", 17, 64, 6),          # one group: a half step, activations in LDS
     ("sym4_g128", 31, 128, 11),
     ("sym4_g128", 12370, 512, 3),     # > 256 row tiles: 4 per workgroup, ragged last workgroup
     ("aff4_g64", 600, 13888, 8),      # activations staged in chunks; odd group count
@@ -127,9 +127,51 @@ def test_gemv_llama13b_shapes(N, K, mat, M):
     _run("aff4_g64", N, K, M, f"llama13b.{mat}")
 
 
-def test_gemv_head_sampled_rows():
-    rows = np.sort(np.random.default_rng(0).choice(152064, 1536, replace=False))
-    _run("aff4_g64", 152064, 5120, 1, "llama13b.head", rows=rows)
+@pytest.mark.parametrize("scheme,N,K,M", [
+    ("sym4_g128", 70000, 256, 4),     # 4375 row tiles: more than 16 per CU
+    ("aff4_g64", 66000, 192, 3),      # affine, odd group count (a half step)
+    ("sym4_g128", 65537, 384, 16),    # one row past 4096 tiles, a full token tile
+])
+def test_gemv_split_k_kernel_matches_oracle(scheme, N, K, M):
+    """Launches with more than 16 row tiles of 16 rows per CU (N > 65536) take the
+    split-K skinny kernel (K interleaved over wavefronts, two row tiles each)."""
+    assert (N + 15) // 16 > 16 * 256
+    _run(scheme, N, K, M, f"splitk.{scheme}.{N}x{K}")
+
+
+_HEAD = {}
+
+
+def _head():
+    """The 13B-shaped tied head, 152064 x 5120 affine 4-bit g64, quantized on the
+    GPU once; the oracle quantizes only the sampled rows (rows are independent)."""
+    if not _HEAD:
+        N, K = 152064, 5120
+        rows = np.sort(np.random.default_rng(0).choice(N, 1536, replace=False))
+        rows = np.unique(np.concatenate([rows, [0, 1, 15, 16, 31, N - 17, N - 2, N - 1]]))
+        W = synth.weights(N, K, 0.02, seed=0, name="llama13b.head")
+        Wd = dev_f32(W)
+        q = w4.quantize_pack(Wd, "aff4_g64")
+        del Wd
+        torch.cuda.synchronize()
+        c, s, b = oracle.quantize_pack(np.ascontiguousarray(W[rows]), "aff4_g64")
+        del W
+        assert np.array_equal(q.codes[torch.from_numpy(rows).cuda()].cpu().numpy(), c)
+        _HEAD.update(q=q, rows=rows, ref=(c, s, b))
+    return _HEAD
+
+
+@pytest.mark.parametrize("M", [1, 2, 8, 16])
+def test_gemv_head_sampled_rows(M):
+    """The tied head of the 13B-shaped stack on sampled rows (first and last
+    tiles among them); at M > 1 this is the split-K skinny kernel (9504 row tiles)."""
+    h = _head()
+    print(f"[gemv] llama13b.head 152064x5120 M={M}", flush=True)
+    x = synth.activations_bf16(M, 5120, seed=0, name=f"llama13b.head.x{M}")
+    y = w4.gemv(h["q"], dev_bf16(x)).cpu().numpy()[:, h["rows"]]
+    yr, S = oracle.gemv_reference(*h["ref"], "aff4_g64", x)
+    r = tolerance_ratio(y, yr, S)
+    assert r <= 1.0, f"worst error is {r:.3f} x tolerance"
 
 
 @pytest.mark.parametrize("ngroups", [2, 3])

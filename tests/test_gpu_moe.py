@@ -51,6 +51,7 @@ def test_route_matches_oracle(M):
     _, rids, rp, margin = oracle.route(x, c, s, b, top_k=8)
     tol_l = (TOL_REL * S + TOL_ABS).max(axis=1)
     for m in range(M):
+        assert len(set(ids[m].tolist())) == 8 and ids[m].min() >= 0 and ids[m].max() < E, m
         if margin[m] > 2 * tol_l[m]:
             assert list(ids[m]) == list(rids[m]), m
         else:  # a near tie: the GPU's set must still be a valid top-8 of the oracle's logits
