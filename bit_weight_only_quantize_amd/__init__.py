@@ -69,6 +69,8 @@ _SIGS = {
     "w4_moe_workspace_bytes": ([_I64, ctypes.c_int, _I64, _I64, _I64, _I64], ctypes.c_size_t),
     "w4a16_moe_gemv": ([ctypes.POINTER(_W4Matrix)] * 6 + [_P, _I64, _P, _P, ctypes.c_int, _P,
                                                           ctypes.c_size_t, _P, _P], ctypes.c_int),
+    "w4a16_moe_gemv_noalloc": ([ctypes.POINTER(_W4Matrix)] * 6 + [_P, _I64, _P, _P, ctypes.c_int, _P, _P],
+                               ctypes.c_int),
     "w4a16_moe_gemv_logits": ([ctypes.POINTER(_W4Matrix)] * 6 + [_P, _I64, _P, ctypes.c_int, _P, _P,
                                                                  _P, ctypes.c_size_t, _P, _P],
                               ctypes.c_int),
@@ -377,3 +379,23 @@ def kv_weighted_sum(p: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(p.device)))
     return out
+
+
+MOE_SCRATCH_BYTES = 16 << 20
+
+
+def moe_gemv_noalloc(gate: QuantizedMatrix, up: QuantizedMatrix, down: QuantizedMatrix,
+                     x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, shared=None,
+                     y: torch.Tensor = None) -> torch.Tensor:
+    """moe_gemv with the library's static per-GPU scratch as its workspace (no
+    device allocation by the library; calls overlapping on one GPU race)."""
+    x = _as_bf16_bits(x, "x")
+    M, top_k = ids.shape
+    if y is None:
+        y = torch.empty((M, gate.K), dtype=torch.float32, device=x.device)
+    descs = [m.desc() for m in (gate, up, down)]
+    sh = [s.desc() for s in shared] if shared is not None else [None, None, None]
+    refs = [ctypes.byref(d) for d in descs] + [ctypes.byref(s) if s is not None else None for s in sh]
+    _check(lib().w4a16_moe_gemv_noalloc(*refs, _ptr(x), M, _ptr(ids), _ptr(weights), top_k, _ptr(y),
+                                        _stream(x.device)))
+    return y

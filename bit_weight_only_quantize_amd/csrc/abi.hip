@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/w4a16.h"
 #include "launch.hpp"
 
@@ -317,6 +319,59 @@ int w4a16_moe_gemv(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* 
     return hip_status(w4::launch_moe(scheme, W, x, M, ids, weights, top_k, workspace, y,
                                      (hipStream_t)stream),
                       "moe_gemv launch");
+}
+
+// Library-owned workspace of w4a16_moe_gemv_noalloc: one static device array
+// per GPU. In host code `scratch` only names the symbol; its device address on
+// the current GPU comes from hipGetSymbolAddress, taken once per device on the
+// first call there and kept in moe_scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[W4_MOE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int moe_scratch_ptr(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(W4_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(W4_EINVAL, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(W4_EHIP, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return W4_OK;
+}
+}  // namespace
+
+int w4a16_moe_gemv_noalloc(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
+                           const w4_matrix* shared_gate, const w4_matrix* shared_up,
+                           const w4_matrix* shared_down, const uint16_t* x, int64_t M,
+                           const int32_t* ids, const float* weights, int top_k, float* y,
+                           void* stream) {
+    w4::MoeMats W;
+    int scheme = 0;
+    const int rc = moe_check(gate, up, down, shared_gate, shared_up, shared_down, M, top_k, W, scheme);
+    if (rc) return rc;
+    if (M == 0 || W.D == 0) return ok();
+    if (!x || !ids || !weights || !y) return fail(W4_EINVAL, "null x, ids, weights or y");
+    if (!aligned16(x) || !aligned16(ids) || !aligned16(weights) || !aligned16(y))
+        return fail(W4_EALIGN, "x, ids, weights and y must be 16-byte aligned");
+    const size_t need = w4::moe_workspace_layout(M, top_k, W.E, W.D, W.F, W.Fs).total;
+    if (need > W4_MOE_SCRATCH_BYTES)
+        return fail(W4_EWORKSPACE, "these sizes need %zu bytes of workspace; the static scratch holds %zu",
+                    need, (size_t)W4_MOE_SCRATCH_BYTES);
+    void* ws = nullptr;
+    const int sr = moe_scratch_ptr(&ws);
+    if (sr) return sr;
+    return hip_status(w4::launch_moe(scheme, W, x, M, ids, weights, top_k, ws, y, (hipStream_t)stream),
+                      "moe_gemv_noalloc launch");
 }
 
 int w4a16_moe_gemv_logits(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,

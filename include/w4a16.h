@@ -29,7 +29,8 @@
  *   - Activations are bf16 (raw uint16 bit patterns), row-major [M][K].
  *   - Every pointer except those documented as host pointers is a DEVICE pointer.
  *     The caller owns every buffer; the library never allocates, frees or keeps a
- *     pointer after the call returns. Work is enqueued on `stream` (a hipStream_t
+ *     pointer after the call returns (w4a16_moe_gemv_noalloc works in a static
+ *     array of the library's own instead of a caller workspace). Work is enqueued on `stream` (a hipStream_t
  *     passed as void*, NULL = the default stream); no call synchronizes the device.
  *   - Device pointers must be 16-byte aligned (W4_EALIGN otherwise).
  *   - Arguments are validated on the host before anything is enqueued; on error
@@ -189,6 +190,25 @@ int w4a16_moe_gemv(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* 
                    const w4_matrix* shared_down,
                    const uint16_t* x, int64_t M, const int32_t* ids, const float* weights,
                    int top_k, void* workspace, size_t workspace_bytes, float* y, void* stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. w4a16_moe_gemv with the
+ * same arguments, results and errors, except that its workspace is a
+ * library-owned static device array of W4_MOE_SCRATCH_BYTES per GPU (set up on
+ * the first call on each device and held until the process ends) instead of a
+ * caller buffer. The call allocates nothing. W4_EWORKSPACE when the sizes need
+ * more than W4_MOE_SCRATCH_BYTES (w4_moe_workspace_bytes gives the need).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (e.g. on two streams) race and must be serialized by the caller. Nothing in
+ * it needs to start at zero; its contents between calls are unspecified.
+ */
+#define W4_MOE_SCRATCH_BYTES ((size_t)16 << 20)
+int w4a16_moe_gemv_noalloc(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
+                           const w4_matrix* shared_gate, const w4_matrix* shared_up,
+                           const w4_matrix* shared_down,
+                           const uint16_t* x, int64_t M, const int32_t* ids, const float* weights,
+                           int top_k, float* y, void* stream);
 
 /*
  * Router selection and the MoE FFN in one call, from router logits computed

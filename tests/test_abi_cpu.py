@@ -129,3 +129,20 @@ def test_quantize_argument_validation_without_a_device():
     assert L.w4_quantize_pack(1, 16, 4, 64, 16, 16, None, None) == -1   # affine without bias
     assert L.w4_quantize_pack(0, 24, 4, 128, 16, 16, None, None) == -3
     assert L.w4_quantize_pack(5, 16, 4, 128, 16, 16, None, None) == -1
+
+
+def test_moe_noalloc_validation_without_a_device():
+    """The allocation-free MoE entry point refuses, before any device call, sizes
+    whose workspace exceeds its static scratch; M == 0 is a no-op."""
+    L = w4.lib()
+    E, D, F, Fs = 128, 2048, 768, 2048
+    gate, up = _desc(1, F, D, E=E), _desc(1, F, D, E=E)
+    down = _desc(1, D, F, E=E)
+    sg, su, sd = _desc(1, Fs, D), _desc(1, Fs, D), _desc(1, D, Fs)
+    args = [ctypes.byref(m) for m in (gate, up, down, sg, su, sd)]
+    assert L.w4a16_moe_gemv_noalloc(*args, 16, 0, 16, 16, 8, 16, None) == 0
+    assert L.w4_moe_workspace_bytes(256, 8, E, D, F, Fs) > w4.MOE_SCRATCH_BYTES
+    assert L.w4a16_moe_gemv_noalloc(*args, 16, 256, 16, 16, 8, 16, None) == -5
+    assert b"static scratch" in L.w4_last_error()
+    assert L.w4a16_moe_gemv_noalloc(*args, 16, 257, 16, 16, 8, 16, None) == -2
+    assert L.w4a16_moe_gemv_noalloc(*args, 16, 4, None, 16, 8, 16, None) == -1
