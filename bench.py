@@ -71,6 +71,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU oracle time budget")
+    ap.add_argument("--moe-path", default="layer", choices=["layer", "single", "launches"],
+                    help="moe26b: w4a16_moe_layer with its default dispatch, w4a16_moe_layer with "
+                         "the single launch for one token, or the router GEMV + "
+                         "w4a16_moe_gemv_logits calls")
     ap.add_argument("--dominant-only", action="store_true",
                     help="only replay the dominant kernel (for counter collection)")
     return ap.parse_args()
@@ -92,6 +96,17 @@ class Ctx:
     def quant(self, N, K, scheme, name, out=None, expert=None):
         W = self.synth.device_weights(N, K, 0.02, 0, name, self.dev)
         q = self.w4.quantize_pack(W, scheme, out=out, expert=expert)
+        del W
+        return q
+
+    def quant_stack(self, E, N, K, scheme, name):
+        """E experts of N x K drawn as one [E*N][K] matrix and quantized in one launch:
+        the [E][N][...] stack is the same bytes as that matrix's storage."""
+        q = self.w4.empty_quantized(scheme, N, K, num_experts=E)
+        W = self.synth.device_weights(E * N, K, 0.02, 0, name, self.dev)
+        flat = self.w4.QuantizedMatrix(scheme, E * N, K, q.codes.view(E * N, -1), q.scale.view(E * N, -1),
+                                       None if q.bias is None else q.bias.view(E * N, -1))
+        self.w4.quantize_pack(W, scheme, out=flat)
         del W
         return q
 
@@ -301,34 +316,46 @@ def run_moe(c: Ctx, a):
     M = a.M or 1
     L = []
     for l in range(layers):
-        gate = w4.empty_quantized("aff4_g64", F, D, num_experts=E)
-        up = w4.empty_quantized("aff4_g64", F, D, num_experts=E)
-        down = w4.empty_quantized("aff4_g64", D, F, num_experts=E)
-        for e in range(E):
-            c.quant(F, D, "aff4_g64", f"moe.L{l}.gate.{e}", out=gate, expert=e)
-            c.quant(F, D, "aff4_g64", f"moe.L{l}.up.{e}", out=up, expert=e)
-            c.quant(D, F, "aff4_g64", f"moe.L{l}.down.{e}", out=down, expert=e)
+        gate = c.quant_stack(E, F, D, "aff4_g64", f"moe.L{l}.gate")
+        up = c.quant_stack(E, F, D, "aff4_g64", f"moe.L{l}.up")
+        down = c.quant_stack(E, D, F, "aff4_g64", f"moe.L{l}.down")
         shared = [c.quant(Fs, D, "aff4_g64", f"moe.L{l}.sg"), c.quant(Fs, D, "aff4_g64", f"moe.L{l}.su"),
                   c.quant(D, Fs, "aff4_g64", f"moe.L{l}.sd")]
         router = c.quant(E, D, "aff8_g64", f"moe.L{l}.router")
         L.append((router, gate, up, down, shared))
     torch.cuda.synchronize()
     _, x = c.x(M, D, "moe.x")
-    ws = torch.empty(w4.moe_workspace_bytes(M, k, E, D, F, Fs), dtype=torch.uint8, device=c.dev)
     ids = [torch.empty((M, k), dtype=torch.int32, device=c.dev) for _ in range(layers)]
     wts = [torch.empty((M, k), dtype=torch.float32, device=c.dev) for _ in range(layers)]
-    logits = torch.empty((M, E), dtype=torch.float32, device=c.dev)
     y = torch.empty((M, D), dtype=torch.float32, device=c.dev)
-    # Router GEMV, then selection + experts in one call (one token: the
-    # selection runs inside the gate/up pass; several: a top-k launch with a
-    # workgroup per token, then one bucketing workgroup).
     one = M == 1
+    if a.moe_path in ("layer", "single"):
+        # router, top-k and the experts from x in one call: for one token three
+        # launches (router GEMV, gate/up selecting its experts itself, down) or
+        # the single launch; for several, router (+ top-k), bucketing, two
+        # passes, combine
+        single = a.moe_path == "single"
+        w4.moe_layer_set_single_launch(single)
+        ws = w4.moe_layer_workspace(M, k, E, D, F, Fs, c.dev)
+        launches = ("one (router, top-k, shared and routed gate/up, down: work items of one persistent grid)"
+                    if one and single else "router gemv, gate/up with the top-k inside, down" if one else
+                    "router (fused with top-k), bucketing, gate/up, down, combine")
 
-    def step():
-        for l, (router, gate, up, down, shared) in enumerate(L):
-            w4.gemv_into(router, x, logits)
-            w4.moe_gemv_logits(gate, up, down, x, logits, top_k=k, shared=shared, workspace=ws,
-                               y=y, ids=ids[l], weights=wts[l])
+        def step():
+            for l, (router, gate, up, down, shared) in enumerate(L):
+                w4.moe_layer(router, gate, up, down, x, top_k=k, shared=shared, workspace=ws, y=y,
+                             ids=ids[l], weights=wts[l])
+    else:
+        ws = torch.empty(w4.moe_workspace_bytes(M, k, E, D, F, Fs), dtype=torch.uint8, device=c.dev)
+        logits = torch.empty((M, E), dtype=torch.float32, device=c.dev)
+        launches = ("router gemv, gate/up with the top-k inside, down" if one else
+                    "router gemv, top-k, bucketing, gate/up, down, combine")
+
+        def step():
+            for l, (router, gate, up, down, shared) in enumerate(L):
+                w4.gemv_into(router, x, logits)
+                w4.moe_gemv_logits(gate, up, down, x, logits, top_k=k, shared=shared, workspace=ws,
+                                   y=y, ids=ids[l], weights=wts[l])
 
     g = c.graph(step)
     ms = c.time_graph(g, a.steps, a.warmup)
@@ -343,14 +370,14 @@ def run_moe(c: Ctx, a):
                         "workload": "gemma-4-26b-a4b-shaped MoE FFN stack", "layers": layers, "M": M,
                         "experts": E, "top_k": k, "d_model": D, "expert_ffn": F, "shared_ffn": Fs,
                         "scheme": "aff4_g64 experts/shared, aff8_g64 router",
-                        "launches_per_layer": ("router gemv, gate/up with the top-k inside, down" if one else
-                                               "router gemv, top-k, bucketing, gate/up, down, combine")})
+                        "entry_point": {"layer": "w4a16_moe_layer", "single": "w4a16_moe_layer (single launch)",
+                                        "launches": "w4a16_gemv + w4a16_moe_gemv_logits"}[a.moe_path],
+                        "launches_per_layer": launches})
     out["hbm_TBps"] = round(tbs, 4)
     out["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
     out["distinct_experts_per_layer"] = sum(distinct) / len(distinct)
     out["step_bytes"] = step_bytes
-    out["roofline"] = hbm_roofline(f"whole MoE layer ({3 if one else 6} launches)", step_bytes // layers,
-                                   ms * 1e3 / layers)
+    out["roofline"] = hbm_roofline(f"whole MoE layer ({launches})", step_bytes // layers, ms * 1e3 / layers)
     return out
 
 

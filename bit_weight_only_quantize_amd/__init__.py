@@ -69,6 +69,12 @@ _SIGS = {
     "w4_moe_workspace_bytes": ([_I64, ctypes.c_int, _I64, _I64, _I64, _I64], ctypes.c_size_t),
     "w4a16_moe_gemv": ([ctypes.POINTER(_W4Matrix)] * 6 + [_P, _I64, _P, _P, ctypes.c_int, _P,
                                                           ctypes.c_size_t, _P, _P], ctypes.c_int),
+    "w4_moe_layer_workspace_bytes": ([_I64, ctypes.c_int, _I64, _I64, _I64, _I64], ctypes.c_size_t),
+    "w4a16_moe_layer": ([ctypes.POINTER(_W4Matrix)] * 7 + [_P, _I64, ctypes.c_int, _P, _P, _P, _P,
+                                                           ctypes.c_size_t, _P], ctypes.c_int),
+    "w4_moe_layer_status": ([_P, ctypes.POINTER(ctypes.c_int32), _P], ctypes.c_int),
+    "w4_moe_layer_set_wait": ([_I64, ctypes.c_int], None),
+    "w4_moe_layer_set_single_launch": ([ctypes.c_int], None),
     "w4a16_moe_gemv_noalloc": ([ctypes.POINTER(_W4Matrix)] * 6 + [_P, _I64, _P, _P, ctypes.c_int, _P, _P],
                                ctypes.c_int),
     "w4a16_moe_gemv_logits": ([ctypes.POINTER(_W4Matrix)] * 6 + [_P, _I64, _P, ctypes.c_int, _P, _P,
@@ -399,3 +405,59 @@ def moe_gemv_noalloc(gate: QuantizedMatrix, up: QuantizedMatrix, down: Quantized
     _check(lib().w4a16_moe_gemv_noalloc(*refs, _ptr(x), M, _ptr(ids), _ptr(weights), top_k, _ptr(y),
                                         _stream(x.device)))
     return y
+
+
+MOE_LAYER_GAVE_UP_LOGITS, MOE_LAYER_GAVE_UP_IDS, MOE_LAYER_GAVE_UP_H = 1, 2, 4
+
+
+def moe_layer_workspace(M: int, top_k: int, E: int, D: int, F: int, Fs: int = 0,
+                        device="cuda") -> torch.Tensor:
+    """A workspace for moe_layer (up to M tokens), zero-filled as its first use requires."""
+    n = int(lib().w4_moe_layer_workspace_bytes(M, top_k, E, D, F, Fs))
+    if n == 0:
+        raise ValueError("invalid sizes for a MoE layer workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_layer(router: QuantizedMatrix, gate: QuantizedMatrix, up: QuantizedMatrix,
+              down: QuantizedMatrix, x: torch.Tensor, top_k: int = 8, shared=None,
+              workspace: torch.Tensor = None, y: torch.Tensor = None, ids: torch.Tensor = None,
+              weights: torch.Tensor = None):
+    """Router, top-k and the MoE FFN from x [M][D]: (y, ids, weights). One token runs
+    as a single launch (see w4a16_moe_layer in include/w4a16.h)."""
+    x = _as_bf16_bits(x, "x")
+    M = x.shape[0]
+    E, F, D = gate.num_experts, gate.N, gate.K
+    Fs = shared[0].N if shared is not None else 0
+    if workspace is None:
+        workspace = moe_layer_workspace(M, top_k, E, D, F, Fs, x.device)
+    if y is None:
+        y = torch.empty((M, D), dtype=torch.float32, device=x.device)
+    if ids is None:
+        ids = torch.empty((M, top_k), dtype=torch.int32, device=x.device)
+    if weights is None:
+        weights = torch.empty((M, top_k), dtype=torch.float32, device=x.device)
+    descs = [m.desc() for m in (router, gate, up, down)]
+    sh = [s.desc() for s in shared] if shared is not None else [None, None, None]
+    refs = [ctypes.byref(d) for d in descs] + [ctypes.byref(s) if s is not None else None for s in sh]
+    _check(lib().w4a16_moe_layer(*refs, _ptr(x), M, top_k, _ptr(ids), _ptr(weights), _ptr(y),
+                                 _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return y, ids, weights
+
+
+def moe_layer_status(workspace: torch.Tensor) -> int:
+    """0, or the W4_MOE_LAYER_GAVE_UP_* bits of the last single-launch call (synchronizes)."""
+    v = ctypes.c_int32()
+    _check(lib().w4_moe_layer_status(_ptr(workspace), ctypes.byref(v), _stream(workspace.device)))
+    return v.value
+
+
+def moe_layer_set_single_launch(enable: bool) -> None:
+    """Whether one token takes the single launch (where it applies) or the launch sequence."""
+    lib().w4_moe_layer_set_single_launch(int(bool(enable)))
+
+
+def moe_layer_set_wait(max_polls: int = 0, withhold: bool = False) -> None:
+    """Testing hook: poll limit of the single-launch layer's waits (0 = default) and
+    whether it withholds its expert selection (every wait for it then gives up)."""
+    lib().w4_moe_layer_set_wait(int(max_polls), int(bool(withhold)))

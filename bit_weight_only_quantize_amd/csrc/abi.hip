@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "../../include/w4a16.h"
@@ -396,6 +397,87 @@ int w4a16_moe_gemv_logits(const w4_matrix* gate, const w4_matrix* up, const w4_m
     return hip_status(w4::launch_moe_logits(scheme, W, x, M, logits, top_k, ids, weights,
                                             workspace, y, (hipStream_t)stream),
                       "moe_gemv_logits launch");
+}
+
+// ---------------------------------------------------------------- MoE layer
+static std::atomic<long long> g_layer_polls{0};
+static std::atomic<int> g_layer_withhold{0};
+static std::atomic<int> g_layer_single{0};
+
+void w4_moe_layer_set_single_launch(int enable) { g_layer_single.store(enable != 0); }
+constexpr long long kLayerDefaultPolls = 1LL << 21;  // each a device-scope load + 128 cycles of sleep: seconds
+
+void w4_moe_layer_set_wait(int64_t max_polls, int withhold) {
+    g_layer_polls.store(max_polls > 0 ? (long long)max_polls : 0);
+    g_layer_withhold.store(withhold != 0);
+}
+
+size_t w4_moe_layer_workspace_bytes(int64_t M, int top_k, int64_t E, int64_t D, int64_t F,
+                                    int64_t Fs) {
+    if (M < 0 || top_k < 1 || top_k > 32 || E < 1 || D < 0 || F < 0 || Fs < 0) return 0;
+    return w4::moe_layer_workspace_layout(M, top_k, E, D, F, Fs).total;
+}
+
+int w4a16_moe_layer(const w4_matrix* router, const w4_matrix* gate, const w4_matrix* up,
+                    const w4_matrix* down, const w4_matrix* shared_gate,
+                    const w4_matrix* shared_up, const w4_matrix* shared_down,
+                    const uint16_t* x, int64_t M, int top_k, int32_t* ids, float* weights,
+                    float* y, void* workspace, size_t workspace_bytes, void* stream) {
+    w4::MoeMats W;
+    int scheme = 0;
+    int rc = moe_check(gate, up, down, shared_gate, shared_up, shared_down, M, top_k, W, scheme);
+    if (rc) return rc;
+    if ((rc = check_matrix(router, "router", 1))) return rc;
+    if (router->N != W.E || router->K != W.D)
+        return fail(W4_ESHAPE, "router must be [E][D] = [%lld][%lld]", (long long)W.E, (long long)W.D);
+    if (W.E > 1024 || top_k > W.E) return fail(W4_ESHAPE, "top_k=%d, E=%lld", top_k, (long long)W.E);
+    if (M == 0 || W.D == 0) return ok();
+    if (W.D > w4::kMaxSkinnyK) return fail(W4_ESHAPE, "D=%lld exceeds %lld", (long long)W.D, (long long)w4::kMaxSkinnyK);
+    if (!x || !ids || !weights || !y || !workspace)
+        return fail(W4_EINVAL, "null x, ids, weights, y or workspace");
+    if (!aligned16(x) || !aligned16(ids) || !aligned16(weights) || !aligned16(y) || !aligned16(workspace))
+        return fail(W4_EALIGN, "x, ids, weights, y and workspace must be 16-byte aligned");
+    const w4::MoeLayerWorkspace L = w4::moe_layer_workspace_layout(M, top_k, W.E, W.D, W.F, W.Fs);
+    if (workspace_bytes < L.total)
+        return fail(W4_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+    hipStream_t st = (hipStream_t)stream;
+    const void* R[3] = {router->codes, router->scale, router->bias};
+    if (M == 1 && g_layer_single.load() && w4::moe_layer_ok(router->scheme, top_k, W.E, W.D, W.F, W.Fs)) {
+        const long long polls = g_layer_polls.load();
+        const hipError_t e = w4::launch_moe_layer(scheme, router->scheme, W, R, x, top_k, ids, weights,
+                                                  workspace, y, polls > 0 ? polls : kLayerDefaultPolls,
+                                                  g_layer_withhold.load(), st);
+        if (e != hipErrorNotSupported) return hip_status(e, "moe_layer launch");
+        // refused before launching anything: the launch sequence below
+    }
+    float* logits = (float*)((uint8_t*)workspace + L.multi);
+    void* ws = (uint8_t*)workspace + L.multi + (((size_t)M * W.E * 4 + 255) & ~(size_t)255);
+    hipError_t e;
+    if (M == 1) {
+        // router GEMV, then the top-k inside the gate/up pass and the down pass
+        e = w4::launch_gemv(router->scheme, router->codes, router->scale, router->bias, W.E, W.D, x,
+                            1, logits, st);
+        if (e != hipSuccess) return hip_status(e, "moe_layer router launch");
+        return hip_status(w4::launch_moe_logits(scheme, W, x, 1, logits, top_k, ids, weights, ws, y, st),
+                          "moe_layer expert launches");
+    }
+    e = w4::launch_route(router->scheme, router->codes, router->scale, router->bias, W.E, W.D, x, M,
+                         top_k, logits, ids, weights, st);
+    if (e != hipSuccess) return hip_status(e, "moe_layer route launch");
+    return hip_status(w4::launch_moe(scheme, W, x, M, ids, weights, top_k, ws, y, st),
+                      "moe_layer expert launches");
+}
+
+int w4_moe_layer_status(const void* workspace, int32_t* status, void* stream) {
+    if (!workspace || !status) return fail(W4_EINVAL, "null workspace or status");
+    if (!aligned16(workspace)) return fail(W4_EALIGN, "workspace must be 16-byte aligned");
+    uint32_t v = 0;
+    hipError_t e = hipMemcpyAsync(&v, (const uint8_t*)workspace + 4 * (size_t)w4::kSyncStatus, 4,
+                                  hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "moe_layer status");
+    *status = (int32_t)v;
+    return ok();
 }
 
 // ---------------------------------------------------------------- INT4 KV cache

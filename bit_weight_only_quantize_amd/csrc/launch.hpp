@@ -90,6 +90,45 @@ hipError_t launch_moe_logits(int scheme, const MoeMats& W, const uint16_t* x, in
                              const float* logits, int k, int32_t* ids, float* wts, void* ws,
                              float* y, hipStream_t st);
 
+// ---- one-token MoE layer in one launch (router, top-k, shared and routed
+// experts); hand-off words at the start of its workspace, zero between calls.
+// A device-scope atomic or coherent access to one line costs ~10 ns and
+// serializes with every other access to that line, so a count with many
+// contributors is split over kSyncRep sub-counters on lines of their own, and
+// what many workgroups poll is replicated on kSyncRep lines. Values that are
+// polled carry their own "written" mark (never zero once written), so a
+// consumer polls the data itself instead of a separate flag.
+constexpr int kSyncLine = 32;  // words per 128-byte line
+constexpr int kSyncRep = 32;   // sub-counters / replicas
+constexpr int kHRep = 8;       // copies of h (one per XCD's readers)
+constexpr int kLayerMaxE = 128, kLayerMaxK = 8;
+enum : int {
+    kSyncErr = 1,       // give-ups of this call (bits)
+    kSyncStatus = 2,    // give-ups of the last call (bits), kept for the host
+    kSyncHTop = 3,      // h sub-counters completed
+    kSyncExitTop = 4,   // exit sub-counters completed
+    kSyncLogits = 1 * kSyncLine,  // kLayerMaxE (value, 1) word pairs: 8 lines
+    kSyncSel = kSyncLogits + 2 * kLayerMaxE,  // + r * kSyncLine: ids + 1, then weights | 2^31
+    kSyncHSub = kSyncSel + kSyncRep * kSyncLine,       // + r * kSyncLine: gate/up items done
+    kSyncHDoneRep = kSyncHSub + kSyncRep * kSyncLine,  // + r * kSyncLine: every h row in
+    kSyncExitSub = kSyncHDoneRep + kSyncRep * kSyncLine,  // + r * kSyncLine: workgroups out
+    kLayerSyncWords = kSyncExitSub + kSyncRep * kSyncLine,
+};
+constexpr unsigned kGaveUpLogits = 1, kGaveUpIds = 2, kGaveUpH = 4;
+struct MoeLayerWorkspace {  // byte offsets
+    size_t sync, h, multi, total;  // multi: where the launch sequence's area starts
+};
+bool moe_layer_ok(int rscheme, int k, int64_t E, int64_t D, int64_t F, int64_t Fs);
+// The single launch's area (sync words, logit replicas, h copies), then the
+// launch sequence's (router logits [M][E], then the w4a16_moe_gemv workspace):
+// the two never overlap, so either path may follow the other on one workspace.
+MoeLayerWorkspace moe_layer_workspace_layout(int64_t M, int k, int64_t E, int64_t D, int64_t F,
+                                             int64_t Fs);
+// router: codes, scale, bias of the [E][D] router (8-bit affine)
+hipError_t launch_moe_layer(int scheme, int rscheme, const MoeMats& W, const void* const* router,
+                            const uint16_t* x, int k, int32_t* ids, float* wts, void* ws,
+                            float* y, long long wait_limit, int withhold, hipStream_t st);
+
 // ---- INT4 KV cache (head vectors of kKvHeadDim values)
 int kv_chunks(int64_t T);  // position chunks of the weighted sum (partials per head)
 hipError_t launch_kv_quantize(const float* const* x, int ncache, int64_t n, int64_t H,

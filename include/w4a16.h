@@ -232,6 +232,67 @@ int w4a16_moe_gemv_logits(const w4_matrix* gate, const w4_matrix* up, const w4_m
                           float* y, void* stream);
 
 /*
+ * One MoE layer from its input ([TurboFieldfare], model section and 量化和精度):
+ * router logits = x * Wr^T, per token the top_k experts with their softmax
+ * weights (exactly as w4_moe_route), then the FFN of w4a16_moe_gemv with them.
+ * Results (ids, weights, y) equal those of w4_moe_route followed by
+ * w4a16_moe_gemv, bit for bit, on either of the two paths below.
+ * By default one token takes three launches (the router GEMV; the gate/up
+ * pass, each of whose workgroups selects the experts from the logits itself;
+ * the down pass with the weighted combine) and several tokens the launches of
+ * w4_moe_route and w4a16_moe_gemv. With w4_moe_layer_set_single_launch(1), one
+ * token with an 8-bit affine router, E <= 128, top_k <= 8, 2048 <= D <= 4096,
+ * 32 <= F <= 1024 and Fs <= 4096 runs as ONE launch instead ([TurboFieldfare]'s
+ * M2 time table spends a third of each token in waits between dependent GPU
+ * submissions): the router rows, the selection, the shared and selected
+ * experts' gate/up rows and the down rows are work items of a grid no larger
+ * than the GPU holds at once, handing results to each other through
+ * device-scope words in the workspace, the down rows' weights streaming while
+ * the gate/up rows are computed. On this GPU each such hand-off costs about
+ * what a launch boundary costs, so the default stays the launch sequence.
+ * router: [E][D] single matrix; the experts as for w4a16_moe_gemv.
+ * x: bf16 [M][D]; ids int32 [M][top_k], weights fp32 [M][top_k], y fp32 [M][D].
+ * workspace: device memory of at least w4_moe_layer_workspace_bytes(...) bytes
+ * (sized for the largest M it will serve), all zero before its first use
+ * (e.g. one hipMemset when it is allocated); every call leaves the single
+ * launch's hand-off words zero again, and either path may follow the other on
+ * one workspace. Calls sharing a workspace must not overlap. A wait inside
+ * the single launch that exceeds the poll limit (w4_moe_layer_set_wait) gives
+ * up instead of hanging: the call then completes with unspecified y and
+ * reports it through w4_moe_layer_status.
+ */
+size_t w4_moe_layer_workspace_bytes(int64_t M, int top_k, int64_t E, int64_t D, int64_t F,
+                                    int64_t Fs);
+int w4a16_moe_layer(const w4_matrix* router, const w4_matrix* gate, const w4_matrix* up,
+                    const w4_matrix* down, const w4_matrix* shared_gate,
+                    const w4_matrix* shared_up, const w4_matrix* shared_down,
+                    const uint16_t* x, int64_t M, int top_k, int32_t* ids, float* weights,
+                    float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-side setting read by later w4a16_moe_layer calls from any thread:
+ * enable != 0 selects the single launch for one token where it applies. */
+void w4_moe_layer_set_single_launch(int enable);
+
+/*
+ * Outcome of the last single-launch w4a16_moe_layer call that used `workspace`
+ * (device pointer): *status (host) = 0 if every hand-off completed, else a set
+ * of W4_MOE_LAYER_GAVE_UP_* bits. Copies one word to the host and synchronizes
+ * `stream`.
+ */
+#define W4_MOE_LAYER_GAVE_UP_LOGITS 1 /* the wait for the router logits gave up */
+#define W4_MOE_LAYER_GAVE_UP_IDS 2 /* a wait for the expert selection gave up */
+#define W4_MOE_LAYER_GAVE_UP_H   4 /* a wait for the gate/up rows gave up */
+int w4_moe_layer_status(const void* workspace, int32_t* status, void* stream);
+
+/*
+ * Testing hook (host-side setting read by later w4a16_moe_layer calls from any
+ * thread): each wait inside the single launch polls at most max_polls times
+ * (<= 0 restores the default of 2^21 polls, a few seconds); withhold != 0 makes the launch
+ * never publish its expert selection, so that every wait for it gives up.
+ */
+void w4_moe_layer_set_wait(int64_t max_polls, int withhold);
+
+/*
  * INT4 KV cache ([Shimmy] §3.2, TurboShimmy INT4 KV): each head vector of
  * W4_KV_HEAD_DIM fp32 values is quantized on its own: scale = max|v| / 7.5
  * (fp32), integers round(v / scale) (halves away from zero, as the page's
