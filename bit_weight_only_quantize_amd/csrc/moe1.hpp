@@ -75,9 +75,9 @@ __device__ __forceinline__ void m1_scale(const uint8_t* s, const uint8_t* b, int
 
 // ---------------------------------------------------------------- gate/up
 // SEL: the workgroup selects the token's experts itself from the router
-// logits (E <= 128, one wavefront, the same top-k as the routing kernel), so no
-// launch of its own is needed for the selection; workgroup 0 publishes the
-// selection for the down pass and the caller.
+// logits (E <= 128, the same top-k as the routing kernel, by ranks over the
+// workgroup's threads), so no launch of its own is needed for the selection;
+// workgroup 0 publishes the selection for the down pass and the caller.
 template <int S, int NV, int R, int XV, int RW, bool SEL>
 __global__ __launch_bounds__(64 * RW) void moe1_gate_up_kernel(Moe1Args a) {
     using T = Traits<S>;
@@ -101,16 +101,11 @@ __global__ __launch_bounds__(64 * RW) void moe1_gate_up_kernel(Moe1Args a) {
         if (!shared) {  // block-uniform
             __shared__ int32_t sel_id[8];
             __shared__ float sel_w[8];
-            if (wave == 0) {
-                float v[2];
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int ei = lane + 64 * j;
-                    const float l = a.logits[min(ei, a.E - 1)];
-                    v[j] = ei < a.E ? l : -INFINITY;
-                }
-                topk_rounds<2>(v, a.E, a.k, sel_id, sel_w);
-            }
+            __shared__ uint64_t keys[128];
+            __shared__ int part[256];
+            __shared__ float stat[2];
+            const float* lgt = a.logits;
+            topk_ranked([&](int e) { return lgt[e]; }, a.E, a.k, sel_id, sel_w, keys, part, stat);
             __syncthreads();
             e = sel_id[slot];
             if (bid == 0 && (int)threadIdx.x < a.k) {

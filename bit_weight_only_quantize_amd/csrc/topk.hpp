@@ -78,4 +78,65 @@ __device__ __forceinline__ void topk_rounds(const float (&v)[EPL], int E, int k,
     }
 }
 
+// Key ordering logits descending, ties (-0 equal to +0) to the lower expert
+// index (non-NaN logits): larger key = earlier rank.
+__device__ __forceinline__ uint64_t rank_key(float v, int e) {
+    uint32_t b = v == 0.f ? 0u : __float_as_uint(v);
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)b << 32) | (0xFFFFFFFFu - (uint32_t)e);
+}
+
+// The same selection as topk_rounds<2> (E <= 128) by 256 threads of a
+// workgroup at once: an expert's rank is the number of experts whose key is
+// larger, each thread counting over 64 of the 128 keys, so the k ranks come
+// out of two barriers instead of k dependent wave-wide arg-max rounds. The
+// softmax statistics are those of topk_rounds<2> (wavefront 0, same lane
+// layout and order), so ids and weights equal its outputs bit for bit.
+// lg(e): logit of expert e < E (any memory); ids / wts: ranks 0..k-1 (any
+// memory); keys (128 u64), part (256 int), stat (2 float): LDS. Every thread of
+// the workgroup must call it (blockDim.x >= 256; threads beyond 255 only pass
+// the barriers).
+template <typename Get>
+__device__ void topk_ranked(Get lg, int E, int k, int32_t* __restrict__ ids,
+                            float* __restrict__ wts, uint64_t* keys, int* part, float* stat) {
+    const int t = threadIdx.x;
+    if (t < 128) keys[t] = rank_key(t < E ? lg(t) : -INFINITY, t);
+    if (t < 64) {
+        float v[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e = t + 64 * j;
+            const float x = lg(min(e, E - 1));
+            v[j] = e < E ? x : -INFINITY;
+        }
+        float mx = fmaxf(v[0], v[1]);
+        mx = wave_max_dpp(mx);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) s += expf(v[j] - mx);
+        const float inv = 1.f / wave_sum_dpp(s);
+        if (t == 0) {
+            stat[0] = mx;
+            stat[1] = inv;
+        }
+    }
+    __syncthreads();
+    if (t < 256) {
+        const int a = t & 127, h = t >> 7;
+        const uint64_t ka = keys[a];
+        int r = 0;
+#pragma unroll 16
+        for (int b = 64 * h; b < 64 * h + 64; ++b) r += keys[b] > ka ? 1 : 0;
+        part[t] = r;
+    }
+    __syncthreads();
+    if (t < E) {
+        const int r = part[t] + part[t + 128];
+        if (r < k) {
+            ids[r] = t;
+            wts[r] = expf(lg(t) - stat[0]) * stat[1];
+        }
+    }
+}
+
 }  // namespace w4

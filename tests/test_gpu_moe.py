@@ -218,3 +218,35 @@ def test_moe_gemv_logits_equals_route_then_gemv(M, E, F, Fs, k):
         assert torch.equal(ids, ids_r)
         assert torch.equal(w, w_r)
         assert torch.equal(y, y_r)
+
+
+@pytest.mark.parametrize("E,k", [(128, 8), (100, 8), (9, 8), (8, 8)])
+def test_single_token_selection_ties_signed_zeros_and_minus_inf(E, k):
+    """The selection inside the one-token gate/up pass (ranks over the
+    workgroup) and the top-k launch of the several-token path agree bit for
+    bit on logits with exact ties, +0 against -0 and -inf entries, and both
+    follow the stable-sort rule: largest first, equal logits (-0 equal to +0)
+    in expert order."""
+    D, F, scheme, seed = 2048, 256, "aff4_g64", 5
+    tag = f"ties.{E}.{k}"
+    print(f"[moe] {tag}", flush=True)
+    gate = _dev_stack(E, F, D, seed, f"{tag}.gate", scheme)
+    up = _dev_stack(E, F, D, seed, f"{tag}.up", scheme)
+    down = _dev_stack(E, D, F, seed, f"{tag}.down", scheme)
+    rng = np.random.default_rng(17)
+    vals = np.array([0.75, 0.5, 0.0, -0.0, -1.0, -np.inf], np.float32)
+    row = vals[rng.integers(0, len(vals), E)]
+    row[rng.integers(0, E)] = 0.75  # at least one finite logit
+    x = dev_bf16(synth.activations_bf16(2, D, seed, f"{tag}.x"))
+    ref_ids = sorted(range(E), key=lambda e: (-float(row[e]), e))[:k]
+    one = torch.from_numpy(row[None, :].copy()).cuda()
+    two = torch.from_numpy(np.stack([row, row])).cuda()
+    y1, ids1, w1 = w4.moe_gemv_logits(gate, up, down, x[:1], one, top_k=k)
+    y2, ids2, w2 = w4.moe_gemv_logits(gate, up, down, x, two, top_k=k)
+    torch.cuda.synchronize()
+    assert ids1.cpu().tolist() == [ref_ids]
+    assert torch.equal(ids1[0], ids2[0]) and torch.equal(ids2[0], ids2[1])
+    assert torch.equal(w1[0], w2[0])
+    lr = row.astype(np.float64)
+    p = np.exp(lr - lr.max()) / np.exp(lr - lr.max()).sum()
+    assert np.allclose(w1[0].cpu().numpy(), p[ref_ids], rtol=1e-6, atol=0)
