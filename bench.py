@@ -5,8 +5,10 @@ Default workload (the one the headline metric is quoted on): a Llama-7B-shaped
 decode layer stack. One step = one decode pass of M tokens (default 1) through
 32 distinct layers, each with the projections Wq, Wk, Wv, Wo (4096x4096), gate,
 up (11008x4096) and down (4096x11008), symmetric INT4 with 128-weight groups
-(scale = absmax/7). Per layer the launches a decode layer's data dependencies
-allow: Q/K/V in one launch (shared input), O, gate+up in one launch, down.
+(scale = absmax/7). Per layer: Q/K/V in one launch (shared input), O, and the
+FFN through w4a16_ffn (h = bf16(gelu(gate x) * (up x)) feeds down): one
+persistent launch for one token, gate+up / activation / down for several
+(--ffn separate: gate+up and down as plain GEMV calls with their own inputs).
 
 Other workloads (--workload): moe26b (Gemma-4-26B-A4B-shaped MoE FFN stack),
 prefill (the two prefill GEMMs), llama13b (13B-shaped stack + tied head),
@@ -15,7 +17,12 @@ gemv1024 (the single 1024x1024 GEMV, cache-hot and cold).
 Weights are seeded N(0, 0.02) drawn on the device and quantized with the
 library's quantize_pack; activations are seeded bf16 N(0, 1). Every step is
 captured once in a HIP graph and replayed; times come from HIP events on the
-stream the kernels run on. Prints one JSON line.
+stream the kernels run on.
+
+With no --workload every workload runs in turn, one JSON line each: the 7B
+stack at M = 4 and 16, the 13B stack (+ head) at M = 1 and 8, the MoE stack at
+M = 1 and 32, prefill, the single GEMV, the INT4 KV cache, and last the
+headline line, the 7B stack at M = 1 with the CPU oracle timed beside it.
 """
 from __future__ import annotations
 
@@ -39,6 +46,7 @@ LLAMA13B = [("wq", 5120, 5120), ("wk", 5120, 5120), ("wv", 5120, 5120), ("wo", 5
 
 GEMV_WAVE_SOURCES = ("common.hpp", "launch.hpp", "skinny.hpp", "gemv_wave.hpp", "gemv.hip")
 GEMM_SOURCES = ("common.hpp", "launch.hpp", "gemm.hip")
+FFN_SOURCES = ("common.hpp", "launch.hpp", "skinny.hpp", "gemv_wave.hpp", "handoff.hpp", "ffn.hip")
 
 
 def weight_bytes(scheme: str, N: int, K: int) -> int:
@@ -62,19 +70,25 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama7b",
-                    choices=["llama7b", "moe26b", "prefill", "llama13b", "gemv1024", "kv"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "llama7b", "moe26b", "prefill", "llama13b", "gemv1024", "kv"],
+                    help="all (default): every workload, one line each, the 7B M=1 headline last")
     ap.add_argument("--context", type=int, default=8192, help="kv: cached positions per layer")
-    ap.add_argument("--M", type=int, default=None, help="decode tokens per step")
+    ap.add_argument("--M", type=int, default=None, help="decode tokens per step (one workload only)")
     ap.add_argument("--scheme", default=None, choices=["sym4_g128", "aff4_g64", "aff8_g64"],
                     help="weight scheme of the llama7b/llama13b stacks (default: sym4_g128 / aff4_g64)")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU oracle time budget")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle time budget, each of the all-cores and one-thread runs")
     ap.add_argument("--moe-path", default="layer", choices=["layer", "single", "launches"],
                     help="moe26b: w4a16_moe_layer with its default dispatch, w4a16_moe_layer with "
                          "the single launch for one token, or the router GEMV + "
                          "w4a16_moe_gemv_logits calls")
+    ap.add_argument("--ffn", default="layer", choices=["layer", "single", "separate"],
+                    help="llama stacks: the FFN through w4a16_ffn (h feeds down) with its default "
+                         "launches, w4a16_ffn with the single persistent launch for one token, or "
+                         "gate+up and down as separate GEMV calls with their own inputs")
     ap.add_argument("--dominant-only", action="store_true",
                     help="only replay the dominant kernel (for counter collection)")
     return ap.parse_args()
@@ -109,6 +123,13 @@ class Ctx:
         self.w4.quantize_pack(W, scheme, out=flat)
         del W
         return q
+
+    def release(self):
+        """Hand the previous workload's device memory back before the next one."""
+        import gc
+        gc.collect()
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
 
     def x(self, M, K, name):
         host = self.synth.activations_bf16(M, K, 0, name)
@@ -198,7 +219,7 @@ def measured_traffic(profile, files):
 
 
 # ---------------------------------------------------------------- dense decode stacks
-def decode_stack(c: Ctx, shapes, scheme, layers, M, head=None):
+def decode_stack(c: Ctx, shapes, scheme, layers, M, head=None, ffn="layer"):
     """Build `layers` distinct layers (and an optional head) and return the step
     and dominant-kernel closures plus byte counts."""
     w4 = c.w4
@@ -213,58 +234,109 @@ def decode_stack(c: Ctx, shapes, scheme, layers, M, head=None):
     xs = {K: v[1] for K, v in xh.items()}
     ys = {nm: c.torch.empty((M, N), dtype=c.torch.float32, device=c.dev) for nm, N, _ in shapes}
     yh = c.torch.empty((M, head[0]), dtype=c.torch.float32, device=c.dev) if head else None
-    # the down projection's activations outgrow one CU's LDS at M = 16 (7B) and
-    # M = 8 (13B): those launches split K across CUs through a workspace
-    need = w4.gemv_workspace_bytes(mats[0]["down"], M)
-    ws = c.torch.empty(need, dtype=c.torch.uint8, device=c.dev) if need else None
+    if ffn in ("layer", "single"):
+        # the FFN through w4a16_ffn: h = bf16(gelu(gate x) * (up x)) feeds down
+        w4.ffn_set_path(w4.FFN_PATH_SINGLE_LAUNCH if ffn == "single" else w4.FFN_PATH_DEFAULT)
+        ws = w4.ffn_workspace(mats[0]["down"], M, c.dev)
+    else:
+        # gate+up and down as separate GEMV calls with their own inputs; the
+        # down projection's activations outgrow one CU's LDS at M = 16 (7B) and
+        # M = 8 (13B): those launches split K across CUs through a workspace
+        need = w4.gemv_workspace_bytes(mats[0]["down"], M)
+        ws = c.torch.empty(need, dtype=c.torch.uint8, device=c.dev) if need else None
+
+    def ffn_call(m):
+        if ffn != "separate":
+            w4.ffn(m["gate"], m["up"], m["down"], xs[d], workspace=ws, y=ys["down"])
+        else:
+            w4.gemv_multi_into([m["gate"], m["up"]], xs[d], [ys["gate"], ys["up"]])
+            w4.gemv_ws_into(m["down"], xs[f], ys["down"], ws)
 
     def step():
         for m in mats:
             w4.gemv_multi_into([m["wq"], m["wk"], m["wv"]], xs[d], [ys["wq"], ys["wk"], ys["wv"]])
             w4.gemv_into(m["wo"], xs[d], ys["wo"])
-            w4.gemv_multi_into([m["gate"], m["up"]], xs[d], [ys["gate"], ys["up"]])
-            w4.gemv_ws_into(m["down"], xs[f], ys["down"], ws)
+            ffn_call(m)
         if hq is not None:
             w4.gemv_into(hq, xs[d], yh)
 
     def dominant():
         for m in mats:
-            w4.gemv_multi_into([m["gate"], m["up"]], xs[d], [ys["gate"], ys["up"]])
+            if ffn != "separate" and M == 1:
+                ffn_call(m)
+            else:
+                w4.gemv_multi_into([m["gate"], m["up"]], xs[d], [ys["gate"], ys["up"]])
 
     per_layer = (gemv_bytes(scheme, [(d, d)] * 3, M) + gemv_bytes(scheme, [(d, d)], M)
                  + gemv_bytes(scheme, [(f, d)] * 2, M) + gemv_bytes(scheme, [(d, f)], M))
     step_bytes = layers * per_layer + (gemv_bytes(scheme, [(head[0], head[1])], M) if head else 0)
-    dom_bytes = gemv_bytes(scheme, [(f, d)] * 2, M)
+    if ffn != "separate" and M == 1:
+        # weights of all three, x, h written once and read by the down rows, y
+        dom_bytes = (2 * weight_bytes(scheme, f, d) + weight_bytes(scheme, d, f) + 2 * d
+                     + 2 * f * 2 + 4 * d)
+    else:
+        dom_bytes = gemv_bytes(scheme, [(f, d)] * 2, M)
     return mats, xh, step, dominant, step_bytes, dom_bytes
 
 
-def cpu_baseline(layer, xs_host, M, budget_s, shapes, scheme, layers):
-    """The oracle as it stands, on layer 0's matrices (host copies), until the budget."""
-    import oracle
+def host_cpu():
+    """CPUs this process may run on, and the CPU model name."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return n, model
+
+
+def _oracle_gemv_pass(layer, xs_host, M, budget_s, shapes, scheme):
+    """Layer 0's matrices through the oracle, in order, until the budget; returns
+    (bytes, matrix names, seconds)."""
+    import oracle
+    import torch
     done_bytes, done, t0 = 0, [], time.perf_counter()
     for name, N, K in shapes:
         q = layer[name]
-        bias = None if q.bias is None else q.bias.view(__import__("torch").int16).cpu().numpy().view("uint16")
+        bias = None if q.bias is None else q.bias.view(torch.int16).cpu().numpy().view("uint16")
         scale = q.scale.cpu().numpy() if scheme == "sym4_g128" else \
-            q.scale.view(__import__("torch").int16).cpu().numpy().view("uint16")
+            q.scale.view(torch.int16).cpu().numpy().view("uint16")
         oracle.gemv_reference(q.codes.cpu().numpy(), scale, bias, scheme, xs_host[K])
         done_bytes += gemv_bytes(scheme, [(N, K)], M)
         done.append(name)
         if time.perf_counter() - t0 > budget_s:
             break
-    dt = time.perf_counter() - t0
-    layer_frac = done_bytes / sum(gemv_bytes(scheme, [(N, K)], M) for _, N, K in shapes)
-    return {
-        "value": done_bytes / dt / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"layer 0 matrices {','.join(done)} ({layer_frac:.0%} of one layer), M={M}: "
-                   f"numpy fp64 dequantize + BLAS product, {dt:.1f} s; "
-                   f"equivalent {M * layer_frac / (dt * layers):.4f} tok/s for {layers} layers"),
-    }
+    return done_bytes, done, time.perf_counter() - t0
+
+
+def cpu_baseline(layer, xs_host, M, budget_s, shapes, scheme, layers):
+    """The oracle as it stands, on layer 0's matrices (host copies), until the
+    budget: once with every thread its BLAS starts, once limited to one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    nproc, model = host_cpu()
+    full = sum(gemv_bytes(scheme, [(N, K)], M) for _, N, K in shapes)
+
+    def leg(cores):
+        nb, done, dt = _oracle_gemv_pass(layer, xs_host, M, budget_s, shapes, scheme)
+        frac = nb / full
+        return {"value": nb / dt / 1e12, "unit": "TB/s", "cores": int(cores), "kind": "oracle",
+                "sample": (f"layer 0 matrices {','.join(done)} ({frac:.0%} of one layer), M={M}: "
+                           f"numpy fp64 dequantize + BLAS product, {dt:.1f} s; "
+                           f"equivalent {M * frac / (dt * layers):.4f} tok/s for {layers} layers")}
+
+    out = leg(threads)
+    with threadpool_limits(limits=1):
+        out["one_thread"] = leg(1)
+    out["nproc"] = nproc
+    out["cpu_model"] = model
+    return out
 
 
 def run_llama(c: Ctx, a, big: bool):
@@ -273,7 +345,9 @@ def run_llama(c: Ctx, a, big: bool):
     layers = a.layers or (40 if big else 32)
     M = a.M or 1
     head = (152064, 5120) if big else None
-    mats, xh, step, dominant, step_bytes, dom_bytes = decode_stack(c, shapes, scheme, layers, M, head)
+    mats, xh, step, dominant, step_bytes, dom_bytes = decode_stack(c, shapes, scheme, layers, M, head,
+                                                                   a.ffn)
+    fused1 = a.ffn == "single" and M == 1
     g_dom = c.graph(dominant)
     if a.dominant_only:
         copy_bytes = calibration_copy(c)
@@ -291,17 +365,29 @@ def run_llama(c: Ctx, a, big: bool):
     out = base_line(a, METRIC, round(tbs, 4), "TB/s", ms, {
         "workload": name, "layers": layers, "M": M, "scheme": scheme,
         "matrices": ", ".join(f"{nm} {N}x{K}" for nm, N, K in shapes) + (f", head {head[0]}x{head[1]}" if head else ""),
-        "launches_per_layer": "qkv (one launch), o, gate+up (one launch), down" + (
-            " (K parts on separate CUs, then a summing launch)" if c.w4.gemv_workspace_bytes(mats[0]["down"], M) else ""),
+        "launches_per_layer": "qkv (one launch), o, " + (
+            "ffn (gate, up, gelu, down: one persistent launch)" if fused1 else
+            "ffn (gate+up with gelu in the epilogue, down)" if a.ffn == "layer" and M == 1 else
+            "ffn (gate+up, gelu, down" + (" in K parts + a summing launch" if c.w4.gemv_workspace_bytes(
+                mats[0]["down"], M) else "") + ")" if a.ffn == "layer" else
+            "gate+up (one launch), down with its own input" + (
+                " (K parts on separate CUs, then a summing launch)"
+                if c.w4.gemv_workspace_bytes(mats[0]["down"], M) else "")),
         "weights": "seeded N(0,0.02) drawn on device", "activations": "bf16 N(0,1)"})
     out["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
     out["tok_per_s"] = round(M / (ms * 1e-3), 1)
     out["step_bytes"] = step_bytes
     traffic = None
-    if not big and M == 1 and layers == 32 and scheme == "sym4_g128":
-        traffic = measured_traffic("gemv_wave_gate_up_llama7b_counters.md", GEMV_WAVE_SOURCES)
-    out["roofline"] = hbm_roofline(f"gemv_wave_kernel (gate+up, 2 x {f}x{d} {scheme}, one launch)",
-                                   dom_bytes, us_dom, traffic)
+    if fused1:
+        if not big and layers == 32 and scheme == "sym4_g128":
+            traffic = measured_traffic("ffn_llama7b_counters.md", FFN_SOURCES)
+        kname = f"ffn_kernel (gate+up 2 x {f}x{d}, gelu, down {d}x{f}, {scheme}, one launch)"
+    elif a.ffn == "layer" and M == 1:
+        kname = (f"w4a16_ffn, two launches: ffn_gate_up_kernel (2 x {f}x{d} {scheme}, gelu epilogue) "
+                 f"+ gemv_wave_kernel (down {d}x{f})")
+    else:
+        kname = f"gate+up GEMV (2 x {f}x{d} {scheme}, one launch)"
+    out["roofline"] = hbm_roofline(kname, dom_bytes, us_dom, traffic)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(mats[0], {K: v[0] for K, v in xh.items()}, M,
                                            a.cpu_seconds, shapes, scheme, layers)
@@ -570,18 +656,33 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE={world}); "
               "the multi-GPU layout is a design note, not a measured path", file=sys.stderr)
         sys.exit(2)
+    if a.workload == "all" and (a.M is not None or a.layers is not None or a.dominant_only):
+        print("--M, --layers and --dominant-only apply to one --workload", file=sys.stderr)
+        sys.exit(2)
     c = Ctx(a)
+    if a.workload != "all":
+        print(json.dumps(run_one(c, a)), flush=True)
+        return
+    runs = [("llama7b", 4), ("llama7b", 16), ("llama13b", 1), ("llama13b", 8), ("moe26b", 1),
+            ("moe26b", 32), ("prefill", None), ("gemv1024", None), ("kv", None)]
+    for workload, M in runs:
+        sub = argparse.Namespace(**dict(vars(a), workload=workload, M=M, no_cpu_baseline=True))
+        print(json.dumps(run_one(c, sub)), flush=True)
+        c.release()
+    head = argparse.Namespace(**dict(vars(a), workload="llama7b", M=1))
+    print(json.dumps(run_one(c, head)), flush=True)
+
+
+def run_one(c, a):
     if a.workload in ("llama7b", "llama13b"):
-        out = run_llama(c, a, a.workload == "llama13b")
-    elif a.workload == "moe26b":
-        out = run_moe(c, a)
-    elif a.workload == "prefill":
-        out = run_prefill(c, a)
-    elif a.workload == "kv":
-        out = run_kv(c, a)
-    else:
-        out = run_gemv1024(c, a)
-    print(json.dumps(out), flush=True)
+        return run_llama(c, a, a.workload == "llama13b")
+    if a.workload == "moe26b":
+        return run_moe(c, a)
+    if a.workload == "prefill":
+        return run_prefill(c, a)
+    if a.workload == "kv":
+        return run_kv(c, a)
+    return run_gemv1024(c, a)
 
 
 if __name__ == "__main__":

@@ -77,6 +77,12 @@ _SIGS = {
     "w4_moe_layer_set_single_launch": ([ctypes.c_int], None),
     "w4a16_moe_gemv_noalloc": ([ctypes.POINTER(_W4Matrix)] * 6 + [_P, _I64, _P, _P, ctypes.c_int, _P, _P],
                                ctypes.c_int),
+    "w4_ffn_workspace_bytes": ([ctypes.POINTER(_W4Matrix), _I64], ctypes.c_size_t),
+    "w4a16_ffn": ([ctypes.POINTER(_W4Matrix)] * 3 + [_P, _I64, _P, _P, _P, ctypes.c_size_t, _P],
+                  ctypes.c_int),
+    "w4_ffn_status": ([_P, ctypes.POINTER(ctypes.c_int32), _P], ctypes.c_int),
+    "w4_ffn_set_wait": ([_I64, ctypes.c_int], None),
+    "w4_ffn_set_path": ([ctypes.c_int], ctypes.c_int),
     "w4a16_moe_gemv_logits": ([ctypes.POINTER(_W4Matrix)] * 6 + [_P, _I64, _P, ctypes.c_int, _P, _P,
                                                                  _P, ctypes.c_size_t, _P, _P],
                               ctypes.c_int),
@@ -461,3 +467,58 @@ def moe_layer_set_wait(max_polls: int = 0, withhold: bool = False) -> None:
     """Testing hook: poll limit of the single-launch layer's waits (0 = default) and
     whether it withholds its expert selection (every wait for it then gives up)."""
     lib().w4_moe_layer_set_wait(int(max_polls), int(bool(withhold)))
+
+
+# ---------------------------------------------------------------- dense gated FFN
+FFN_GAVE_UP_H = 4
+
+
+def ffn_workspace(down: QuantizedMatrix, M: int, device="cuda") -> torch.Tensor:
+    """A workspace for ffn (up to M tokens), zero-filled as its first use requires."""
+    d = down.desc()
+    n = int(lib().w4_ffn_workspace_bytes(ctypes.byref(d), M))
+    if n == 0:
+        raise ValueError("invalid sizes for an FFN workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def ffn(gate: QuantizedMatrix, up: QuantizedMatrix, down: QuantizedMatrix, x: torch.Tensor,
+        workspace: torch.Tensor = None, y: torch.Tensor = None, h: torch.Tensor = None,
+        want_h: bool = False):
+    """Gated FFN from x [M][D]: y = W_down · bf16(gelu_tanh(W_gate x) * (W_up x)).
+    Returns y (fp32 [M][D]), or (y, h) with h bf16 [M][F] when h is given or
+    want_h. The launches follow ffn_set_path (see w4a16_ffn in include/w4a16.h)."""
+    x = _as_bf16_bits(x, "x")
+    M = x.shape[0] if x.dim() == 2 else 1
+    if workspace is None:
+        workspace = ffn_workspace(down, M, x.device)
+    if y is None:
+        y = torch.empty((M, down.N), dtype=torch.float32, device=x.device)
+    if h is None and want_h:
+        h = torch.empty((M, gate.N), dtype=torch.bfloat16, device=x.device)
+    dg, du, dd = gate.desc(), up.desc(), down.desc()
+    _check(lib().w4a16_ffn(ctypes.byref(dg), ctypes.byref(du), ctypes.byref(dd), _ptr(x), M, _ptr(h),
+                           _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return (y, h) if h is not None else y
+
+
+def ffn_status(workspace: torch.Tensor) -> int:
+    """0, or FFN_GAVE_UP_H if the last single-launch call gave up a wait (synchronizes)."""
+    v = ctypes.c_int32()
+    _check(lib().w4_ffn_status(_ptr(workspace), ctypes.byref(v), _stream(workspace.device)))
+    return v.value
+
+
+FFN_PATH_DEFAULT, FFN_PATH_SINGLE_LAUNCH, FFN_PATH_SEQUENCE = 0, 1, 2
+
+
+def ffn_set_path(path: int) -> None:
+    """How one token runs: FFN_PATH_DEFAULT (two launches), FFN_PATH_SINGLE_LAUNCH
+    (one persistent launch where it applies) or FFN_PATH_SEQUENCE (three launches)."""
+    _check(lib().w4_ffn_set_path(int(path)))
+
+
+def ffn_set_wait(max_polls: int = 0, withhold: bool = False) -> None:
+    """Testing hook: poll limit of the single launch's waits (0 = default) and whether
+    it withholds the "h complete" flag (every wait for it then gives up)."""
+    lib().w4_ffn_set_wait(int(max_polls), int(bool(withhold)))

@@ -148,6 +148,26 @@ int w4a16_gemv_ws(const w4_matrix* W, const uint16_t* x, int64_t M, float* y, vo
                       "gemv launch");  // need > 0: the K-part plan exists, so it launches
 }
 
+// Up to four non-empty matrices sharing x (same scheme and K), validated.
+static hipError_t gemv_multi_dispatch(int scheme, int n, const void* const* c,
+                                      const void* const* sc, const void* const* b,
+                                      const int64_t* N, int64_t K, const uint16_t* x, int64_t M,
+                                      float* const* y, hipStream_t st) {
+    if (M == 1 && w4::gemv_wave_ok(scheme, K))
+        return w4::launch_gemv_wave(scheme, n, c, sc, b, N, K, x, y, st);
+    if (w4::gemv_mfma_ok(scheme, K, M)) {
+        const hipError_t e = w4::launch_gemv_mfma(scheme, n, c, sc, b, N, K, x, M, y, st);
+        if (e != hipErrorNotSupported) return e;
+    }
+    if (w4::gemv_wave_mt_ok(scheme, K, M))
+        return w4::launch_gemv_wave_mt(scheme, n, c, sc, b, N, K, x, M, y, st);
+    for (int i = 0; i < n; ++i) {
+        const hipError_t e = w4::launch_gemv(scheme, c[i], sc[i], b[i], N[i], K, x, M, y[i], st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 int w4a16_gemv_multi(const w4_matrix* const* Ws, int count, const uint16_t* x, int64_t M,
                      float* const* ys, void* stream) {
     if (!Ws || !ys) return fail(W4_EINVAL, "null Ws or ys");
@@ -185,24 +205,8 @@ int w4a16_gemv_multi(const w4_matrix* const* Ws, int count, const uint16_t* x, i
         ++n;
     }
     if (n == 0) return ok();
-    const int scheme = Ws[0]->scheme;
-    if (M == 1 && w4::gemv_wave_ok(scheme, K))
-        return hip_status(w4::launch_gemv_wave(scheme, n, c, sc, b, N, K, x, y, st),
-                          "gemv_multi launch");
-    if (w4::gemv_mfma_ok(scheme, K, M)) {
-        const hipError_t e = w4::launch_gemv_mfma(scheme, n, c, sc, b, N, K, x, M, y, st);
-        if (e != hipErrorNotSupported) return hip_status(e, "gemv_multi launch");
-    }
-    if (w4::gemv_wave_mt_ok(scheme, K, M))
-        return hip_status(w4::launch_gemv_wave_mt(scheme, n, c, sc, b, N, K, x, M, y, st),
-                          "gemv_multi launch");
-    for (int i = 0; i < count; ++i) {
-        if (Ws[i]->N == 0) continue;
-        hipError_t e = w4::launch_gemv(Ws[i]->scheme, Ws[i]->codes, Ws[i]->scale, Ws[i]->bias,
-                                       Ws[i]->N, K, x, M, ys[i], st);
-        if (e != hipSuccess) return hip_status(e, "gemv_multi launch");
-    }
-    return ok();
+    return hip_status(gemv_multi_dispatch(Ws[0]->scheme, n, c, sc, b, N, K, x, M, y, st),
+                      "gemv_multi launch");
 }
 
 int w4a16_gemm(const w4_matrix* W, const uint16_t* X, int64_t M, uint16_t* Y, void* stream) {
@@ -478,6 +482,102 @@ int w4_moe_layer_status(const void* workspace, int32_t* status, void* stream) {
     if (e != hipSuccess) return hip_status(e, "moe_layer status");
     *status = (int32_t)v;
     return ok();
+}
+
+// ---------------------------------------------------------------- dense gated FFN
+static std::atomic<long long> g_ffn_polls{0};
+static std::atomic<bool> g_ffn_withhold{false};
+static std::atomic<int> g_ffn_path{W4_FFN_PATH_DEFAULT};
+constexpr long long kFfnDefaultPolls = 1LL << 21;
+
+void w4_ffn_set_wait(int64_t max_polls, int withhold) {
+    g_ffn_polls.store(max_polls > 0 ? (long long)max_polls : 0);
+    g_ffn_withhold.store(withhold != 0);
+}
+
+int w4_ffn_set_path(int path) {
+    if (path != W4_FFN_PATH_DEFAULT && path != W4_FFN_PATH_SINGLE_LAUNCH && path != W4_FFN_PATH_SEQUENCE)
+        return fail(W4_EINVAL, "unknown FFN path %d", path);
+    g_ffn_path.store(path);
+    return ok();
+}
+
+size_t w4_ffn_workspace_bytes(const w4_matrix* down, int64_t M) {
+    if (!down || down->num_experts != 1 || down->N <= 0 || down->K <= 0 || M < 1 || M > 64 ||
+        !known(down->scheme))
+        return 0;
+    return w4::ffn_workspace_layout(down->scheme, M, down->N, down->K).total;
+}
+
+int w4a16_ffn(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down, const uint16_t* x,
+              int64_t M, uint16_t* h, float* y, void* workspace, size_t workspace_bytes,
+              void* stream) {
+    int rc;
+    if ((rc = check_matrix(gate, "gate", 1)) || (rc = check_matrix(up, "up", 1)) ||
+        (rc = check_matrix(down, "down", 1)))
+        return rc;
+    if (gate->scheme != up->scheme || gate->scheme != down->scheme)
+        return fail(W4_ESHAPE, "gate, up and down must share one scheme");
+    const int64_t D = gate->K, F = gate->N;
+    if (up->N != F || up->K != D || down->N != D || down->K != F)
+        return fail(W4_ESHAPE, "gate and up must be [F][D], down [D][F] (F=%lld, D=%lld)",
+                    (long long)F, (long long)D);
+    if (M < 0 || M > 64) return fail(W4_ESHAPE, "M=%lld out of range [0, 64]", (long long)M);
+    if (M == 0) return ok();
+    if (D > w4::kMaxSkinnyK || F > w4::kMaxSkinnyK)
+        return fail(W4_ESHAPE, "D=%lld and F=%lld must not exceed %lld", (long long)D, (long long)F,
+                    (long long)w4::kMaxSkinnyK);
+    if (!x || !y || !workspace) return fail(W4_EINVAL, "null x, y or workspace");
+    if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || (h && !aligned16(h)))
+        return fail(W4_EALIGN, "x, y, h and workspace must be 16-byte aligned");
+    const w4::FfnWorkspace L = w4::ffn_workspace_layout(gate->scheme, M, D, F);
+    if (workspace_bytes < L.total)
+        return fail(W4_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* base = (uint8_t*)workspace;
+    const int scheme = gate->scheme;
+    const void* G[3] = {gate->codes, gate->scale, gate->bias};
+    const void* U[3] = {up->codes, up->scale, up->bias};
+    const void* Dn[3] = {down->codes, down->scale, down->bias};
+    const int path = g_ffn_path.load();
+    uint16_t* hh = h ? h : (uint16_t*)(base + L.h);
+    if (M == 1 && path == W4_FFN_PATH_SINGLE_LAUNCH) {
+        const long long polls = g_ffn_polls.load();
+        const hipError_t e = w4::launch_ffn_fused(scheme, G, U, Dn, D, F, x, h, y, workspace,
+                                                  polls > 0 ? polls : kFfnDefaultPolls,
+                                                  g_ffn_withhold.load(), st);
+        if (e != hipErrorNotSupported) return hip_status(e, "ffn launch");
+        // refused before launching anything: the launches below
+    }
+    hipError_t e = hipErrorNotSupported;
+    if (M == 1 && path != W4_FFN_PATH_SEQUENCE) {
+        // gate/up rows with the activation in their epilogue, then down
+        e = w4::launch_ffn_gate_up(scheme, G, U, D, F, x, hh, st);
+        if (e != hipSuccess && e != hipErrorNotSupported) return hip_status(e, "ffn gate/up launch");
+    }
+    if (e == hipErrorNotSupported) {
+        // gate and up in one GEMV launch, the activation, then down
+        float* g = (float*)(base + L.g);
+        float* u = (float*)(base + L.u);
+        const void* c2[2] = {gate->codes, up->codes};
+        const void* s2[2] = {gate->scale, up->scale};
+        const void* b2[2] = {gate->bias, up->bias};
+        const int64_t N2[2] = {F, F};
+        float* y2[2] = {g, u};
+        e = gemv_multi_dispatch(scheme, 2, c2, s2, b2, N2, D, x, M, y2, st);
+        if (e == hipSuccess) e = w4::launch_ffn_act(g, u, hh, M * F, st);
+        if (e != hipSuccess) return hip_status(e, "ffn gate/up launches");
+    }
+    if (M >= 2 && M <= 16 && w4::gemv_mfma_split_bytes(scheme, D, F, M) > 0)
+        e = w4::launch_gemv_mfma(scheme, 1, &Dn[0], &Dn[1], &Dn[2], &D, F, hh, M, &y, st,
+                                 (float*)(base + L.part));
+    else
+        e = w4::launch_gemv(scheme, down->codes, down->scale, down->bias, D, F, hh, M, y, st);
+    return hip_status(e, "ffn down launch");
+}
+
+int w4_ffn_status(const void* workspace, int32_t* status, void* stream) {
+    return w4_moe_layer_status(workspace, status, stream);  // the same word of the same layout
 }
 
 // ---------------------------------------------------------------- INT4 KV cache

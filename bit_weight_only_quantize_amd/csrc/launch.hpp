@@ -129,6 +129,24 @@ hipError_t launch_moe_layer(int scheme, int rscheme, const MoeMats& W, const voi
                             const uint16_t* x, int k, int32_t* ids, float* wts, void* ws,
                             float* y, long long wait_limit, int withhold, hipStream_t st);
 
+// ---- dense gated FFN: h = bf16(gelu_tanh(W_gate x) * (W_up x)), y = W_down h
+struct FfnWorkspace {  // byte offsets: hand-off words, h (copies, or the
+    size_t sync, h, g, u, part, total;  // sequence's h), g and u, down K parts
+};
+FfnWorkspace ffn_workspace_layout(int scheme, int64_t M, int64_t D, int64_t F);
+// one token in one persistent launch (4-bit schemes, D / 32 in (64, 256],
+// F / 32 in (320, 512]); hipErrorNotSupported (nothing launched) otherwise
+bool ffn_fused_ok(int scheme, int64_t D, int64_t F);
+hipError_t launch_ffn_fused(int scheme, const void* const* gate, const void* const* up,
+                            const void* const* down, int64_t D, int64_t F, const uint16_t* x,
+                            uint16_t* h, float* y, void* ws, long long wait_limit, int withhold,
+                            hipStream_t st);
+// one token, the gate/up rows alone (4-bit schemes, D / 32 <= 256): h to h
+bool ffn_gate_up_ok(int scheme, int64_t D, int64_t F);
+hipError_t launch_ffn_gate_up(int scheme, const void* const* gate, const void* const* up, int64_t D,
+                              int64_t F, const uint16_t* x, uint16_t* h, hipStream_t st);
+hipError_t launch_ffn_act(const float* g, const float* u, uint16_t* h, int64_t n, hipStream_t st);
+
 // ---- INT4 KV cache (head vectors of kKvHeadDim values)
 int kv_chunks(int64_t T);  // position chunks of the weighted sum (partials per head)
 hipError_t launch_kv_quantize(const float* const* x, int ncache, int64_t n, int64_t H,

@@ -35,20 +35,16 @@
 //                 experts, then waits for every h row, stages one copy of h in
 //                 LDS and reduces y[n] = shared(n) + sum_j w_j * down_j(n) in a
 //                 fixed order
-// Hand-off data is written with device-scope atomic stores and read with
-// device-scope atomic loads, which are coherent across the XCDs' L2 caches by
-// themselves; a count follows the completion of its contributor's stores
-// (vmcnt 0). Measured alternatives: device-scope release/acquire fences write
-// back or invalidate whole L2 caches per wavefront (13x slower); one counter or
-// flag shared by every workgroup serializes at ~10 ns per access (4x slower);
-// polling the hand-off data itself from every thread floods the coherent path
-// (3x slower). The last workgroup to finish resets the hand-off words, so each
+// Hand-offs follow handoff.hpp (device-scope atomic stores and loads, split
+// counters, replicated flags). Polling the hand-off data itself from every
+// thread instead of one poller per workgroup floods the coherent path (3x
+// slower). The last workgroup to finish resets the hand-off words, so each
 // call leaves them zero.
 #include <algorithm>
-#include <mutex>
 
 #include "common.hpp"
 #include "gemv_wave.hpp"
+#include "handoff.hpp"
 #include "launch.hpp"
 #include "moe1.hpp"
 #include "skinny.hpp"
@@ -76,37 +72,6 @@ struct LayerArgs {
 constexpr int kLayerRW = 4;  // wavefronts per workgroup
 constexpr int kLayerThreads = 64 * kLayerRW;
 constexpr int kRouterRows = 2 * kLayerRW, kGuRows = 2 * kLayerRW, kDownRows = 2 * kLayerRW;
-
-// ---------------------------------------------------------------- hand-offs
-// Device-coherent accesses of hand-off data (relaxed atomics at device scope).
-__device__ __forceinline__ void put32(void* p, uint32_t v) {
-    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void put64(void* p, uint64_t v) {
-    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t get32(const void* p) {
-    return __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t get64(const void* p) {
-    return __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned count(unsigned* p) {
-    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Contributors to a split count of n: contributor i counts on sub-counter
-// i % kSyncRep (whose share is n / kSyncRep, one more for the first n %
-// kSyncRep); the one completing a sub-counter counts on the top word, and the
-// one completing that (min(n, kSyncRep) sub-counters) is told so.
-__device__ bool split_count(unsigned* sync, int sub_base, int top, int i, int n) {
-    const int r = i % kSyncRep;
-    const unsigned share = n / kSyncRep + (r < n % kSyncRep ? 1 : 0);
-    if (count(sync + sub_base + r * kSyncLine) != share - 1) return false;
-    const unsigned subs = n < kSyncRep ? n : kSyncRep;
-    return count(sync + top) == subs - 1;
-}
 
 // Thread 0 polls until the k selection words of its replica line (ids from
 // word 0, weights from word kLayerMaxK) are all written, at most `limit`
@@ -136,36 +101,6 @@ __device__ bool poll_selection(const LayerArgs& a, int k, int32_t* sid, float* s
         if (n >= a.wait_limit) return false;
         __builtin_amdgcn_s_sleep(2);
     }
-}
-
-// Workgroup-wide: thread 0 polls a replicated flag >= 1; the barrier orders
-// the workgroup's later loads after the poll that saw it.
-__device__ bool wg_wait_flag(const LayerArgs& a, int rep_base, unsigned err_bit, int* sflag) {
-    if (threadIdx.x == 0) {
-        const unsigned* p = a.sync + rep_base + (blockIdx.x % kSyncRep) * kSyncLine;
-        bool ok = false;
-        for (long long n = 0;; ++n) {
-            if (get32(p) >= 1u) { ok = true; break; }
-            if (n >= a.wait_limit) break;
-            __builtin_amdgcn_s_sleep(2);
-        }
-        if (!ok) atomicOr(a.sync + kSyncErr, err_bit);
-        *sflag = ok;
-    }
-    __syncthreads();
-    const bool ok = *sflag != 0;
-    __syncthreads();
-    return ok;
-}
-
-// The thread index as a value the compiler cannot trace to threadIdx: every
-// lane-dependent address of an item is then computed inside the item, not
-// hoisted out of the persistent loop (hoisted, the invariants of all four item
-// kinds would stay live at once and the kernel would need twice the registers).
-__device__ __forceinline__ int item_tid() {
-    int t = threadIdx.x;
-    asm volatile("" : "+v"(t));
-    return t;
 }
 
 // ---------------------------------------------------------------- router item
@@ -437,7 +372,7 @@ __device__ void down_item(const LayerArgs& a, int item, uint32_t* smem, int* sfl
         }
     }
     asm volatile("" ::: "memory");
-    const bool have_h = wg_wait_flag(a, kSyncHDoneRep, kGaveUpH, sflag);
+    const bool have_h = wg_wait_flag(a.sync, a.wait_limit, kSyncHDoneRep, kGaveUpH, sflag);
     // stage one copy of h: the k slot rows and the shared row (16-element vectors)
     const int total = k * VRF + VRS;
     if (have_h) {
@@ -576,39 +511,13 @@ MoeLayerWorkspace moe_layer_workspace_layout(int64_t M, int k, int64_t E, int64_
     return w;
 }
 
-// Blocks of one kernel instance that fit on a CU at once (occupancy API),
-// cached per (kernel, LDS bytes, device); 0 when the kernel needs scratch.
-static int resident_per_cu(const void* kern, size_t lds, int dev) {
-    struct Entry {
-        const void* kern;
-        size_t lds;
-        int dev, n;
-    };
-    static std::mutex mu;
-    static Entry cache[32];
-    static int used = 0;
-    std::lock_guard<std::mutex> lock(mu);
-    for (int i = 0; i < used; ++i)
-        if (cache[i].kern == kern && cache[i].lds == lds && cache[i].dev == dev) return cache[i].n;
-    hipFuncAttributes attr{};
-    int n = 0;
-    if (hipFuncGetAttributes(&attr, kern) != hipSuccess || attr.localSizeBytes > 0) n = 0;
-    else if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kLayerThreads, lds) != hipSuccess) n = 0;
-    if (used < 32) cache[used++] = Entry{kern, lds, dev, n};
-    return n;
-}
-
 template <int S, int RS, int NVR, int NV, int NVD, int NVS>
 static hipError_t go_layer(const LayerArgs& a, size_t lds, hipStream_t st) {
     auto kern = moe_layer_kernel<S, RS, NVR, NV, NVD, NVS>;
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    const int per_cu = resident_per_cu((const void*)kern, lds, dev);
-    if (per_cu < 1 || cus < 1) return hipErrorNotSupported;  // nothing launched
-    const int items = a.n_router + a.n_sgu + a.n_rgu + a.n_down;
-    const int grid = std::min(items, per_cu * cus);
+    hipError_t e = hipSuccess;
+    const int grid = persistent_grid((const void*)kern, kLayerThreads, lds,
+                                     a.n_router + a.n_sgu + a.n_rgu + a.n_down, &e);
+    if (grid < 1) return e;  // nothing launched
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kLayerThreads), lds, st, a);
     return hipGetLastError();
 }

@@ -293,6 +293,64 @@ int w4_moe_layer_status(const void* workspace, int32_t* status, void* stream);
 void w4_moe_layer_set_wait(int64_t max_polls, int withhold);
 
 /*
+ * Dense gated FFN of one decode layer: per token h = bf16(gelu_tanh(W_gate x) *
+ * (W_up x)) (round to nearest even; the pages name no activation, this is the
+ * gated GELU of the Gemma family, the one the expert FFN uses), then y = W_down h
+ * (fp32 accumulate). [airllm] §3.1 credits its decode speed to fusing a layer's
+ * operators into fewer kernel launches; [TurboFieldfare]'s M2 time table
+ * spends a third of each token waiting between dependent GPU submissions.
+ * One token with a 4-bit scheme and D / 32 <= 256 takes two launches: the
+ * gate/up rows with the activation in their epilogue (h written once, bf16),
+ * then the down GEMV. Several tokens, other shapes, or W4_FFN_PATH_SEQUENCE:
+ * three launches (gate and up in one GEMV launch, the activation, down with K
+ * parts for 2 <= M <= 16 where h does not fit a CU). W4_FFN_PATH_SINGLE_LAUNCH
+ * runs one token with a 4-bit scheme, D / 32 in (64, 256] and F / 32 in
+ * (320, 512] (e.g. the 7B and 13B shapes) as ONE launch: the gate/up rows and
+ * the down rows are work items of a grid no larger than the GPU holds at once,
+ * the down rows' weights streaming before h is complete, h handed over through
+ * device-scope words and copies in the workspace. On this GPU that hand-off
+ * (and the down rows' arithmetic, which can only start once h is complete)
+ * costs more than the launch boundary it removes, so it is not the default.
+ * All paths give the same bits for one token.
+ * gate, up: single matrices [F][D]; down: [D][F]; one scheme for all three.
+ * x: bf16 [M][D]; h: bf16 [M][F] out, or NULL; y: fp32 [M][D] out; 0 <= M <= 64,
+ * D, F <= 28672. workspace: device memory of at least w4_ffn_workspace_bytes(down,
+ * M) bytes (sized for the largest M it will serve), all zero before its first
+ * use (e.g. one hipMemset when it is allocated); every call leaves its hand-off
+ * words zero again. Calls sharing a workspace must not overlap. A wait inside
+ * the single launch that exceeds the poll limit (w4_ffn_set_wait) gives up
+ * instead of hanging: the call then completes with those rows of y unwritten
+ * and reports it through w4_ffn_status.
+ */
+size_t w4_ffn_workspace_bytes(const w4_matrix* down, int64_t M);
+int w4a16_ffn(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
+              const uint16_t* x, int64_t M, uint16_t* h, float* y, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Host-side setting read by later w4a16_ffn calls from any thread (W4_EINVAL
+ * for another value). */
+#define W4_FFN_PATH_DEFAULT 0       /* two launches for one token where they apply */
+#define W4_FFN_PATH_SINGLE_LAUNCH 1 /* one persistent launch for one token where it applies */
+#define W4_FFN_PATH_SEQUENCE 2      /* always the three-launch sequence */
+int w4_ffn_set_path(int path);
+
+/*
+ * Outcome of the last single-launch w4a16_ffn call that used `workspace` (device
+ * pointer): *status (host) = 0 if every hand-off completed, else
+ * W4_FFN_GAVE_UP_H. Copies one word to the host and synchronizes `stream`.
+ */
+#define W4_FFN_GAVE_UP_H 4 /* a wait for the gate/up rows gave up */
+int w4_ffn_status(const void* workspace, int32_t* status, void* stream);
+
+/*
+ * Testing hook (host-side setting read by later w4a16_ffn calls from any
+ * thread): each wait inside the single launch polls at most max_polls times
+ * (<= 0 restores the default of 2^21 polls, a few seconds); withhold != 0 makes
+ * the launch never announce that h is complete, so that every wait gives up.
+ */
+void w4_ffn_set_wait(int64_t max_polls, int withhold);
+
+/*
  * INT4 KV cache ([Shimmy] §3.2, TurboShimmy INT4 KV): each head vector of
  * W4_KV_HEAD_DIM fp32 values is quantized on its own: scale = max|v| / 7.5
  * (fp32), integers round(v / scale) (halves away from zero, as the page's

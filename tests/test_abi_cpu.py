@@ -146,3 +146,27 @@ def test_moe_noalloc_validation_without_a_device():
     assert b"static scratch" in L.w4_last_error()
     assert L.w4a16_moe_gemv_noalloc(*args, 16, 257, 16, 16, 8, 16, None) == -2
     assert L.w4a16_moe_gemv_noalloc(*args, 16, 4, None, 16, 8, 16, None) == -1
+
+
+def test_ffn_validation_without_a_device():
+    """w4a16_ffn checks shapes, scheme agreement, alignment and the workspace size
+    before any device call; M == 0 is a no-op."""
+    L = w4.lib()
+    D, F = 4096, 11008
+    gate, up, down = _desc(0, F, D), _desc(0, F, D), _desc(0, D, F)
+    need = L.w4_ffn_workspace_bytes(ctypes.byref(down), 1)
+    # hand-off words + 8 copies of h (bf16) + g and u (fp32) for the launch sequence
+    assert need >= 8 * F * 2 + 2 * F * 4
+    assert L.w4_ffn_workspace_bytes(ctypes.byref(down), 16) > need
+    assert L.w4_ffn_workspace_bytes(None, 1) == 0 and L.w4_ffn_workspace_bytes(ctypes.byref(down), 0) == 0
+    args = [ctypes.byref(m) for m in (gate, up, down)]
+    assert L.w4a16_ffn(*args, 16, 0, None, 16, 16, need, None) == 0             # M == 0
+    assert L.w4a16_ffn(*args, 16, 1, None, 16, 16, need - 16, None) == -5       # workspace too small
+    assert L.w4a16_ffn(*args, 16, 1, None, 16, None, need, None) == -1          # no workspace
+    assert L.w4a16_ffn(*args, 16, 1, 8, 16, 16, need, None) == -3               # h misaligned
+    assert L.w4a16_ffn(*args, 16, 65, None, 16, 16, need, None) == -2
+    bad_up = _desc(0, F, 2048)
+    assert L.w4a16_ffn(args[0], ctypes.byref(bad_up), args[2], 16, 1, None, 16, 16, need, None) == -2
+    bad_down = _desc(1, D, F)
+    assert L.w4a16_ffn(args[0], args[1], ctypes.byref(bad_down), 16, 1, None, 16, 16, need, None) == -2
+    assert b"scheme" in L.w4_last_error()
