@@ -89,6 +89,8 @@ def parse():
                     help="llama stacks: the FFN through w4a16_ffn (h feeds down) with its default "
                          "launches, w4a16_ffn with the single persistent launch for one token, or "
                          "gate+up and down as separate GEMV calls with their own inputs")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="first run a plain 1 GiB copy (for scaling HBM byte counters), then the workload")
     ap.add_argument("--dominant-only", action="store_true",
                     help="only replay the dominant kernel (for counter collection)")
     return ap.parse_args()
@@ -260,17 +262,25 @@ def decode_stack(c: Ctx, shapes, scheme, layers, M, head=None, ffn="layer"):
         if hq is not None:
             w4.gemv_into(hq, xs[d], yh)
 
+    hbuf = c.torch.empty((M, f), dtype=c.torch.bfloat16, device=c.dev)
+    gu_ws = w4.ffn_gate_up_workspace(mats[0]["gate"], M, c.dev)
+
     def dominant():
         for m in mats:
-            if ffn != "separate" and M == 1:
+            if ffn == "single" and M == 1:
                 ffn_call(m)
+            elif ffn == "layer" and M == 1:
+                w4.ffn_gate_up(m["gate"], m["up"], xs[d], h=hbuf, workspace=gu_ws)
             else:
                 w4.gemv_multi_into([m["gate"], m["up"]], xs[d], [ys["gate"], ys["up"]])
 
     per_layer = (gemv_bytes(scheme, [(d, d)] * 3, M) + gemv_bytes(scheme, [(d, d)], M)
                  + gemv_bytes(scheme, [(f, d)] * 2, M) + gemv_bytes(scheme, [(d, f)], M))
     step_bytes = layers * per_layer + (gemv_bytes(scheme, [(head[0], head[1])], M) if head else 0)
-    if ffn != "separate" and M == 1:
+    if ffn == "layer" and M == 1:
+        # gate and up weights, x, h written
+        dom_bytes = 2 * weight_bytes(scheme, f, d) + 2 * d + 2 * f
+    elif ffn == "single" and M == 1:
         # weights of all three, x, h written once and read by the down rows, y
         dom_bytes = (2 * weight_bytes(scheme, f, d) + weight_bytes(scheme, d, f) + 2 * d
                      + 2 * f * 2 + 4 * d)
@@ -297,21 +307,23 @@ def host_cpu():
 
 
 def _oracle_gemv_pass(layer, xs_host, M, budget_s, shapes, scheme):
-    """Layer 0's matrices through the oracle, in order, until the budget; returns
-    (bytes, matrix names, seconds)."""
+    """Layer 0's matrices through the oracle, in order and again, until the budget;
+    returns (bytes, matrices done, seconds)."""
     import oracle
     import torch
-    done_bytes, done, t0 = 0, [], time.perf_counter()
+    host = {}
     for name, N, K in shapes:
         q = layer[name]
         bias = None if q.bias is None else q.bias.view(torch.int16).cpu().numpy().view("uint16")
         scale = q.scale.cpu().numpy() if scheme == "sym4_g128" else \
             q.scale.view(torch.int16).cpu().numpy().view("uint16")
-        oracle.gemv_reference(q.codes.cpu().numpy(), scale, bias, scheme, xs_host[K])
+        host[name] = (q.codes.cpu().numpy(), scale, bias)
+    done_bytes, done, t0 = 0, 0, time.perf_counter()
+    while time.perf_counter() - t0 <= budget_s:
+        name, N, K = shapes[done % len(shapes)]
+        oracle.gemv_reference(*host[name], scheme, xs_host[K])
         done_bytes += gemv_bytes(scheme, [(N, K)], M)
-        done.append(name)
-        if time.perf_counter() - t0 > budget_s:
-            break
+        done += 1
     return done_bytes, done, time.perf_counter() - t0
 
 
@@ -327,9 +339,10 @@ def cpu_baseline(layer, xs_host, M, budget_s, shapes, scheme, layers):
         nb, done, dt = _oracle_gemv_pass(layer, xs_host, M, budget_s, shapes, scheme)
         frac = nb / full
         return {"value": nb / dt / 1e12, "unit": "TB/s", "cores": int(cores), "kind": "oracle",
-                "sample": (f"layer 0 matrices {','.join(done)} ({frac:.0%} of one layer), M={M}: "
-                           f"numpy fp64 dequantize + BLAS product, {dt:.1f} s; "
-                           f"equivalent {M * frac / (dt * layers):.4f} tok/s for {layers} layers")}
+                "sample": (f"layer 0's {len(shapes)} matrices ({','.join(n for n, _, _ in shapes)}) "
+                           f"cycled {done} times ({frac:.2f} layers' bytes), M={M}: numpy fp64 "
+                           f"dequantize + BLAS product, {dt:.1f} s; equivalent "
+                           f"{M * frac / (dt * layers):.4f} tok/s for {layers} layers")}
 
     out = leg(threads)
     with threadpool_limits(limits=1):
@@ -383,8 +396,9 @@ def run_llama(c: Ctx, a, big: bool):
             traffic = measured_traffic("ffn_llama7b_counters.md", FFN_SOURCES)
         kname = f"ffn_kernel (gate+up 2 x {f}x{d}, gelu, down {d}x{f}, {scheme}, one launch)"
     elif a.ffn == "layer" and M == 1:
-        kname = (f"w4a16_ffn, two launches: ffn_gate_up_kernel (2 x {f}x{d} {scheme}, gelu epilogue) "
-                 f"+ gemv_wave_kernel (down {d}x{f})")
+        if not big and layers == 32 and scheme == "sym4_g128":
+            traffic = measured_traffic("ffn_gate_up_llama7b_counters.md", FFN_SOURCES)
+        kname = f"ffn_gate_up_kernel (gate+up 2 x {f}x{d} {scheme}, gelu epilogue, one launch)"
     else:
         kname = f"gate+up GEMV (2 x {f}x{d} {scheme}, one launch)"
     out["roofline"] = hbm_roofline(kname, dom_bytes, us_dom, traffic)
@@ -660,6 +674,8 @@ def main():
         print("--M, --layers and --dominant-only apply to one --workload", file=sys.stderr)
         sys.exit(2)
     c = Ctx(a)
+    if a.calibrate:
+        calibration_copy(c)
     if a.workload != "all":
         print(json.dumps(run_one(c, a)), flush=True)
         return

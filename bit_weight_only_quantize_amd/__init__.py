@@ -80,6 +80,9 @@ _SIGS = {
     "w4_ffn_workspace_bytes": ([ctypes.POINTER(_W4Matrix), _I64], ctypes.c_size_t),
     "w4a16_ffn": ([ctypes.POINTER(_W4Matrix)] * 3 + [_P, _I64, _P, _P, _P, ctypes.c_size_t, _P],
                   ctypes.c_int),
+    "w4_ffn_gate_up_workspace_bytes": ([ctypes.POINTER(_W4Matrix), _I64], ctypes.c_size_t),
+    "w4a16_ffn_gate_up": ([ctypes.POINTER(_W4Matrix)] * 2 + [_P, _I64, _P, _P, ctypes.c_size_t, _P],
+                          ctypes.c_int),
     "w4_ffn_status": ([_P, ctypes.POINTER(ctypes.c_int32), _P], ctypes.c_int),
     "w4_ffn_set_wait": ([_I64, ctypes.c_int], None),
     "w4_ffn_set_path": ([ctypes.c_int], ctypes.c_int),
@@ -500,6 +503,30 @@ def ffn(gate: QuantizedMatrix, up: QuantizedMatrix, down: QuantizedMatrix, x: to
     _check(lib().w4a16_ffn(ctypes.byref(dg), ctypes.byref(du), ctypes.byref(dd), _ptr(x), M, _ptr(h),
                            _ptr(y), _ptr(workspace), workspace.numel(), _stream(x.device)))
     return (y, h) if h is not None else y
+
+
+def ffn_gate_up_workspace(gate: QuantizedMatrix, M: int, device="cuda") -> torch.Tensor:
+    """A workspace for ffn_gate_up (up to M tokens)."""
+    d = gate.desc()
+    n = int(lib().w4_ffn_gate_up_workspace_bytes(ctypes.byref(d), M))
+    if n == 0:
+        raise ValueError("invalid sizes for an FFN gate/up workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def ffn_gate_up(gate: QuantizedMatrix, up: QuantizedMatrix, x: torch.Tensor, h: torch.Tensor = None,
+                workspace: torch.Tensor = None) -> torch.Tensor:
+    """h (bf16 [M][F]) = bf16(gelu_tanh(W_gate x) * (W_up x)): the gate/up half of ffn."""
+    x = _as_bf16_bits(x, "x")
+    M = x.shape[0] if x.dim() == 2 else 1
+    dg, du = gate.desc(), up.desc()
+    if workspace is None:
+        workspace = ffn_gate_up_workspace(gate, M, x.device)
+    if h is None:
+        h = torch.empty((M, gate.N), dtype=torch.bfloat16, device=x.device)
+    _check(lib().w4a16_ffn_gate_up(ctypes.byref(dg), ctypes.byref(du), _ptr(x), M, _ptr(h),
+                                   _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return h
 
 
 def ffn_status(workspace: torch.Tensor) -> int:

@@ -509,24 +509,79 @@ size_t w4_ffn_workspace_bytes(const w4_matrix* down, int64_t M) {
     return w4::ffn_workspace_layout(down->scheme, M, down->N, down->K).total;
 }
 
+// The gate/up half of the FFN into hh (bf16 [M][F]); g, u: fp32 [M][F] each
+// (workspace) for the sequence.
+static hipError_t ffn_gate_up_launches(const w4_matrix* gate, const w4_matrix* up, const uint16_t* x,
+                                       int64_t M, uint16_t* hh, float* g, float* u, int path,
+                                       hipStream_t st) {
+    const int scheme = gate->scheme;
+    const int64_t D = gate->K, F = gate->N;
+    const void* G[3] = {gate->codes, gate->scale, gate->bias};
+    const void* U[3] = {up->codes, up->scale, up->bias};
+    if (path != W4_FFN_PATH_SEQUENCE) {
+        // gate/up rows with the activation in their epilogue
+        const hipError_t e = M == 1 ? w4::launch_ffn_gate_up(scheme, G, U, D, F, x, hh, st)
+                                    : w4::launch_gemv_mfma_gated(scheme, G, U, F, D, x, M, hh, st);
+        if (e != hipErrorNotSupported) return e;
+    }
+    // gate and up in one GEMV launch, then the activation
+    const void* c2[2] = {gate->codes, up->codes};
+    const void* s2[2] = {gate->scale, up->scale};
+    const void* b2[2] = {gate->bias, up->bias};
+    const int64_t N2[2] = {F, F};
+    float* y2[2] = {g, u};
+    hipError_t e = gemv_multi_dispatch(scheme, 2, c2, s2, b2, N2, D, x, M, y2, st);
+    if (e == hipSuccess) e = w4::launch_ffn_act(g, u, hh, M * F, st);
+    return e;
+}
+
+static int ffn_check_gate_up(const w4_matrix* gate, const w4_matrix* up, int64_t M) {
+    int rc;
+    if ((rc = check_matrix(gate, "gate", 1)) || (rc = check_matrix(up, "up", 1))) return rc;
+    if (gate->scheme != up->scheme) return fail(W4_ESHAPE, "gate and up must share one scheme");
+    if (up->N != gate->N || up->K != gate->K)
+        return fail(W4_ESHAPE, "gate and up must both be [F][D]");
+    if (M < 0 || M > 64) return fail(W4_ESHAPE, "M=%lld out of range [0, 64]", (long long)M);
+    if (gate->K > w4::kMaxSkinnyK || gate->N > w4::kMaxSkinnyK)
+        return fail(W4_ESHAPE, "D=%lld and F=%lld must not exceed %lld", (long long)gate->K,
+                    (long long)gate->N, (long long)w4::kMaxSkinnyK);
+    return W4_OK;
+}
+
+size_t w4_ffn_gate_up_workspace_bytes(const w4_matrix* gate, int64_t M) {
+    if (!gate || gate->num_experts != 1 || gate->N <= 0 || gate->K <= 0 || M < 1 || M > 64 ||
+        !known(gate->scheme))
+        return 0;
+    return 2 * (((size_t)M * gate->N * 4 + 255) & ~(size_t)255);
+}
+
+int w4a16_ffn_gate_up(const w4_matrix* gate, const w4_matrix* up, const uint16_t* x, int64_t M,
+                      uint16_t* h, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = ffn_check_gate_up(gate, up, M);
+    if (rc) return rc;
+    if (M == 0) return ok();
+    if (!x || !h || !workspace) return fail(W4_EINVAL, "null x, h or workspace");
+    if (!aligned16(x) || !aligned16(h) || !aligned16(workspace))
+        return fail(W4_EALIGN, "x, h and workspace must be 16-byte aligned");
+    const size_t need = w4_ffn_gate_up_workspace_bytes(gate, M);
+    if (workspace_bytes < need)
+        return fail(W4_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    float* g = (float*)workspace;
+    float* u = (float*)((uint8_t*)workspace + need / 2);
+    return hip_status(ffn_gate_up_launches(gate, up, x, M, h, g, u, g_ffn_path.load(), (hipStream_t)stream),
+                      "ffn gate/up launch");
+}
+
 int w4a16_ffn(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down, const uint16_t* x,
               int64_t M, uint16_t* h, float* y, void* workspace, size_t workspace_bytes,
               void* stream) {
-    int rc;
-    if ((rc = check_matrix(gate, "gate", 1)) || (rc = check_matrix(up, "up", 1)) ||
-        (rc = check_matrix(down, "down", 1)))
-        return rc;
-    if (gate->scheme != up->scheme || gate->scheme != down->scheme)
-        return fail(W4_ESHAPE, "gate, up and down must share one scheme");
+    int rc = ffn_check_gate_up(gate, up, M);
+    if (rc || (rc = check_matrix(down, "down", 1))) return rc;
+    if (gate->scheme != down->scheme) return fail(W4_ESHAPE, "gate, up and down must share one scheme");
     const int64_t D = gate->K, F = gate->N;
-    if (up->N != F || up->K != D || down->N != D || down->K != F)
-        return fail(W4_ESHAPE, "gate and up must be [F][D], down [D][F] (F=%lld, D=%lld)",
-                    (long long)F, (long long)D);
-    if (M < 0 || M > 64) return fail(W4_ESHAPE, "M=%lld out of range [0, 64]", (long long)M);
+    if (down->N != D || down->K != F)
+        return fail(W4_ESHAPE, "down must be [D][F] = [%lld][%lld]", (long long)D, (long long)F);
     if (M == 0) return ok();
-    if (D > w4::kMaxSkinnyK || F > w4::kMaxSkinnyK)
-        return fail(W4_ESHAPE, "D=%lld and F=%lld must not exceed %lld", (long long)D, (long long)F,
-                    (long long)w4::kMaxSkinnyK);
     if (!x || !y || !workspace) return fail(W4_EINVAL, "null x, y or workspace");
     if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || (h && !aligned16(h)))
         return fail(W4_EALIGN, "x, y, h and workspace must be 16-byte aligned");
@@ -549,25 +604,9 @@ int w4a16_ffn(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
         if (e != hipErrorNotSupported) return hip_status(e, "ffn launch");
         // refused before launching anything: the launches below
     }
-    hipError_t e = hipErrorNotSupported;
-    if (M == 1 && path != W4_FFN_PATH_SEQUENCE) {
-        // gate/up rows with the activation in their epilogue, then down
-        e = w4::launch_ffn_gate_up(scheme, G, U, D, F, x, hh, st);
-        if (e != hipSuccess && e != hipErrorNotSupported) return hip_status(e, "ffn gate/up launch");
-    }
-    if (e == hipErrorNotSupported) {
-        // gate and up in one GEMV launch, the activation, then down
-        float* g = (float*)(base + L.g);
-        float* u = (float*)(base + L.u);
-        const void* c2[2] = {gate->codes, up->codes};
-        const void* s2[2] = {gate->scale, up->scale};
-        const void* b2[2] = {gate->bias, up->bias};
-        const int64_t N2[2] = {F, F};
-        float* y2[2] = {g, u};
-        e = gemv_multi_dispatch(scheme, 2, c2, s2, b2, N2, D, x, M, y2, st);
-        if (e == hipSuccess) e = w4::launch_ffn_act(g, u, hh, M * F, st);
-        if (e != hipSuccess) return hip_status(e, "ffn gate/up launches");
-    }
+    hipError_t e = ffn_gate_up_launches(gate, up, x, M, hh, (float*)(base + L.g),
+                                        (float*)(base + L.u), path, st);
+    if (e != hipSuccess) return hip_status(e, "ffn gate/up launches");
     if (M >= 2 && M <= 16 && w4::gemv_mfma_split_bytes(scheme, D, F, M) > 0)
         e = w4::launch_gemv_mfma(scheme, 1, &Dn[0], &Dn[1], &Dn[2], &D, F, hh, M, &y, st,
                                  (float*)(base + L.part));

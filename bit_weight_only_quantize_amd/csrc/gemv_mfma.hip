@@ -51,8 +51,11 @@ struct LdsPlan {
     size_t lds = 0;
 };
 
+// gated: tiles come in (gate, up) pairs that one workgroup must hold together,
+// so TP is even and x must fit in one pass (no chunks, no K parts)
 template <int S>
-static bool plan_mfma_lds(int tiles, int64_t K, int64_t M, bool split, LdsPlan& P) {
+static bool plan_mfma_lds(int tiles, int64_t K, int64_t M, bool split, LdsPlan& P,
+                          bool gated = false) {
     constexpr int kCUs = 256, kWaves = 16;
     constexpr size_t kLds = 160 * 1024;
     if (tiles == 0) return false;
@@ -63,9 +66,14 @@ static bool plan_mfma_lds(int tiles, int64_t K, int64_t M, bool split, LdsPlan& 
     // a run of CS steps on TP tiles per workgroup: the K-slice split WK puts
     // about 24 steps of code loads in flight per CU; returns the LDS bytes
     // (activations, sums and scale blocks), 0 if they do not fit
+    int TP1 = (tiles + kCUs - 1) / kCUs;
+    // the K-slice split follows the tiles per CU before a gated plan rounds
+    // TP up to even, so that gated and plain launches sum in the same order
+    const int tp_wk = TP1;
     auto fit = [&](LdsPlan& q) -> size_t {
         const int depth = q.chunked ? 2 : 4;
-        int WK = (24 + q.TP * depth / 2) / (q.TP * depth);
+        const int tpw = gated ? tp_wk : q.TP;
+        int WK = (24 + tpw * depth / 2) / (tpw * depth);
         WK = std::max(1, std::min({WK, kWaves / q.TP, q.CS}));
         // every K-slice of a full run non-empty
         while (WK > 1 && (WK - 1) * ((q.CS + WK - 1) / WK) >= q.CS) --WK;
@@ -76,9 +84,17 @@ static bool plan_mfma_lds(int tiles, int64_t K, int64_t M, bool split, LdsPlan& 
         q.SG = sgmax <= 16 ? 16 : sgmax <= 32 ? 32 : sgmax <= 64 ? 64 : 128;
         size_t lds = MfmaLdsLayout<S>((int)K, (int)M, q.CS).bytes() + (size_t)q.TP * WK * 16 * (q.SG + 1) * 4;
         lds = std::max(lds, WK > 1 ? (size_t)q.TP * WK * 64 * 16 : (size_t)0);
+        if (gated) lds = std::max(lds, (size_t)q.TP * 64 * 16);  // the pairs' hand-over
         return lds <= kLds ? lds : 0;
     };
-    const int TP1 = (tiles + kCUs - 1) / kCUs;
+    // an odd TP would have to grow by one: fewer workgroups than CUs for the
+    // same rows measured slower than the plain launch plus the activation
+    // (13B gate/up at M = 8: 7 -> 8 tiles per workgroup); one tile per CU
+    // becomes two on half the CUs
+    if (gated && (TP1 & 1)) {
+        if (TP1 > 1) return false;
+        TP1 = 2;
+    }
     if (TP1 > kWaves) return false;
     LdsPlan q;
     q.TP = TP1;
@@ -88,6 +104,7 @@ static bool plan_mfma_lds(int tiles, int64_t K, int64_t M, bool split, LdsPlan& 
         P = q;
         return true;
     }
+    if (gated) return false;
     // x does not fit. With room for partial outputs: K parts on different
     // CUs, each part's x one chunk; the plan with the fewest code steps per
     // CU (TP x part steps), the fewest parts on a tie, all in one round of
@@ -121,6 +138,68 @@ static bool plan_mfma_lds(int tiles, int64_t K, int64_t M, bool split, LdsPlan& 
         }
     }
     return false;
+}
+
+template <int S>
+static bool try_mfma_gated(const void* const* codes, const void* const* scale,
+                           const void* const* bias, int64_t N, int64_t K, const uint16_t* x,
+                           int64_t M, uint16_t* h, hipStream_t st) {
+    constexpr size_t kLds = 160 * 1024;
+    GemvGroupArgs a{};
+    for (int i = 0; i < 2; ++i) {
+        a.codes[i] = (const uint8_t*)codes[i];
+        a.scale[i] = (const uint8_t*)scale[i];
+        a.bias[i] = (const uint8_t*)bias[i];
+        a.N[i] = (int)N;
+    }
+    a.count = 2;
+    a.h = h;
+    const int tiles = 2 * (int)((N + 15) / 16);
+    LdsPlan P;
+    if (!plan_mfma_lds<S>(tiles, K, M, false, P, true)) return false;
+    auto go = [&](auto kern) {
+        if (P.lds > 64 * 1024)
+            (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+        hipLaunchKernelGGL(kern, dim3(P.grid), dim3(1024), P.lds, st, a, (int)K, (int)M, x, tiles,
+                           P.TP, P.WK, P.CS, P.KP, (float*)nullptr);
+    };
+    // the same depth / staging choices as the plain launch below
+    auto by_depth = [&](auto sgc) {
+        constexpr int G = decltype(sgc)::value;
+        if constexpr (G <= 32 && S != AFF4_G64) {
+            if (M >= 12) {
+                if (P.spw >= 4) go(gemv_mfma_lds_kernel<S, 4, G, false, false, 8, true>);
+                else go(gemv_mfma_lds_kernel<S, 2, G, false, false, 8, true>);
+                return;
+            }
+        }
+        // (the affine 4-bit variant with 128-group scale blocks takes two steps
+        // in flight: with four, the pairs' hand-over spills a register)
+        if constexpr (!(S == AFF4_G64 && G == 128)) {
+            if (P.spw >= 4) {
+                go(gemv_mfma_lds_kernel<S, 4, G, false, false, 4, true>);
+                return;
+            }
+        }
+        go(gemv_mfma_lds_kernel<S, 2, G, false, false, 4, true>);
+    };
+    if (P.SG == 16) by_depth(std::integral_constant<int, 16>{});
+    else if (P.SG == 32) by_depth(std::integral_constant<int, 32>{});
+    else if (P.SG == 64) by_depth(std::integral_constant<int, 64>{});
+    else by_depth(std::integral_constant<int, 128>{});
+    return true;
+}
+
+hipError_t launch_gemv_mfma_gated(int scheme, const void* const* gate, const void* const* up,
+                                  int64_t N, int64_t K, const uint16_t* x, int64_t M, uint16_t* h,
+                                  hipStream_t st) {
+    if (!gemv_mfma_ok(scheme, K, M) || scheme == AFF8_G64 || N <= 0) return hipErrorNotSupported;
+    const void* c[2] = {gate[0], up[0]};
+    const void* s[2] = {gate[1], up[1]};
+    const void* b[2] = {gate[2], up[2]};
+    const bool ok = scheme == SYM4_G128 ? try_mfma_gated<SYM4_G128>(c, s, b, N, K, x, M, h, st)
+                                        : try_mfma_gated<AFF4_G64>(c, s, b, N, K, x, M, h, st);
+    return ok ? hipGetLastError() : hipErrorNotSupported;
 }
 
 template <int S>

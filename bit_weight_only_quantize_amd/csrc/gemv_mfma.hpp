@@ -416,7 +416,14 @@ __device__ __forceinline__ int lds_swz(int mp, int lr) {
 // tile, as one chunk, and writes its partial outputs to part + p * M * N
 // ([M][N]). A template switch, so that the other launches keep constant
 // chunk offsets.
-template <int S, int DEPTH, int SGMAX, bool CHUNKED, bool PARTS = false, int UW = 4>
+//
+// GATED (one pass, no K parts): matrices 0 (gate) and 1 (up) of equal N, tiles
+// interleaved (tile 2j = rows 16j.. of gate, 2j + 1 the same rows of up) with
+// an even TP, so a workgroup holds both halves of each pair; the up wavefront
+// hands its tile to the gate wavefront through LDS, which stores
+// h = bf16(gelu_tanh(g) * u) to a.h instead of y.
+template <int S, int DEPTH, int SGMAX, bool CHUNKED, bool PARTS = false, int UW = 4,
+          bool GATED = false>
 __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, int K, int M,
                                                               const uint16_t* x, int tiles,
                                                               int TP, int WK, int CS, int KP,
@@ -449,11 +456,15 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
     const int tile_raw = ((int)blockIdx.x - kp * gpp) * TP + tw;
     const int tile = min(tile_raw, tiles - 1);
     int i = 0;
+    if constexpr (GATED) {
+        i = tile & 1;
+    } else {
 #pragma unroll
-    for (int q = 1; q < kMaxGroup; ++q)
-        if (q < a.count && tile >= a.tile_start[q]) i = q;
+        for (int q = 1; q < kMaxGroup; ++q)
+            if (q < a.count && tile >= a.tile_start[q]) i = q;
+    }
     const int N = a.N[i];
-    const int row0 = (tile - a.tile_start[i]) * 16;
+    const int row0 = GATED ? (tile >> 1) * 16 : (tile - a.tile_start[i]) * 16;
     const uint8_t* codes = a.codes[i];
     const uint8_t* scale = a.scale[i];
     const uint8_t* bias = a.bias[i];
@@ -709,6 +720,24 @@ __global__ __launch_bounds__(1024) void gemv_mfma_lds_kernel(GemvGroupArgs a, in
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] += o[r];
         }
+    }
+    if constexpr (GATED) {
+        // pairs meet: the up wavefront parks its tile, the gate wavefront
+        // (tw even, its partner tw + 1 in this workgroup) finishes the pair
+        __syncthreads();  // LDS reads of the reduction / activations are done
+        if (i == 1) *reinterpret_cast<f32x4_t*>(lds + 4 * (tw * 64 + lane)) = acc;
+        __syncthreads();
+        if (i == 1 || tile_raw >= tiles) return;
+        const f32x4_t u = *reinterpret_cast<const f32x4_t*>(lds + 4 * ((tw + 1) * 64 + lane));
+        const int nn = row0 + c16;
+        if (nn < N) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * g + r;
+                if (m < M) a.h[(int64_t)m * N + nn] = (uint16_t)f32_to_bf16_rne(gelu_tanh(acc[r]) * u[r]);
+            }
+        }
+        return;
     }
     if (tile_raw >= tiles) return;
     float* y = PARTS ? part + (int64_t)kp * M * N : a.y[i];

@@ -42,6 +42,7 @@ struct GemvGroupArgs {
     int N[kMaxGroup];
     int tile_start[kMaxGroup + 1];  // first block of each matrix; tile_start[count] = grid
     int count;
+    uint16_t* h;  // gated launches: bf16(gelu_tanh(y[0]) * y[1]) [M][N] instead of y
 };
 
 // Opaque VGPR copy of a constant: keeps the compiler from folding it into

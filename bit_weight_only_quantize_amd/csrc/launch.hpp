@@ -36,6 +36,13 @@ hipError_t launch_gemv_mfma(int scheme, int count, const void* const* codes,
                             const void* const* scale, const void* const* bias, const int64_t* N,
                             int64_t K, const uint16_t* x, int64_t M, float* const* y,
                             hipStream_t st, float* part = nullptr);
+// gate and up ([N][K] each, 4-bit) for 2 <= M <= 16 in one launch whose
+// epilogue writes h = bf16(gelu_tanh(gate x) * (up x)), bf16 [M][N]; the
+// same bits as the two GEMVs and the activation. hipErrorNotSupported
+// (nothing launched) where x does not fit one pass.
+hipError_t launch_gemv_mfma_gated(int scheme, const void* const* gate, const void* const* up,
+                                  int64_t N, int64_t K, const uint16_t* x, int64_t M, uint16_t* h,
+                                  hipStream_t st);
 // bytes of partial outputs the K-part plan needs (0: no K parts for this shape)
 size_t gemv_mfma_split_bytes(int scheme, int64_t N, int64_t K, int64_t M);
 

@@ -327,8 +327,19 @@ int w4a16_ffn(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
               const uint16_t* x, int64_t M, uint16_t* h, float* y, void* workspace,
               size_t workspace_bytes, void* stream);
 
-/* Host-side setting read by later w4a16_ffn calls from any thread (W4_EINVAL
- * for another value). */
+/*
+ * The gate/up half of w4a16_ffn on its own: h = bf16(gelu_tanh(W_gate x) *
+ * (W_up x)), bf16 [M][F] (required), the launches w4a16_ffn takes for that half
+ * (one for one token with a 4-bit scheme and D / 32 <= 256, else a GEMV launch
+ * and the activation). workspace: at least w4_ffn_gate_up_workspace_bytes(gate,
+ * M) bytes, contents irrelevant. Same limits and errors as w4a16_ffn.
+ */
+size_t w4_ffn_gate_up_workspace_bytes(const w4_matrix* gate, int64_t M);
+int w4a16_ffn_gate_up(const w4_matrix* gate, const w4_matrix* up, const uint16_t* x, int64_t M,
+                      uint16_t* h, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-side setting read by later w4a16_ffn and w4a16_ffn_gate_up calls from
+ * any thread (W4_EINVAL for another value). */
 #define W4_FFN_PATH_DEFAULT 0       /* two launches for one token where they apply */
 #define W4_FFN_PATH_SINGLE_LAUNCH 1 /* one persistent launch for one token where it applies */
 #define W4_FFN_PATH_SEQUENCE 2      /* always the three-launch sequence */

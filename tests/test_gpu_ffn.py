@@ -195,3 +195,37 @@ def test_withheld_flag_gives_up_and_the_workspace_recovers():
     y2 = w4.ffn(gate, up, down, x, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("M,D,F,scheme", [(1, 4096, 11008, "sym4_g128"), (4, 4096, 11008, "sym4_g128"),
+                                          (1, 2048, 768, "aff4_g64")])
+def test_gate_up_half_equals_the_ffn_h(M, D, F, scheme):
+    print(f"[ffn] gate/up half M={M} D={D} F={F}", flush=True)
+    _, (gate, up, down) = _ffn(D, F, scheme, f"ffn.{D}.{F}.{scheme}")
+    x = dev_bf16(synth.activations_bf16(M, D, 31, f"ffn.xh.{M}"))
+    _, h_ref = w4.ffn(gate, up, down, x, want_h=True)
+    h = w4.ffn_gate_up(gate, up, x)
+    torch.cuda.synchronize()
+    assert torch.equal(h.view(torch.int16), h_ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,D,F,scheme", [
+    (4, 4096, 11008, "sym4_g128"),   # 7B: 6 tile pairs per workgroup
+    (16, 4096, 11008, "sym4_g128"),
+    (13, 4096, 11008, "sym4_g128"),  # 8 staging loads in flight per lane
+    (4, 2048, 4096, "aff4_g64"),     # affine regrouping, 2 tiles per workgroup
+    (2, 2048, 768, "aff4_g64"),      # 1 tile per CU becomes a pair on half the CUs
+    (8, 5120, 13824, "aff4_g64"),    # 13B: 7 tiles per CU, so gate/up + activation launches
+])
+def test_several_tokens_gated_launch_equals_the_sequence(M, D, F, scheme):
+    """Several tokens: gate and up in one skinny launch whose epilogue writes h
+    (tile pairs in one workgroup) against gate/up GEMV + activation launches."""
+    print(f"[ffn] gated M={M} D={D} F={F} {scheme}", flush=True)
+    _, (gate, up, down) = _ffn(D, F, scheme, f"ffn.{D}.{F}.{scheme}")
+    x = dev_bf16(synth.activations_bf16(M, D, 33, f"ffn.xq.{M}"))
+    y0, h0 = w4.ffn(gate, up, down, x, want_h=True)
+    y1, h1 = _with_path(w4.FFN_PATH_SEQUENCE, lambda: w4.ffn(gate, up, down, x, want_h=True))
+    torch.cuda.synchronize()
+    assert torch.equal(h0.view(torch.int16), h1.view(torch.int16))
+    assert torch.equal(y0, y1)
+
