@@ -44,9 +44,7 @@ LLAMA13B = [("wq", 5120, 5120), ("wk", 5120, 5120), ("wv", 5120, 5120), ("wo", 5
             ("gate", 13824, 5120), ("up", 13824, 5120), ("down", 5120, 13824)]
 
 
-GEMV_WAVE_SOURCES = ("common.hpp", "launch.hpp", "skinny.hpp", "gemv_wave.hpp", "gemv.hip")
 GEMM_SOURCES = ("common.hpp", "launch.hpp", "gemm.hip")
-FFN_SOURCES = ("common.hpp", "launch.hpp", "skinny.hpp", "gemv_wave.hpp", "handoff.hpp", "ffn.hip")
 
 
 def weight_bytes(scheme: str, N: int, K: int) -> int:
@@ -205,17 +203,29 @@ def kernel_sources_digest(files):
     return h.hexdigest()
 
 
-def measured_traffic(profile, files):
-    """HBM bytes per launch from a committed counter summary (a line
-    `traffic_bytes_per_launch: <int> sources_sha256: <hex>`), or None when the
-    summary is missing or the kernel has changed since."""
-    path = os.path.join(ROOT, "profiles", profile)
+def library_digest():
+    """sha256 over every library source file (name and bytes, sorted by name)."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "bit_weight_only_quantize_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key):
+    """HBM bytes per launch (or per layer) for `key` from the committed counter
+    summary (a line `traffic <key>: <int> sources_sha256: <hex>`), or None when it
+    is missing or any library source has changed since the counters were taken."""
     try:
-        text = open(path).read()
+        text = open(os.path.join(ROOT, "profiles", "hbm_counters.md")).read()
     except OSError:
         return None
-    m = __import__("re").search(r"traffic_bytes_per_launch:\s*(\d+)\s+sources_sha256:\s*([0-9a-f]{64})", text)
-    if not m or m.group(2) != kernel_sources_digest(files):
+    m = __import__("re").search(r"traffic " + __import__("re").escape(key) +
+                                r":\s*(\d+)\s+sources_sha256:\s*([0-9a-f]{64})", text)
+    if not m or m.group(2) != library_digest():
         return None
     return int(m.group(1))
 
@@ -269,7 +279,7 @@ def decode_stack(c: Ctx, shapes, scheme, layers, M, head=None, ffn="layer"):
         for m in mats:
             if ffn == "single" and M == 1:
                 ffn_call(m)
-            elif ffn == "layer" and M == 1:
+            elif ffn == "layer":
                 w4.ffn_gate_up(m["gate"], m["up"], xs[d], h=hbuf, workspace=gu_ws)
             else:
                 w4.gemv_multi_into([m["gate"], m["up"]], xs[d], [ys["gate"], ys["up"]])
@@ -277,9 +287,9 @@ def decode_stack(c: Ctx, shapes, scheme, layers, M, head=None, ffn="layer"):
     per_layer = (gemv_bytes(scheme, [(d, d)] * 3, M) + gemv_bytes(scheme, [(d, d)], M)
                  + gemv_bytes(scheme, [(f, d)] * 2, M) + gemv_bytes(scheme, [(d, f)], M))
     step_bytes = layers * per_layer + (gemv_bytes(scheme, [(head[0], head[1])], M) if head else 0)
-    if ffn == "layer" and M == 1:
+    if ffn == "layer":
         # gate and up weights, x, h written
-        dom_bytes = 2 * weight_bytes(scheme, f, d) + 2 * d + 2 * f
+        dom_bytes = 2 * weight_bytes(scheme, f, d) + 2 * M * d + 2 * M * f
     elif ffn == "single" and M == 1:
         # weights of all three, x, h written once and read by the down rows, y
         dom_bytes = (2 * weight_bytes(scheme, f, d) + weight_bytes(scheme, d, f) + 2 * d
@@ -391,14 +401,16 @@ def run_llama(c: Ctx, a, big: bool):
     out["tok_per_s"] = round(M / (ms * 1e-3), 1)
     out["step_bytes"] = step_bytes
     traffic = None
+    if layers == (40 if big else 32) and scheme == ("aff4_g64" if big else "sym4_g128"):
+        traffic = measured_traffic(f"{'llama13b' if big else 'llama7b'}_m{M}/ffn_gate_up")
     if fused1:
-        if not big and layers == 32 and scheme == "sym4_g128":
-            traffic = measured_traffic("ffn_llama7b_counters.md", FFN_SOURCES)
+        traffic = None
         kname = f"ffn_kernel (gate+up 2 x {f}x{d}, gelu, down {d}x{f}, {scheme}, one launch)"
     elif a.ffn == "layer" and M == 1:
-        if not big and layers == 32 and scheme == "sym4_g128":
-            traffic = measured_traffic("ffn_gate_up_llama7b_counters.md", FFN_SOURCES)
         kname = f"ffn_gate_up_kernel (gate+up 2 x {f}x{d} {scheme}, gelu epilogue, one launch)"
+    elif a.ffn == "layer":
+        kname = (f"w4a16_ffn_gate_up (gate+up 2 x {f}x{d} {scheme}, gelu: the gated skinny launch, "
+                 "or where its tile pairs do not fit the GEMV launch + the activation launch)")
     else:
         kname = f"gate+up GEMV (2 x {f}x{d} {scheme}, one launch)"
     out["roofline"] = hbm_roofline(kname, dom_bytes, us_dom, traffic)
@@ -477,7 +489,10 @@ def run_moe(c: Ctx, a):
     out["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
     out["distinct_experts_per_layer"] = sum(distinct) / len(distinct)
     out["step_bytes"] = step_bytes
-    out["roofline"] = hbm_roofline(f"whole MoE layer ({launches})", step_bytes // layers, ms * 1e3 / layers)
+    traffic = (measured_traffic(f"moe_m{M}/layer")
+               if a.moe_path == "layer" and layers == 30 and M in (1, 32) else None)
+    out["roofline"] = hbm_roofline(f"whole MoE layer ({launches})", step_bytes // layers, ms * 1e3 / layers,
+                                   traffic)
     return out
 
 
@@ -543,7 +558,9 @@ def run_kv(c: Ctx, a):
     res["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
     res["tok_per_s"] = round(1 / (ms * 1e-3), 1)
     res["step_bytes"] = step_bytes
-    res["roofline"] = hbm_roofline(f"kv_scores_kernel ({Hq} heads x {Tn} positions, INT4 keys)", scores_b, us_dom)
+    traffic = measured_traffic("kv/scores") if layers == 32 and T == 8192 else None
+    res["roofline"] = hbm_roofline(f"kv_scores_kernel ({Hq} heads x {Tn} positions, INT4 keys)", scores_b, us_dom,
+                                   traffic)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = kv_cpu_baseline(L[0], q, p, a.cpu_seconds, Tn)
     return res

@@ -138,7 +138,12 @@ __device__ __forceinline__ void mfma_tiles(const MfmaTile (&tl)[WR * RT], int K,
 #pragma unroll
     for (int k = 0; k < SR; ++k) {
         const int r = min(wave + NW * k, ROWS - 1);
-        const MfmaTile& tt = tl[r / 16];
+        // the row's tile by selects (a runtime index into the tile array
+        // would put the array in scratch memory)
+        MfmaTile tt = tl[0];
+#pragma unroll
+        for (int q = 1; q < WR * RT; ++q)
+            if (r / 16 == q) tt = tl[q];
         const int n = min(tt.row0 + r % 16, tt.N - 1);
 #pragma unroll
         for (int j = 0; j < SL; ++j) {
@@ -158,7 +163,10 @@ __device__ __forceinline__ void mfma_tiles(const MfmaTile (&tl)[WR * RT], int K,
     uint32_t coff[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const MfmaTile& tt = tl[wr * RT + rt];
+        MfmaTile tt = tl[rt];
+#pragma unroll
+        for (int q = 1; q < WR; ++q)
+            if (wr == q) tt = tl[q * RT + rt];
         const int n = min(tt.row0 + c16, tt.N - 1);
         cb[rt] = tt.codes;
         coff[rt] = (uint32_t)n * (uint32_t)(K / 2);

@@ -48,122 +48,13 @@ __global__ __launch_bounds__(64) void topk_softmax_kernel(const float* __restric
     topk_rounds<EPL>(v, E, k, ids + (int64_t)m * k, wts + (int64_t)m * k);
 }
 
-// Router GEMV and top-k fused, one 1024-thread workgroup per token (E <= 128):
-// wavefront w computes logits of rows 8w .. 8w+7 as the M = 1 wave GEMV does
-// (activations staged in LDS by every wavefront, issued ahead of its code
-// loads; DPP row sums), writes them to LDS and to `logits`, then wavefront 0
-// selects. One launch and no round trip of the logits through memory.
-constexpr int kRouteRows = 8;  // rows per wavefront, 16 wavefronts
-template <int S, int NV>
-__global__ __launch_bounds__(1024) void route_fused_kernel(const uint8_t* __restrict__ codes,
-                                                           const uint8_t* __restrict__ scale,
-                                                           const uint8_t* __restrict__ bias, int E,
-                                                           int K, const uint16_t* x, int k,
-                                                           float* __restrict__ logits,
-                                                           int32_t* __restrict__ ids,
-                                                           float* __restrict__ wts) {
-    using T = Traits<S>;
-    using L = XLayout<S, 1>;
-    constexpr int R = kRouteRows;
-    extern __shared__ __align__(16) uint32_t smem[];
-    __shared__ float ls[128];
-    const int m = blockIdx.x;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int VR = K / T::KV;
-    const int64_t rowbytes = (int64_t)K * T::BITS / 8;
-    const int64_t groups = K / T::GROUP;
-    constexpr int SB = T::AFFINE ? 2 : 4;
-    const uint16_t* xm = x + (int64_t)m * K;
-    uint32_t* xs = smem;
-    float* XS = reinterpret_cast<float*>(smem + K / 2);
-
-    XStage<S, 1, 1024> xstage;  // VR <= 64 * NV <= 1024 vectors
-    xstage.fetch(xm, VR, threadIdx.x);
-    asm volatile("" ::: "memory");  // keep the code loads behind these
-
-    u32x4_t c[R][NV];
-    float sc[R][NV], bi[R][NV];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int64_t n = min(wave * R + r, E - 1);
-        const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(codes + n * rowbytes);
-        const uint8_t* sp = scale + n * groups * SB;
-        const uint8_t* bp = T::AFFINE ? bias + n * groups * 2 : nullptr;
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int v = min(lane + 64 * j, VR - 1);
-            c[r][j] = __builtin_nontemporal_load(cp + v);
-            const int g = v / T::VPG;
-            if constexpr (T::AFFINE) {
-                sc[r][j] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(sp)[g]);
-                bi[r][j] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(bp)[g]);
-            } else {
-                sc[r][j] = reinterpret_cast<const float*>(sp)[g];
-            }
-        }
-    }
-    xstage.commit(VR, xs, XS, threadIdx.x);  // waits for the activations only
-    __syncthreads();
-
-    const uint32_t MASK = opaque(0x000F000Fu);
-    const uint32_t MAGIC = unpack_magic<S>();
-    float acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int v = lane + 64 * j;
-        if (v >= VR) break;
-        uint32_t xp[L::XW];
-        read_pairs<S>(xs, v, xp);
-        const float X = XS[v];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            acc[r] = apply_group<S>(acc[r], dot_code_vector<S>(c[r][j], xp, MASK, MAGIC), X,
-                                    sc[r][j], T::AFFINE ? bi[r][j] : 0.f);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const float tot = wave_sum_to_lane63(acc[r]);
-        const int n = wave * R + r;
-        if (lane == 63 && n < E) {
-            ls[n] = tot;
-            logits[(int64_t)m * E + n] = tot;
-        }
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    float v[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) v[j] = lane + 64 * j < E ? ls[lane + 64 * j] : -INFINITY;
-    topk_rounds<2>(v, E, k, ids + (int64_t)m * k, wts + (int64_t)m * k);
-}
-
 hipError_t launch_route(int scheme, const void* codes, const void* scale, const void* bias,
                         int64_t E, int64_t K, const uint16_t* x, int64_t M, int k, float* logits,
                         int32_t* ids, float* wts, hipStream_t st) {
-    const int kv = scheme == AFF8_G64 ? 16 : 32;
-    const int64_t VR = K / kv;
-    // Fused only for several tokens: one workgroup streams the whole router and
-    // runs the kernel's (large, unrolled) code on a cold CU, which costs more
-    // than a second launch when there is a single token (measured: M = 1 12.7
-    // vs 5.6 us; M = 32 13.1 vs 21.8 us).
-    if (M >= 16 && E <= 16 * kRouteRows && VR >= 1 && VR <= 128) {
-        const size_t lds = (size_t)(K / 2 + VR) * 4;
-        const int nv = VR <= 64 ? 1 : 2;
-        auto go = [&](auto kern) {
-            hipLaunchKernelGGL(kern, dim3((unsigned)M), dim3(1024), lds, st, (const uint8_t*)codes,
-                               (const uint8_t*)scale, (const uint8_t*)bias, (int)E, (int)K, x, k,
-                               logits, ids, wts);
-        };
-        switch (scheme) {
-            case SYM4_G128: nv == 1 ? go(route_fused_kernel<SYM4_G128, 1>) : go(route_fused_kernel<SYM4_G128, 2>); break;
-            case AFF4_G64: nv == 1 ? go(route_fused_kernel<AFF4_G64, 1>) : go(route_fused_kernel<AFF4_G64, 2>); break;
-            default: nv == 1 ? go(route_fused_kernel<AFF8_G64, 1>) : go(route_fused_kernel<AFF8_G64, 2>); break;
-        }
-        return hipGetLastError();
-    }
+    // The router GEMV, then one single-wavefront workgroup per token. (One
+    // 1024-thread workgroup per token streaming the router and selecting
+    // without the logits' round trip through memory measured slower in the
+    // Gemma-shaped layer at 32 tokens: 16.9 us against 6.1 + 4.7 us.)
     hipError_t e = launch_gemv(scheme, codes, scale, bias, E, K, x, M, logits, st);
     if (e != hipSuccess) return e;
     if (E <= 128)
