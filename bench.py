@@ -87,6 +87,9 @@ def parse():
                     help="llama stacks: the FFN through w4a16_ffn (h feeds down) with its default "
                          "launches, w4a16_ffn with the single persistent launch for one token, or "
                          "gate+up and down as separate GEMV calls with their own inputs")
+    ap.add_argument("--kv-append", default="fused", choices=["fused", "separate"],
+                    help="kv: the new K and V quantized inside the scores and weighted-sum launches "
+                         "(w4_kv_scores_append, w4_kv_weighted_sum_append), or by w4_kv_append first")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run a plain 1 GiB copy (for scaling HBM byte counters), then the workload")
     ap.add_argument("--dominant-only", action="store_true",
@@ -499,10 +502,13 @@ def run_moe(c: Ctx, a):
 # ---------------------------------------------------------------- INT4 KV cache
 def run_kv(c: Ctx, a):
     """Decode over an INT4 KV cache (Shimmy article §3.2, TurboShimmy): per layer,
-    append the new token's K and V vectors (quantize, one launch), then the fused-dequant
-    scores over the T + 1 cached keys and the weighted sum over the T + 1 cached
-    values. The weights are a fixed softmax of random logits: the softmax itself
-    is not a library operation. Llama-7B-shaped: 32 layers, 32 heads of 128."""
+    append the new token's K and V vectors (quantize), the fused-dequant scores over
+    the T + 1 cached keys and the weighted sum over the T + 1 cached values. By
+    default the key append runs inside the scores launch and the value append
+    inside the weighted-sum launch; `--kv-append separate` appends both first in a
+    launch of their own. The weights are a fixed softmax of random logits: the
+    softmax itself is not a library operation. Llama-7B-shaped: 32 layers, 32
+    heads of 128."""
     torch, w4 = c.torch, c.w4
     layers = a.layers or 32
     Hq = Hkv = 32
@@ -528,21 +534,31 @@ def run_kv(c: Ctx, a):
     ws = torch.empty(w4.kv_weighted_sum_workspace_bytes(Hq, Tn), dtype=torch.uint8, device=c.dev)
     torch.cuda.synchronize()
 
+    fused = a.kv_append == "fused"
+
     def step():
         for kc, ks, vc, vs in L:
-            w4.kv_append(knew, vnew, (kc, ks), (vc, vs), T)
-            w4.kv_scores(q, kc, ks, Tn, out=scores)
-            w4.kv_weighted_sum(p, vc, vs, workspace=ws, out=out)
+            if fused:
+                w4.kv_scores_append(q, knew, kc, ks, T, out=scores)
+                w4.kv_weighted_sum_append(p, vnew, vc, vs, T, workspace=ws, out=out)
+            else:
+                w4.kv_append(knew, vnew, (kc, ks), (vc, vs), T)
+                w4.kv_scores(q, kc, ks, Tn, out=scores)
+                w4.kv_weighted_sum(p, vc, vs, workspace=ws, out=out)
 
     def dominant():
         for kc, ks, _, _ in L:
-            w4.kv_scores(q, kc, ks, Tn, out=scores)
+            if fused:  # rewrites position T with the same codes every time
+                w4.kv_scores_append(q, knew, kc, ks, T, out=scores)
+            else:
+                w4.kv_scores(q, kc, ks, Tn, out=scores)
 
     cache_b = Hkv * Tn * (D // 2 + 4)                  # one of K or V: codes + scales
     scores_b = cache_b + Hq * D * 4 + Hq * Tn * 4        # + q read + scores written
     wsum_b = cache_b + Hq * Tn * 4 + Hq * D * 4          # + weights read + out written
-    quant_b = 2 * Hkv * (D * 4 + D // 2 + 4)             # new K, V: fp32 in, codes + scale out
-    step_bytes = layers * (scores_b + wsum_b + quant_b)
+    quant1_b = Hkv * (D * 4 + D // 2 + 4)                # one new vector per head: fp32 in, codes + scale out
+    step_bytes = layers * (scores_b + wsum_b + 2 * quant1_b)
+    dom_b = scores_b + quant1_b if fused else scores_b
     g = c.graph(step)
     ms = c.time_graph(g, a.steps, a.warmup)
     g_dom = c.graph(dominant)
@@ -553,14 +569,18 @@ def run_kv(c: Ctx, a):
                         "workload": "llama7b-shaped INT4 KV cache decode, 32 layers", "layers": layers,
                         "heads_q": Hq, "heads_kv": Hkv, "head_dim": D, "context": Tn,
                         "cache_bytes": layers * 2 * cache_b,
-                        "launches_per_layer": "append K and V (one launch), scores, weighted sum (+ chunk add)"},
+                        "launches_per_layer": ("scores with the K append, weighted sum with the V append "
+                                               "(+ chunk add)" if fused else
+                                               "append K and V (one launch), scores, weighted sum (+ chunk add)")},
                     dtype="f32")
     res["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
     res["tok_per_s"] = round(1 / (ms * 1e-3), 1)
     res["step_bytes"] = step_bytes
-    traffic = measured_traffic("kv/scores") if layers == 32 and T == 8192 else None
-    res["roofline"] = hbm_roofline(f"kv_scores_kernel ({Hq} heads x {Tn} positions, INT4 keys)", scores_b, us_dom,
-                                   traffic)
+    traffic = (measured_traffic("kv/scores_append" if fused else "kv/scores")
+               if layers == 32 and T == 8192 else None)
+    res["roofline"] = hbm_roofline(f"kv_scores_kernel ({Hq} heads x {Tn} positions, INT4 keys"
+                                   + (", the new key appended in the same launch)" if fused else ")"),
+                                   dom_b, us_dom, traffic)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = kv_cpu_baseline(L[0], q, p, a.cpu_seconds, Tn)
     return res

@@ -59,7 +59,10 @@ _SIGS = {
     "w4_kv_quantize": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "w4_kv_append": ([_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "w4_kv_scores": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
+    "w4_kv_scores_append": ([_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "w4_kv_weighted_sum_workspace_bytes": ([_I64, _I64], ctypes.c_size_t),
+    "w4_kv_weighted_sum_append": ([_P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t,
+                                   _P], ctypes.c_int),
     "w4_kv_weighted_sum": ([_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, ctypes.c_size_t, _P],
                            ctypes.c_int),
     "w4a16_gemv_ws": ([ctypes.POINTER(_W4Matrix), _P, _I64, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
@@ -375,6 +378,22 @@ def kv_scores(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, T: int
     return out
 
 
+def kv_scores_append(q: torch.Tensor, k_new: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                     pos: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Quantize k_new fp32 [n][Hkv][128] (or [Hkv][128]) into the key cache at pos .. pos+n-1 and
+    return scores fp32 [Hq][pos+n] over every position (one launch for n <= 16)."""
+    if k_new.dtype != torch.float32 or not k_new.is_contiguous():
+        raise ValueError("k_new must be contiguous fp32")
+    n = 1 if k_new.dim() == 2 else k_new.shape[0]
+    Hq = q.shape[0]
+    Hkv, T_max = scales.shape
+    if out is None:
+        out = torch.empty((Hq, pos + n), dtype=torch.float32, device=q.device)
+    _check(lib().w4_kv_scores_append(_ptr(q), _ptr(k_new), n, Hq, Hkv, pos, T_max, _ptr(codes),
+                                     _ptr(scales), _ptr(out), _stream(q.device)))
+    return out
+
+
 def kv_weighted_sum_workspace_bytes(Hq: int, T: int) -> int:
     return int(lib().w4_kv_weighted_sum_workspace_bytes(Hq, T))
 
@@ -393,6 +412,29 @@ def kv_weighted_sum(p: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
     _check(lib().w4_kv_weighted_sum(_ptr(p), Hq, Hkv, T, T_max, _ptr(codes), _ptr(scales), _ptr(out),
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(p.device)))
+    return out
+
+
+def kv_weighted_sum_append(p: torch.Tensor, v_new: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                           pos: int, workspace: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Quantize v_new fp32 [n][Hkv][128] (or [Hkv][128]) into the value cache at pos .. pos+n-1 and
+    return out fp32 [Hq][128] = sum over t < pos+n = p.shape[1] of p[h][t] * dequant(V)[t]."""
+    if v_new.dtype != torch.float32 or not v_new.is_contiguous():
+        raise ValueError("v_new must be contiguous fp32")
+    n = 1 if v_new.dim() == 2 else v_new.shape[0]
+    Hq, T = p.shape
+    if T != pos + n:
+        raise ValueError(f"p covers {T} positions, pos + n = {pos + n}")
+    Hkv, T_max = scales.shape
+    if out is None:
+        out = torch.empty((Hq, KV_HEAD_DIM), dtype=torch.float32, device=p.device)
+    need = kv_weighted_sum_workspace_bytes(Hq, T)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=p.device)
+    _check(lib().w4_kv_weighted_sum_append(_ptr(p), _ptr(v_new), n, Hq, Hkv, pos, T_max, _ptr(codes),
+                                           _ptr(scales), _ptr(out), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(p.device)))
     return out
 
 

@@ -678,8 +678,32 @@ int w4_kv_scores(const float* q, int64_t Hq, int64_t Hkv, int64_t T, int64_t T_m
     if (T == 0) return ok();
     if (!q || !scores) return fail(W4_EINVAL, "null q or scores");
     if (!aligned16(q) || !aligned16(scores)) return fail(W4_EALIGN, "q and scores must be 16-byte aligned");
-    return hip_status(w4::launch_kv_scores(q, Hq, Hkv, T, T_max, codes, scales, scores, (hipStream_t)stream),
+    return hip_status(w4::launch_kv_scores(q, Hq, Hkv, T, T_max, codes, scales, scores, nullptr, 0,
+                                           (hipStream_t)stream),
                       "kv_scores launch");
+}
+
+int w4_kv_scores_append(const float* q, const float* k_new, int64_t n, int64_t Hq, int64_t Hkv,
+                        int64_t pos, int64_t T_max, uint8_t* k_codes, float* k_scales,
+                        float* scores, void* stream) {
+    int rc = kv_check_append(n, Hkv, pos, T_max);
+    if (rc) return rc;
+    if (n < 1) return fail(W4_ESHAPE, "n=%lld: at least one new position", (long long)n);
+    const int64_t T = pos + n;
+    rc = kv_check_cache(Hq, Hkv, T, T_max, k_codes, k_scales);
+    if (rc) return rc;
+    if (!q || !k_new || !scores) return fail(W4_EINVAL, "null q, k_new or scores");
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(scores))
+        return fail(W4_EALIGN, "q, k_new and scores must be 16-byte aligned");
+    const hipStream_t st = (hipStream_t)stream;
+    if (n <= w4::kKvFuseMax)
+        return hip_status(w4::launch_kv_scores(q, Hq, Hkv, T, T_max, k_codes, k_scales, scores, k_new,
+                                               pos, st),
+                          "kv_scores_append launch");
+    hipError_t e = w4::launch_kv_quantize(&k_new, 1, n, Hkv, pos, T_max, &k_codes, &k_scales, st);
+    if (e == hipSuccess)
+        e = w4::launch_kv_scores(q, Hq, Hkv, T, T_max, k_codes, k_scales, scores, nullptr, 0, st);
+    return hip_status(e, "kv_scores_append launches");
 }
 
 size_t w4_kv_weighted_sum_workspace_bytes(int64_t Hq, int64_t T) {
@@ -701,8 +725,38 @@ int w4_kv_weighted_sum(const float* p, int64_t Hq, int64_t Hkv, int64_t T, int64
                     workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(W4_EALIGN, "workspace must be 16-byte aligned");
     return hip_status(w4::launch_kv_weighted_sum(p, Hq, Hkv, T, T_max, codes, scales, out,
-                                                 (float*)workspace, (hipStream_t)stream),
+                                                 (float*)workspace, nullptr, 0, (hipStream_t)stream),
                       "kv_weighted_sum launch");
+}
+
+int w4_kv_weighted_sum_append(const float* p, const float* v_new, int64_t n, int64_t Hq,
+                              int64_t Hkv, int64_t pos, int64_t T_max, uint8_t* v_codes,
+                              float* v_scales, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    int rc = kv_check_append(n, Hkv, pos, T_max);
+    if (rc) return rc;
+    if (n < 1) return fail(W4_ESHAPE, "n=%lld: at least one new position", (long long)n);
+    const int64_t T = pos + n;
+    rc = kv_check_cache(Hq, Hkv, T, T_max, v_codes, v_scales);
+    if (rc) return rc;
+    if (!p || !v_new || !out) return fail(W4_EINVAL, "null p, v_new or out");
+    if (!aligned16(p) || !aligned16(v_new) || !aligned16(out))
+        return fail(W4_EALIGN, "p, v_new and out must be 16-byte aligned");
+    const size_t need = w4_kv_weighted_sum_workspace_bytes(Hq, T);
+    if (!workspace || workspace_bytes < need)
+        return fail(W4_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(W4_EALIGN, "workspace must be 16-byte aligned");
+    const hipStream_t st = (hipStream_t)stream;
+    if (n <= w4::kKvFuseMax)
+        return hip_status(w4::launch_kv_weighted_sum(p, Hq, Hkv, T, T_max, v_codes, v_scales, out,
+                                                     (float*)workspace, v_new, pos, st),
+                          "kv_weighted_sum_append launch");
+    hipError_t e = w4::launch_kv_quantize(&v_new, 1, n, Hkv, pos, T_max, &v_codes, &v_scales, st);
+    if (e == hipSuccess)
+        e = w4::launch_kv_weighted_sum(p, Hq, Hkv, T, T_max, v_codes, v_scales, out,
+                                       (float*)workspace, nullptr, 0, st);
+    return hip_status(e, "kv_weighted_sum_append launches");
 }
 
 }  // extern "C"

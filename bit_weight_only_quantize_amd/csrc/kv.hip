@@ -97,14 +97,55 @@ __device__ __forceinline__ float kv_dot32(const u32x4_t c, const float* qe, cons
     return acc;
 }
 
+// Positions pos .. T - 1 that arrive with the product's own launch (the append
+// fused into the product; pos == T: none). Their cached bytes are not read:
+// the lanes that handle a new position quantize it from the input, with the
+// arithmetic of kv_quantize_kernel, and use the codes and scale from registers;
+// the first query head of each kv group writes them into the cache. No lane of
+// the launch reads a position >= pos from the cache, so the writes race with
+// nothing.
+struct KvNew {
+    const float* x;   // [T - pos][Hkv][kKvHeadDim] fp32
+    uint8_t* codes;   // the cache the new positions go to
+    float* scales;
+    int pos;
+};
+
+// One new head vector quantized by the whole wavefront with the lane layout and
+// arithmetic of kv_quantize_kernel (lane l: elements 2l and 2l + 1, byte l; max
+// |v| by the same butterfly), then handed out in the products' layout: lane
+// (j, c) gets bytes 16c .. 16c + 15, i.e. elements 32c .. 32c + 31. s_out is the
+// vector's scale on every lane.
+__device__ __forceinline__ u32x4_t kv_quantize_wave(const float* __restrict__ src, int lane, float& s_out) {
+    const float2 e = reinterpret_cast<const float2*>(src)[lane];
+    float m = fmaxf(fabsf(e.x), fabsf(e.y));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float s = m / 7.5f;
+    auto code = [&](float a) -> uint32_t {
+        const float q = s > 0.f ? fminf(fmaxf(roundf(a / s), -8.f), 7.f) : 0.f;
+        return (uint32_t)((int)q + 8);
+    };
+    const uint32_t b = code(e.x) | (code(e.y) << 4);
+    // word i of the vector (bytes 4i .. 4i + 3) assembled on lane 4i
+    const uint32_t wd = b | (__shfl_down(b, 1) << 8) | (__shfl_down(b, 2) << 16) | (__shfl_down(b, 3) << 24);
+    const int c = lane & 3;
+    u32x4_t w;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) w[d] = __shfl(wd, 16 * c + 4 * d);
+    s_out = s;
+    return w;
+}
+
 template <int CHUNK, int DEPTH>
 __global__ __launch_bounds__(256) void kv_scores_kernel(const float* __restrict__ q, int Hq,
                                                         int group, int T, int64_t T_max,
                                                         const uint8_t* __restrict__ codes,
                                                         const float* __restrict__ scales,
-                                                        float* __restrict__ scores, int nch) {
+                                                        float* __restrict__ scores, int nch,
+                                                        KvNew nw) {
     const int lane = threadIdx.x & 63;
-    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);  // (chunk, head) with heads fastest
+    const int w = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (chunk, head) with heads fastest
     if (w >= nch * Hq) return;                           // whole wavefront
     const int h = w % Hq, ch = w / Hq;
     const int g = h / group;
@@ -118,33 +159,74 @@ __global__ __launch_bounds__(256) void kv_scores_kernel(const float* __restrict_
         qe[i] = e.x;
         qo[i] = e.y;
     }
-    float qs = 0.f;
+    // 8 * sum q, the same instructions wherever it is needed (exact: an fma or a
+    // product and a difference with it give the same bits); taken after the
+    // first cache loads are issued, so they do not wait for q
+    auto q8sum = [&]() {
+        float qs = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) qs += qe[i] + qo[i];
+        for (int i = 0; i < 16; ++i) qs += qe[i] + qo[i];
+        return 8.f * qs;
+    };
     const int t0 = ch * CHUNK;
     const uint8_t* base = codes + (int64_t)g * T_max * (kKvHeadDim / 2) + 16 * c;
     const float* sbase = scales + (int64_t)g * T_max;
     constexpr int IT = CHUNK / 16;
-    u32x4_t cb[DEPTH];
-    float sb[DEPTH];
-    auto load = [&](int it, int slot) {  // clamped: keys past T reload T - 1
-        const int t = min(t0 + 16 * min(it, IT - 1) + j, T - 1);
-        cb[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(base + (int64_t)t * (kKvHeadDim / 2)));
-        sb[slot] = sbase[t];
-    };
+    const int Tc = nw.pos;  // cached positions read here: 0 .. Tc - 1
+    if (Tc > t0) {  // wave-uniform: this chunk holds cached positions
+        // the scales of every step first, then the code loads DEPTH steps ahead:
+        // the steps then wait on code loads only
+        float sb[IT];
 #pragma unroll
-    for (int p = 0; p < DEPTH; ++p) load(p, p);
+        for (int it = 0; it < IT; ++it) sb[it] = sbase[min(t0 + 16 * it + j, Tc - 1)];
+        __builtin_amdgcn_sched_barrier(0);  // issued before the code loads, in this order
+        u32x4_t cb[DEPTH];
+        auto load = [&](int it, int slot) {  // clamped: keys past Tc reload Tc - 1
+            const int t = min(t0 + 16 * min(it, IT - 1) + j, Tc - 1);
+            cb[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(base + (int64_t)t * (kKvHeadDim / 2)));
+        };
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int slot = it % DEPTH;
-        float d = kv_dot32(cb[slot], qe, qo) - 8.f * qs;
-        const float s = sb[slot];
-        if (it + DEPTH < IT) load(it + DEPTH, slot);
+        for (int p = 0; p < DEPTH; ++p) load(p, p);
+        __builtin_amdgcn_sched_barrier(0);  // all DEPTH in flight before the first wait
+        const float q8 = q8sum();
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int slot = it % DEPTH;
+            float d = kv_dot32(cb[slot], qe, qo) - q8;
+            const float s = sb[it];
+            if (it + DEPTH < IT) load(it + DEPTH, slot);
+            d += __shfl_xor(d, 1);
+            d += __shfl_xor(d, 2);
+            // every lane stores (no branch in the load pipeline): the 4 lanes of
+            // a key store the same value, keys past Tc rewrite the score of Tc - 1
+            scores[(int64_t)h * T + min(t0 + 16 * it + j, Tc - 1)] = s * d;
+            __builtin_amdgcn_sched_barrier(0);  // steps in order: each waits for its own codes only
+        }
+    }
+    // new positions of this chunk, one at a time (wave-uniform loop); the four
+    // lanes of the position's key score it exactly as above
+    if (max(Tc, t0) >= min(T, t0 + CHUNK)) return;  // wave-uniform: no new position here
+    // the compiler must not share this q sum's instructions with the one above
+    // and hoist them before the branch: that would wait for q before the first
+    // cache load is issued
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(qe[i]), "+v"(qo[i]));
+    const float q8 = q8sum();
+    const int Hkv = Hq / group;
+    for (int t = max(Tc, t0); t < min(T, t0 + CHUNK); ++t) {
+        float s;
+        const u32x4_t cw = kv_quantize_wave(nw.x + ((int64_t)(t - Tc) * Hkv + g) * kKvHeadDim, lane, s);
+        float d = kv_dot32(cw, qe, qo) - q8;
         d += __shfl_xor(d, 1);
         d += __shfl_xor(d, 2);
-        // every lane stores (no branch in the load pipeline): the 4 lanes of a
-        // key store the same value, keys past T rewrite the score of T - 1
-        scores[(int64_t)h * T + min(t0 + 16 * it + j, T - 1)] = s * d;
+        if (j == ((t - t0) & 15)) {
+            scores[(int64_t)h * T + t] = s * d;
+            if (h % group == 0) {
+                const int64_t row = (int64_t)g * T_max + t;
+                *reinterpret_cast<u32x4_t*>(nw.codes + row * (kKvHeadDim / 2) + 16 * c) = cw;
+                if (c == 0) nw.scales[row] = s;
+            }
+        }
     }
 }
 
@@ -160,9 +242,9 @@ __global__ __launch_bounds__(256) void kv_wsum_kernel(const float* __restrict__ 
                                                       int group, int T, int64_t T_max,
                                                       const uint8_t* __restrict__ codes,
                                                       const float* __restrict__ scales,
-                                                      float* __restrict__ part, int nch) {
+                                                      float* __restrict__ part, int nch, KvNew nw) {
     const int lane = threadIdx.x & 63;
-    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int w = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w >= nch * Hq) return;
     const int h = w % Hq, ch = w / Hq;
     const int g = h / group;
@@ -172,26 +254,14 @@ __global__ __launch_bounds__(256) void kv_wsum_kernel(const float* __restrict__ 
     const float* sbase = scales + (int64_t)g * T_max;
     const float* prow = pw + (int64_t)h * T;
     constexpr int IT = CHUNK / 16;
-    u32x4_t cb[DEPTH];
-    float wb[DEPTH];
-    auto load = [&](int it, int slot) {  // keys past T get weight 0
-        const int tt = t0 + 16 * min(it, IT - 1) + j;
-        const int t = min(tt, T - 1);
-        cb[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(base + (int64_t)t * (kKvHeadDim / 2)));
-        wb[slot] = tt < T ? prow[t] * sbase[t] : 0.f;
-    };
+    const int Tc = nw.pos;  // cached positions read here: 0 .. Tc - 1
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = 0.f;
     float W = 0.f;
-#pragma unroll
-    for (int p = 0; p < DEPTH; ++p) load(p, p);
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int slot = it % DEPTH;
-        const u32x4_t cw = cb[slot];
-        const float wt = wb[slot];
-        if (it + DEPTH < IT) load(it + DEPTH, slot);
+    // one position's share: weight wt times this lane's 32 nibbles (as 0..15)
+    auto accumulate = [&](const u32x4_t cw, float wt) {
+        asm("" : "+v"(wt));  // wt is rounded on its own: never contracted into W's sum
         W += wt;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -202,6 +272,54 @@ __global__ __launch_bounds__(256) void kv_wsum_kernel(const float* __restrict__ 
                 acc[8 * d + 2 * b] = fmaf(wt, (float)((lo >> (8 * b)) & 0xFFu), acc[8 * d + 2 * b]);
                 acc[8 * d + 2 * b + 1] = fmaf(wt, (float)((hi >> (8 * b)) & 0xFFu), acc[8 * d + 2 * b + 1]);
             }
+        }
+    };
+    if (Tc > t0) {  // wave-uniform: this chunk holds cached positions
+        // The weights' operands of every step first (unconditional loads at
+        // clamped positions), then the code loads DEPTH steps ahead: the steps
+        // wait on code loads only. A load under the "key < Tc" condition would
+        // become a branch that waits for every load in flight.
+        float pb[IT], sb[IT];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int t = min(t0 + 16 * it + j, Tc - 1);
+            pb[it] = prow[t];
+            sb[it] = sbase[t];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // issued before the code loads, in this order
+        u32x4_t cb[DEPTH];
+        auto load = [&](int it, int slot) {
+            const int t = min(t0 + 16 * min(it, IT - 1) + j, Tc - 1);
+            cb[slot] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(base + (int64_t)t * (kKvHeadDim / 2)));
+        };
+#pragma unroll
+        for (int p = 0; p < DEPTH; ++p) load(p, p);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int slot = it % DEPTH;
+            const u32x4_t cw = cb[slot];
+            float pv = pb[it], sv = sb[it];
+            asm("" : "+v"(pv), "+v"(sv));  // keeps the loads out of the select (no branch)
+            const float wt = t0 + 16 * it + j < Tc ? pv * sv : 0.f;  // keys past Tc: 0
+            if (it + DEPTH < IT) load(it + DEPTH, slot);
+            accumulate(cw, wt);
+            __builtin_amdgcn_sched_barrier(0);  // steps in order: each waits for its own codes only
+        }
+    }
+    // New positions (see KvNew), one at a time; only the four lanes of the
+    // position's key weigh it. A lane's new positions come after all of its
+    // cached ones, and the zero-weight steps add exact zeros to sums that are
+    // never -0, so the totals equal those of a read from the cache.
+    const int Hkv = Hq / group;
+    for (int t = max(Tc, t0); t < min(T, t0 + CHUNK); ++t) {  // wave-uniform
+        float s;
+        const u32x4_t cw = kv_quantize_wave(nw.x + ((int64_t)(t - Tc) * Hkv + g) * kKvHeadDim, lane, s);
+        const bool mine = j == ((t - t0) & 15);
+        accumulate(cw, mine ? prow[t] * s : 0.f);
+        if (mine && h % group == 0) {
+            const int64_t row = (int64_t)g * T_max + t;
+            *reinterpret_cast<u32x4_t*>(nw.codes + row * (kKvHeadDim / 2) + 16 * c) = cw;
+            if (c == 0) nw.scales[row] = s;
         }
     }
 #pragma unroll
@@ -281,25 +399,32 @@ hipError_t launch_kv_quantize(const float* const* x, int ncache, int64_t n, int6
     return hipGetLastError();
 }
 
+// xnew: the fp32 vectors of positions pos .. T - 1, quantized into codes/scales
+// by this launch (null: none, pos ignored)
 hipError_t launch_kv_scores(const float* q, int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max,
                             const uint8_t* codes, const float* scales, float* scores,
-                            hipStream_t st) {
+                            const float* xnew, int64_t pos, hipStream_t st) {
     const int nch = kv_chunks(T);
     const int64_t waves = (int64_t)nch * Hq;
+    const KvNew nw{xnew, const_cast<uint8_t*>(codes), const_cast<float*>(scales),
+                   (int)(xnew ? pos : T)};
     hipLaunchKernelGGL((kv_scores_kernel<kKvChunk, kKvDepth>), dim3((unsigned)((waves + 3) / 4)),
                        dim3(256), 0, st, q, (int)Hq, (int)(Hq / Hkv), (int)T, T_max, codes, scales,
-                       scores, nch);
+                       scores, nch, nw);
     return hipGetLastError();
 }
 
 hipError_t launch_kv_weighted_sum(const float* p, int64_t Hq, int64_t Hkv, int64_t T,
                                   int64_t T_max, const uint8_t* codes, const float* scales,
-                                  float* out, float* part, hipStream_t st) {
+                                  float* out, float* part, const float* xnew, int64_t pos,
+                                  hipStream_t st) {
     const int nch = kv_chunks(T);
     const int64_t waves = (int64_t)nch * Hq;
+    const KvNew nw{xnew, const_cast<uint8_t*>(codes), const_cast<float*>(scales),
+                   (int)(xnew ? pos : T)};
     hipLaunchKernelGGL((kv_wsum_kernel<kKvChunk, kKvDepth>), dim3((unsigned)((waves + 3) / 4)),
                        dim3(256), 0, st, p, (int)Hq, (int)(Hq / Hkv), (int)T, T_max, codes, scales,
-                       part, nch);
+                       part, nch, nw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kv_wsum_add_kernel, dim3((unsigned)((Hq * kKvHeadDim + 15) / 16)),

@@ -159,11 +159,15 @@ int kv_chunks(int64_t T);  // position chunks of the weighted sum (partials per 
 hipError_t launch_kv_quantize(const float* const* x, int ncache, int64_t n, int64_t H,
                               int64_t pos, int64_t T_max, uint8_t* const* codes,
                               float* const* scales, hipStream_t st);
+// xnew (fp32 [T - pos][Hkv][128], or null): positions pos .. T - 1 are quantized
+// into codes/scales by the product's own launch and never read from the cache
+constexpr int kKvFuseMax = 16;  // the entry points fuse appends of up to this many positions
 hipError_t launch_kv_scores(const float* q, int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max,
                             const uint8_t* codes, const float* scales, float* scores,
-                            hipStream_t st);
+                            const float* xnew, int64_t pos, hipStream_t st);
 hipError_t launch_kv_weighted_sum(const float* p, int64_t Hq, int64_t Hkv, int64_t T,
                                   int64_t T_max, const uint8_t* codes, const float* scales,
-                                  float* out, float* part, hipStream_t st);
+                                  float* out, float* part, const float* xnew, int64_t pos,
+                                  hipStream_t st);
 
 }  // namespace w4

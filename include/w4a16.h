@@ -402,6 +402,21 @@ int w4_kv_append(const float* k, const float* v, int64_t n, int64_t Hkv, int64_t
 int w4_kv_scores(const float* q, int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max,
                  const uint8_t* codes, const float* scales, float* scores, void* stream);
 
+/*
+ * The key append fused into the scores ([Shimmy] §3.2 quantizes on append;
+ * [airllm] §3.1 fuses the operators of a step): k_new fp32
+ * [n][Hkv][W4_KV_HEAD_DIM] is quantized into positions pos .. pos + n - 1 of the
+ * key cache, and scores fp32 [Hq][T] are written over the T = pos + n positions.
+ * Cache contents and scores equal w4_kv_quantize then w4_kv_scores bit for bit.
+ * For n <= 16 this is one launch, which takes the new positions' codes and
+ * scales from registers and reads only positions < pos from the cache; for
+ * larger n the append launch, then the scores launch. 1 <= n, pos + n <= T_max,
+ * other shapes and errors as for w4_kv_quantize and w4_kv_scores.
+ */
+int w4_kv_scores_append(const float* q, const float* k_new, int64_t n, int64_t Hq, int64_t Hkv,
+                        int64_t pos, int64_t T_max, uint8_t* k_codes, float* k_scales,
+                        float* scores, void* stream);
+
 /* Host-only. Workspace bytes w4_kv_weighted_sum needs for Hq heads over T positions. */
 size_t w4_kv_weighted_sum_workspace_bytes(int64_t Hq, int64_t T);
 
@@ -417,6 +432,20 @@ size_t w4_kv_weighted_sum_workspace_bytes(int64_t Hq, int64_t T);
 int w4_kv_weighted_sum(const float* p, int64_t Hq, int64_t Hkv, int64_t T, int64_t T_max,
                        const uint8_t* codes, const float* scales, float* out, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * The value append fused into the weighted sum, as w4_kv_scores_append does for
+ * the keys: v_new fp32 [n][Hkv][W4_KV_HEAD_DIM] goes into positions pos .. pos +
+ * n - 1 of the value cache, and out fp32 [Hq][W4_KV_HEAD_DIM] is the weighted sum
+ * over the T = pos + n positions with p fp32 [Hq][T]. The workspace needs
+ * w4_kv_weighted_sum_workspace_bytes(Hq, T) bytes. Cache contents and out equal
+ * w4_kv_quantize then w4_kv_weighted_sum bit for bit. For n <= 16 the append
+ * adds no launch; for larger n it is a launch of its own first.
+ */
+int w4_kv_weighted_sum_append(const float* p, const float* v_new, int64_t n, int64_t Hq,
+                              int64_t Hkv, int64_t pos, int64_t T_max, uint8_t* v_codes,
+                              float* v_scales, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char* w4_last_error(void);

@@ -120,6 +120,17 @@ def test_kv_argument_validation_without_a_device():
     assert L.w4_kv_weighted_sum(16, 8, 4, 10, 16, 16, 16, 16, 16, need - 16, None) == -5
     assert L.w4_kv_weighted_sum(16, 8, 4, 0, 16, 16, 16, 16, 16, need, None) == -2   # no position
     assert L.w4_kv_weighted_sum(16, 8, 4, 10, 16, 16, 16, 16, 8, need, None) == -3
+    # fused appends: (q|p, new, n, Hq, Hkv, pos, T_max, codes, scales, out[, ws, bytes], stream)
+    assert L.w4_kv_scores_append(16, 16, 0, 8, 4, 3, 16, 16, 16, 16, None) == -2      # no new position
+    assert L.w4_kv_scores_append(16, 16, 2, 8, 4, 15, 16, 16, 16, 16, None) == -2     # past T_max
+    assert L.w4_kv_scores_append(16, 16, 1, 6, 4, 3, 16, 16, 16, 16, None) == -2      # 6 heads over 4
+    assert L.w4_kv_scores_append(16, None, 1, 8, 4, 3, 16, 16, 16, 16, None) == -1
+    assert L.w4_kv_scores_append(16, 16, 1, 8, 4, 3, 16, 16, 16, 8, None) == -3
+    need = L.w4_kv_weighted_sum_workspace_bytes(8, 4)
+    assert L.w4_kv_weighted_sum_append(16, 16, 1, 8, 4, 3, 16, 16, 16, 16, 16, need - 16, None) == -5
+    assert L.w4_kv_weighted_sum_append(16, 16, 0, 8, 4, 3, 16, 16, 16, 16, 16, need, None) == -2
+    assert L.w4_kv_weighted_sum_append(16, 16, 1, 8, 4, 3, 16, None, 16, 16, 16, need, None) == -1
+    assert L.w4_kv_weighted_sum_append(16, 24, 1, 8, 4, 3, 16, 16, 16, 16, 16, need, None) == -3
 
 
 def test_quantize_argument_validation_without_a_device():

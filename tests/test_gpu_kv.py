@@ -103,6 +103,71 @@ def test_kv_append_equals_two_quantize_calls():
     assert np.array_equal(vc[1].cpu().numpy()[:, pos:pos + n].view(np.uint32), s_ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("Hq,Hkv,pos,n,T_max", [
+    (32, 32, 8192, 1, 8193),   # a 7B-shaped layer's decode step at 8K context, as the bench runs it
+    (32, 8, 999, 1, 1024),     # query heads in groups of 4, ragged last chunk
+    (8, 2, 0, 1, 5),           # empty cache: the new position is all there is
+    (4, 4, 0, 16, 16),         # sixteen new positions, nothing cached
+    (6, 3, 120, 16, 300),      # new positions across a chunk boundary
+    (6, 3, 128, 1, 300),       # the new position opens a chunk
+    (4, 2, 29, 5, 64),         # across a 16-position step
+    (4, 2, 10, 17, 64),        # more than sixteen: the append is a launch of its own
+    (4, 2, 100, 40, 200),
+])
+def test_kv_append_fused_into_products(Hq, Hkv, pos, n, T_max):
+    """w4_kv_scores_append / w4_kv_weighted_sum_append against the append launch
+    followed by the plain products: caches and outputs bit for bit, and the
+    outputs against the oracle over the whole cache."""
+    print(f"[kv_fused_append] Hq={Hq} Hkv={Hkv} pos={pos} n={n} T_max={T_max}", flush=True)
+    name = f"kvf.{Hq}.{Hkv}.{pos}.{n}"
+    T = pos + n
+    K = _vectors((Hkv, T_max, D), name + ".K")
+    V = _vectors((Hkv, T_max, D), name + ".V", seed=1)
+    k_new = np.ascontiguousarray(K[:, pos:T].transpose(1, 0, 2))      # [n][Hkv][D]
+    v_new = np.ascontiguousarray(V[:, pos:T].transpose(1, 0, 2))
+    kc, ks = oracle.kv_quantize(K)
+    vc, vs = oracle.kv_quantize(V)
+
+    def old_cache(c, s):
+        """The cache with positions < pos filled (from the oracle), the rest stale."""
+        cd = torch.full((Hkv, T_max, D // 2), 0x5A, dtype=torch.uint8, device="cuda")
+        sd = torch.full((Hkv, T_max), float("nan"), dtype=torch.float32, device="cuda")
+        cd[:, :pos] = torch.from_numpy(c[:, :pos]).cuda()
+        sd[:, :pos] = torch.from_numpy(s[:, :pos]).cuda()
+        return cd, sd
+
+    q = torch.from_numpy(synth.normal_f32((Hq, D), 1.0, 0, name + ".q")).cuda()
+    knd, vnd = torch.from_numpy(k_new).cuda(), torch.from_numpy(v_new).cuda()
+    # the launch sequence
+    ka = old_cache(kc, ks)
+    w4.kv_quantize(knd, ka[0], ka[1], pos)
+    sc_a = w4.kv_scores(q, ka[0], ka[1], T)
+    p = torch.softmax(sc_a / np.float32(np.sqrt(D)), dim=1).contiguous()
+    va = old_cache(vc, vs)
+    w4.kv_quantize(vnd, va[0], va[1], pos)
+    out_a = w4.kv_weighted_sum(p, va[0], va[1])
+    # fused
+    kb = old_cache(kc, ks)
+    sc_b = w4.kv_scores_append(q, knd, kb[0], kb[1], pos)
+    vb = old_cache(vc, vs)
+    ws = torch.full((w4.kv_weighted_sum_workspace_bytes(Hq, T),), 0xFF, dtype=torch.uint8, device="cuda")
+    out_b = w4.kv_weighted_sum_append(p, vnd, vb[0], vb[1], pos, workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in ((ka, kb), (va, vb)):
+        assert torch.equal(a[0], b[0]), "codes differ"
+        assert torch.equal(a[1][:, :T].view(torch.int32), b[1][:, :T].view(torch.int32)), "scales differ"
+        assert torch.isnan(b[1][:, T:]).all(), "positions past pos + n written"
+    assert torch.equal(sc_a.view(torch.int32), sc_b.view(torch.int32)), "scores differ"
+    assert torch.equal(out_a.view(torch.int32), out_b.view(torch.int32)), "weighted sums differ"
+    # the new positions' codes against the oracle's codec
+    assert np.array_equal(kb[0][:, pos:T].cpu().numpy(), kc[:, pos:T])
+    assert np.array_equal(vb[1][:, pos:T].cpu().numpy().view(np.uint32), vs[:, pos:T].view(np.uint32))
+    y, S = oracle.kv_scores(q.cpu().numpy(), kc[:, :T], ks[:, :T])
+    assert tolerance_ratio(sc_b.cpu().numpy(), y, S) <= 1.0
+    yo, So = oracle.kv_weighted_sum(p.cpu().numpy(), vc[:, :T], vs[:, :T])
+    assert tolerance_ratio(out_b.cpu().numpy(), yo, So) <= 1.0
+
+
 def test_kv_quantize_then_read_back():
     """The device codec feeds the device products: quantize K on the GPU, score
     one-hot queries, and read the dequantized cache back element by element."""
