@@ -90,10 +90,17 @@ __global__ __launch_bounds__(64 * RW) void moe1_gate_up_kernel(Moe1Args a) {
     const bool shared = bid >= a.k * a.tiles_r;
     const int slot = shared ? 0 : bid / a.tiles_r;
     const int tile = shared ? bid - a.k * a.tiles_r : bid % a.tiles_r;
-    // the expert id, then this wavefront's share of the activations (they do
-    // not depend on the id), then the weights
+    // the expert id (or the router logits it is selected from), then this
+    // wavefront's share of the activations (they do not depend on the id), then
+    // the weights: the loads drain in issue order, so waiting for the first
+    // ones does not wait for the later ones
     int e = 0;
     if constexpr (!SEL) e = shared ? 0 : a.ids[slot];
+    float lt = 0.f, l64 = 0.f;
+    if constexpr (SEL) {
+        const float* lgt = a.logits;
+        if (!shared) topk_ranked_load([&](int e) { return lgt[e]; }, a.E, lt, l64);  // block-uniform
+    }
     XStage<S, XV, 64 * RW> xstage;
     xstage.fetch(a.x, VR, threadIdx.x);
     asm volatile("" ::: "memory");  // keep the weight loads behind these
@@ -104,8 +111,7 @@ __global__ __launch_bounds__(64 * RW) void moe1_gate_up_kernel(Moe1Args a) {
             __shared__ uint64_t keys[128];
             __shared__ int part[256];
             __shared__ float stat[2];
-            const float* lgt = a.logits;
-            topk_ranked([&](int e) { return lgt[e]; }, a.E, a.k, sel_id, sel_w, keys, part, stat);
+            topk_ranked_select(lt, l64, a.E, a.k, sel_id, sel_w, keys, part, stat);
             __syncthreads();
             e = sel_id[slot];
             if (bid == 0 && (int)threadIdx.x < a.k) {
@@ -186,10 +192,14 @@ __global__ __launch_bounds__(64 * RW) void moe1_down_kernel(Moe1Args a) {
     uint32_t* sbase = smem + 8 * regw;
 
     // routing of this lane's slot group first, then this thread's share of h
-    // and hs (independent of the routing), then the weights
+    // and hs and the shared expert's rows (independent of the routing), then
+    // the routed rows. The routing loads are unconditional (clamped slot) and
+    // the slot test comes at use: a load under it would compile into a branch
+    // whose join waits for it before anything else is issued.
     const int g = lane >> 3, sl = lane & 7;
-    int e = g < k ? a.ids[g] : -1;
-    const float w_raw = g < k ? a.wts[g] : 0.f;
+    const int gq = max(min(g, k - 1), 0);
+    int e = a.ids[gq];
+    const float w_raw = a.wts[gq];
     const int total = k * VRF + VRS;
     u32x4_t d[XV][Q];
 #pragma unroll
@@ -201,12 +211,27 @@ __global__ __launch_bounds__(64 * RW) void moe1_down_kernel(Moe1Args a) {
         for (int q = 0; q < Q; ++q) d[t][q] = reinterpret_cast<const u32x4_t*>(src)[q];
     }
     asm volatile("" ::: "memory");  // keep the weight loads behind these
-    const bool valid = e >= 0 && e < a.E;
-    const float wg = valid ? w_raw : 0.f;
-    if (!valid) e = 0;  // a readable expert; its contribution is multiplied by 0
     const int row0 = blockIdx.x * RW * R + wave * R;
     u32x4_t cr[R][NVD], cs[R][NVS > 0 ? NVS : 1];
     float sr[R][NVD], br[R][NVD], ss[R][NVS > 0 ? NVS : 1], bs[R][NVS > 0 ? NVS : 1];
+    if constexpr (NVS > 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t n = min(row0 + r, D - 1);
+            const uint8_t *cp, *sp, *bp;
+            m1_row<S>(a.sdown, 0, n, Fs, cp, sp, bp);
+#pragma unroll
+            for (int t = 0; t < NVS; ++t) {
+                const int v = min(lane + 64 * t, VRS - 1);
+                cs[r][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cp) + v);
+                m1_scale<S>(sp, bp, v / T::VPG, ss[r][t], bs[r][t]);
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // nothing that waits for the routing moves above this
+    const bool valid = g < k && e >= 0 && e < a.E;
+    const float wg = valid ? w_raw : 0.f;
+    if (!valid) e = 0;  // a readable expert; its contribution is multiplied by 0
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int64_t n = min(row0 + r, D - 1);
@@ -217,15 +242,6 @@ __global__ __launch_bounds__(64 * RW) void moe1_down_kernel(Moe1Args a) {
             const int v = min(sl + 8 * t, VRF - 1);
             cr[r][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cp) + v);
             m1_scale<S>(sp, bp, v / T::VPG, sr[r][t], br[r][t]);
-        }
-        if constexpr (NVS > 0) {
-            m1_row<S>(a.sdown, 0, n, Fs, cp, sp, bp);
-#pragma unroll
-            for (int t = 0; t < NVS; ++t) {
-                const int v = min(lane + 64 * t, VRS - 1);
-                cs[r][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cp) + v);
-                m1_scale<S>(sp, bp, v / T::VPG, ss[r][t], bs[r][t]);
-            }
         }
     }
     // commit the staged rows (waits for them only; the weights stay in flight)

@@ -314,6 +314,10 @@ __global__ __launch_bounds__(64 * NW) void moe_routed_kernel(MoeRoutedArgs a) {
             compute(cb[u], r0 + u);
         }
     }
+    // the output stage's pair ids (see 6.), issued under the last steps
+    int pv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pv[r] = a.pairs[first + min(4 * g + r, cnt - 1)];
 #pragma unroll
     for (int u = 0; u < DEPTH - 1; ++u)
         if (full + u < steps) compute(cb[u], full + u);
@@ -321,11 +325,19 @@ __global__ __launch_bounds__(64 * NW) void moe_routed_kernel(MoeRoutedArgs a) {
     // 6. outputs of the descriptor's pairs (slots past cnt hold garbage:
     //    their group sums were never staged)
     const int n = row0 + c16;
+    // the four pair ids first, unconditionally (clamped): a load under the
+    // slot test compiles into a branch that waits for it, one round trip per slot
+    // (for the shared expert's descriptors, first + slot < M <= the pair count)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(pv[r]));  // the loads stay unconditional
+    int64_t prs[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) prs[r] = sh ? first + min(4 * g + r, cnt - 1) : pv[r];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int slot = 4 * g + r;
         if (slot < cnt) {
-            const int64_t pr = sh ? first + slot : a.pairs[first + slot];
+            const int64_t pr = prs[r];
             if constexpr (GU) {
                 (sh ? a.hs : a.h)[pr * N + n] = (uint16_t)f32_to_bf16_rne(gelu_tanh(acc[0][r]) * acc[1][r]);
             } else {

@@ -92,23 +92,27 @@ __device__ __forceinline__ uint64_t rank_key(float v, int e) {
 // out of two barriers instead of k dependent wave-wide arg-max rounds. The
 // softmax statistics are those of topk_rounds<2> (wavefront 0, same lane
 // layout and order), so ids and weights equal its outputs bit for bit.
-// lg(e): logit of expert e < E (any memory); ids / wts: ranks 0..k-1 (any
-// memory); keys (128 u64), part (256 int), stat (2 float): LDS. Every thread of
-// the workgroup must call it (blockDim.x >= 256; threads beyond 255 only pass
-// the barriers).
+// Two steps, so that a caller can issue the logit loads first and other loads
+// behind them: topk_ranked_load gives thread t the logits of experts t and t +
+// 64 (clamped indices, every thread, no branch), topk_ranked_select ranks them.
+// ids / wts: ranks 0..k-1 (any memory); keys (128 u64), part (256 int), stat
+// (2 float): LDS. Every thread of the workgroup takes part (blockDim.x >= 256;
+// threads beyond 255 only pass the barriers).
 template <typename Get>
-__device__ void topk_ranked(Get lg, int E, int k, int32_t* __restrict__ ids,
-                            float* __restrict__ wts, uint64_t* keys, int* part, float* stat) {
+__device__ __forceinline__ void topk_ranked_load(Get lg, int E, float& lt, float& l64) {
     const int t = threadIdx.x;
-    if (t < 128) keys[t] = rank_key(t < E ? lg(t) : -INFINITY, t);
+    lt = lg(min(t, E - 1));
+    l64 = lg(min(t + 64, E - 1));
+}
+
+__device__ __forceinline__ void topk_ranked_select(float lt, float l64, int E, int k,
+                                                   int32_t* __restrict__ ids,
+                                                   float* __restrict__ wts, uint64_t* keys,
+                                                   int* part, float* stat) {
+    const int t = threadIdx.x;
+    if (t < 128) keys[t] = rank_key(t < E ? lt : -INFINITY, t);
     if (t < 64) {
-        float v[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int e = t + 64 * j;
-            const float x = lg(min(e, E - 1));
-            v[j] = e < E ? x : -INFINITY;
-        }
+        const float v[2] = {t < E ? lt : -INFINITY, t + 64 < E ? l64 : -INFINITY};
         float mx = fmaxf(v[0], v[1]);
         mx = wave_max_dpp(mx);
         float s = 0.f;
@@ -134,7 +138,7 @@ __device__ void topk_ranked(Get lg, int E, int k, int32_t* __restrict__ ids,
         const int r = part[t] + part[t + 128];
         if (r < k) {
             ids[r] = t;
-            wts[r] = expf(lg(t) - stat[0]) * stat[1];
+            wts[r] = expf(lt - stat[0]) * stat[1];
         }
     }
 }
