@@ -454,7 +454,7 @@ def run_moe(c: Ctx, a):
         ws = w4.moe_layer_workspace(M, k, E, D, F, Fs, c.dev)
         launches = ("one (router, top-k, shared and routed gate/up, down: work items of one persistent grid)"
                     if one and single else "router gemv, gate/up with the top-k inside, down" if one else
-                    "router (fused with top-k), bucketing, gate/up, down, combine")
+                    "router gemv, top-k, bucketing, gate/up, down, combine")
 
         def step():
             for l, (router, gate, up, down, shared) in enumerate(L):
