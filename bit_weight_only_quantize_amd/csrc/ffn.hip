@@ -75,7 +75,8 @@ __device__ __forceinline__ void ffn_scale(const uint8_t* s, const uint8_t* b, in
 // ---------------------------------------------------------------- gate/up item
 // R (gate, up) row pairs per wavefront. HANDOFF: h goes to the kHRep copies
 // (device-scope stores) and the item counts itself; else h goes to a.h only.
-template <int S, int NV, int R, bool HANDOFF>
+// XV: activation vectors staged per thread (the row's D / KV vectors <= 256 XV).
+template <int S, int NV, int R, bool HANDOFF, int XV = 1>
 __device__ void ffn_gate_up_item(const FfnArgs& a, int item, uint32_t* smem, int* sflag) {
     using T = Traits<S>;
     using L = XLayout<S, 1>;
@@ -84,10 +85,10 @@ __device__ void ffn_gate_up_item(const FfnArgs& a, int item, uint32_t* smem, int
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int D = a.D, F = a.F, VR = D / T::KV;
-    const int64_t rowbytes = (int64_t)D / 2, groups = D / T::GROUP;
+    const int64_t rowbytes = (int64_t)D * T::BITS / 8, groups = D / T::GROUP;
     uint32_t* xs = smem;
     float* XS = reinterpret_cast<float*>(smem + D / 2);
-    XStage<S, 1, kFfnThreads> xstage;  // D / 32 <= 256 vectors
+    XStage<S, XV, kFfnThreads> xstage;
     xstage.fetch(a.x, VR, tid);
     asm volatile("" ::: "memory");  // the weight loads go out behind the activations
     const int row0 = item * (kFfnRW * R) + wave * R;
@@ -285,10 +286,10 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_kernel(FfnArgs a) {
 // The gate/up rows on their own (one token): h = bf16(gelu_tanh(g) * u) to a.h,
 // one workgroup per RW * 2 row pairs; the down projection follows as a GEMV
 // launch.
-template <int S, int NV>
+template <int S, int NV, int XV>
 __global__ __launch_bounds__(kFfnThreads) void ffn_gate_up_kernel(FfnArgs a) {
     extern __shared__ __align__(16) uint32_t smem[];
-    ffn_gate_up_item<S, NV, 2, false>(a, blockIdx.x, smem, nullptr);
+    ffn_gate_up_item<S, NV, 2, false, XV>(a, blockIdx.x, smem, nullptr);
 }
 
 // h = bf16(gelu_tanh(g) * u) elementwise (the launch sequence for M > 1).
@@ -377,18 +378,38 @@ hipError_t launch_ffn_fused(int scheme, const void* const* gate, const void* con
                                : pick_ffn<AFF4_G64>(nvg, nvd, a, lds, st);
 }
 
+template <int S, int NV>
+static void go_ffn_gate_up_nv(const FfnArgs& a, int blocks, size_t lds, hipStream_t st) {
+    constexpr int XV = NV * 64 > 256 ? 2 : 1;  // D / KV vectors <= 64 NV
+    hipLaunchKernelGGL((ffn_gate_up_kernel<S, NV, XV>), dim3(blocks), dim3(kFfnThreads), lds, st, a);
+}
+
 template <int S>
 static hipError_t go_ffn_gate_up(int nv, const FfnArgs& a, int blocks, size_t lds, hipStream_t st) {
-    switch (nv) {
-        case 1: hipLaunchKernelGGL((ffn_gate_up_kernel<S, 1>), dim3(blocks), dim3(kFfnThreads), lds, st, a); break;
-        case 2: hipLaunchKernelGGL((ffn_gate_up_kernel<S, 2>), dim3(blocks), dim3(kFfnThreads), lds, st, a); break;
-        case 3: hipLaunchKernelGGL((ffn_gate_up_kernel<S, 3>), dim3(blocks), dim3(kFfnThreads), lds, st, a); break;
-        default: hipLaunchKernelGGL((ffn_gate_up_kernel<S, 4>), dim3(blocks), dim3(kFfnThreads), lds, st, a); break;
+    if constexpr (Traits<S>::BITS == 4) {  // D / 32 <= 256 vectors
+        switch (nv) {
+            case 1: go_ffn_gate_up_nv<S, 1>(a, blocks, lds, st); break;
+            case 2: go_ffn_gate_up_nv<S, 2>(a, blocks, lds, st); break;
+            case 3: go_ffn_gate_up_nv<S, 3>(a, blocks, lds, st); break;
+            default: go_ffn_gate_up_nv<S, 4>(a, blocks, lds, st); break;
+        }
+    } else {  // 8-bit: D / 16 <= 512 vectors
+        switch (nv) {
+            case 1: go_ffn_gate_up_nv<S, 1>(a, blocks, lds, st); break;
+            case 2: go_ffn_gate_up_nv<S, 2>(a, blocks, lds, st); break;
+            case 3: go_ffn_gate_up_nv<S, 3>(a, blocks, lds, st); break;
+            case 4: go_ffn_gate_up_nv<S, 4>(a, blocks, lds, st); break;
+            case 5: go_ffn_gate_up_nv<S, 5>(a, blocks, lds, st); break;
+            case 6: go_ffn_gate_up_nv<S, 6>(a, blocks, lds, st); break;
+            case 7: go_ffn_gate_up_nv<S, 7>(a, blocks, lds, st); break;
+            default: go_ffn_gate_up_nv<S, 8>(a, blocks, lds, st); break;
+        }
     }
     return hipGetLastError();
 }
 
 bool ffn_gate_up_ok(int scheme, int64_t D, int64_t F) {
+    if (scheme == AFF8_G64) return D % 64 == 0 && F % 64 == 0 && D / 16 <= 512;
     if (scheme != SYM4_G128 && scheme != AFF4_G64) return false;
     const int64_t g = scheme == SYM4_G128 ? 128 : 64;
     return D % g == 0 && F % g == 0 && D / 32 <= 256;
@@ -405,10 +426,12 @@ hipError_t launch_ffn_gate_up(int scheme, const void* const* gate, const void* c
     a.D = (int)D;
     a.F = (int)F;
     const int blocks = (int)((F + kFfnRW * 2 - 1) / (kFfnRW * 2));
-    const size_t lds = (size_t)(D / 2 + D / 32) * 4;
-    const int nv = ffn_nv(D / 32);
+    const int64_t VR = D / (scheme == AFF8_G64 ? 16 : 32);  // 16-byte code vectors per row
+    const size_t lds = (size_t)(D / 2 + VR) * 4;
+    const int nv = ffn_nv(VR);
     return scheme == SYM4_G128 ? go_ffn_gate_up<SYM4_G128>(nv, a, blocks, lds, st)
-                               : go_ffn_gate_up<AFF4_G64>(nv, a, blocks, lds, st);
+           : scheme == AFF4_G64 ? go_ffn_gate_up<AFF4_G64>(nv, a, blocks, lds, st)
+                                : go_ffn_gate_up<AFF8_G64>(nv, a, blocks, lds, st);
 }
 
 hipError_t launch_ffn_act(const float* g, const float* u, uint16_t* h, int64_t n, hipStream_t st) {

@@ -193,12 +193,13 @@ static bool try_mfma_gated(const void* const* codes, const void* const* scale,
 hipError_t launch_gemv_mfma_gated(int scheme, const void* const* gate, const void* const* up,
                                   int64_t N, int64_t K, const uint16_t* x, int64_t M, uint16_t* h,
                                   hipStream_t st) {
-    if (!gemv_mfma_ok(scheme, K, M) || scheme == AFF8_G64 || N <= 0) return hipErrorNotSupported;
+    if (!gemv_mfma_ok(scheme, K, M) || N <= 0) return hipErrorNotSupported;
     const void* c[2] = {gate[0], up[0]};
     const void* s[2] = {gate[1], up[1]};
     const void* b[2] = {gate[2], up[2]};
-    const bool ok = scheme == SYM4_G128 ? try_mfma_gated<SYM4_G128>(c, s, b, N, K, x, M, h, st)
-                                        : try_mfma_gated<AFF4_G64>(c, s, b, N, K, x, M, h, st);
+    const bool ok = scheme == SYM4_G128  ? try_mfma_gated<SYM4_G128>(c, s, b, N, K, x, M, h, st)
+                    : scheme == AFF4_G64 ? try_mfma_gated<AFF4_G64>(c, s, b, N, K, x, M, h, st)
+                                         : try_mfma_gated<AFF8_G64>(c, s, b, N, K, x, M, h, st);
     return ok ? hipGetLastError() : hipErrorNotSupported;
 }
 

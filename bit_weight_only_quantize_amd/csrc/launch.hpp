@@ -148,7 +148,7 @@ hipError_t launch_ffn_fused(int scheme, const void* const* gate, const void* con
                             const void* const* down, int64_t D, int64_t F, const uint16_t* x,
                             uint16_t* h, float* y, void* ws, long long wait_limit, int withhold,
                             hipStream_t st);
-// one token, the gate/up rows alone (4-bit schemes, D / 32 <= 256): h to h
+// one token, the gate/up rows alone (4-bit: D / 32 <= 256; 8-bit: D / 16 <= 512): h to h
 bool ffn_gate_up_ok(int scheme, int64_t D, int64_t F);
 hipError_t launch_ffn_gate_up(int scheme, const void* const* gate, const void* const* up, int64_t D,
                               int64_t F, const uint16_t* x, uint16_t* h, hipStream_t st);

@@ -299,11 +299,14 @@ void w4_moe_layer_set_wait(int64_t max_polls, int withhold);
  * (fp32 accumulate). [airllm] §3.1 credits its decode speed to fusing a layer's
  * operators into fewer kernel launches; [TurboFieldfare]'s M2 time table
  * spends a third of each token waiting between dependent GPU submissions.
- * One token with a 4-bit scheme and D / 32 <= 256 takes two launches: the
- * gate/up rows with the activation in their epilogue (h written once, bf16),
- * then the down GEMV. Several tokens, other shapes, or W4_FFN_PATH_SEQUENCE:
- * three launches (gate and up in one GEMV launch, the activation, down with K
- * parts for 2 <= M <= 16 where h does not fit a CU). W4_FFN_PATH_SINGLE_LAUNCH
+ * One token (D / 32 <= 256 with 4-bit codes, D / 16 <= 512 with 8-bit ones)
+ * takes two launches: the gate/up rows with the activation in their epilogue
+ * (h written once, bf16), then the down GEMV. 2 to 16 tokens take two as well
+ * where the skinny kernel can pair each gate tile with the up tile of the same
+ * rows in one workgroup (its epilogue writes h). Other shapes, or
+ * W4_FFN_PATH_SEQUENCE: three launches (gate and up in one GEMV launch, the
+ * activation, down with K parts for 2 <= M <= 16 where h does not fit a CU).
+ * W4_FFN_PATH_SINGLE_LAUNCH
  * runs one token with a 4-bit scheme, D / 32 in (64, 256] and F / 32 in
  * (320, 512] (e.g. the 7B and 13B shapes) as ONE launch: the gate/up rows and
  * the down rows are work items of a grid no larger than the GPU holds at once,
@@ -330,8 +333,8 @@ int w4a16_ffn(const w4_matrix* gate, const w4_matrix* up, const w4_matrix* down,
 /*
  * The gate/up half of w4a16_ffn on its own: h = bf16(gelu_tanh(W_gate x) *
  * (W_up x)), bf16 [M][F] (required), the launches w4a16_ffn takes for that half
- * (one for one token with a 4-bit scheme and D / 32 <= 256, else a GEMV launch
- * and the activation). workspace: at least w4_ffn_gate_up_workspace_bytes(gate,
+ * (one where the gate/up rows carry the activation in their epilogue, else a
+ * GEMV launch and the activation). workspace: at least w4_ffn_gate_up_workspace_bytes(gate,
  * M) bytes, contents irrelevant. Same limits and errors as w4a16_ffn.
  */
 size_t w4_ffn_gate_up_workspace_bytes(const w4_matrix* gate, int64_t M);

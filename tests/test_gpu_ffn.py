@@ -2,12 +2,13 @@
 h = bf16(gelu_tanh(W_gate x) * (W_up x)), y = W_down h.
 
 One token takes two launches by default (gate/up rows with the activation in
-their epilogue, then the down GEMV); switched on, the 7B / 13B shapes run as a
-single launch whose down rows wait for h through device-scope words; several
-tokens (and any shape on request) take the three-launch sequence. For one token
-the three paths must give the same bits (the same per-row arithmetic in the
-same order), on consecutive calls sharing one workspace and inside a replayed
-HIP graph. Against the oracle (its own quantization of the same seeded weights and
+their epilogue, then the down GEMV), 4-bit and 8-bit codes alike; switched on,
+the 7B / 13B shapes run as a single launch whose down rows wait for h through
+device-scope words; several tokens take the skinny kernel in gated-pair mode
+(gate and up tiles of the same rows in one workgroup) where the tiles pair up;
+the rest (and any shape on request) take the three-launch sequence. The paths
+must give the same bits (the same per-row arithmetic in the same order), on
+consecutive calls sharing one workspace and inside a replayed HIP graph. Against the oracle (its own quantization of the same seeded weights and
 its fp64 chain): every h within the interval the gate/up tolerance allows plus
 one bf16 rounding, y within 2e-3*S + 1e-5 with S = sum|w_down||h|. The give-up
 path of the single launch's wait is forced from the host (the "h complete" flag
@@ -132,7 +133,6 @@ def test_several_tokens_match_oracle(M):
     (1, 2048, 768, "aff4_g64"),    # two launches (outside the single launch's shapes)
     (1, 9216, 1024, "sym4_g128"),  # D / 32 > 256: the sequence
     (3, 2048, 768, "aff4_g64"),
-    (1, 1024, 2048, "aff8_g64"),   # 8-bit codes
 ])
 def test_other_shapes_take_the_sequence(M, D, F, scheme):
     print(f"[ffn] sequence M={M} D={D} F={F} {scheme}", flush=True)
@@ -229,3 +229,28 @@ def test_several_tokens_gated_launch_equals_the_sequence(M, D, F, scheme):
     assert torch.equal(h0.view(torch.int16), h1.view(torch.int16))
     assert torch.equal(y0, y1)
 
+
+
+@pytest.mark.parametrize("M,D,F", [
+    (1, 1024, 2048),
+    (1, 4096, 11008),   # 7B shape: 256 code vectors per row, one staged per thread
+    (1, 5120, 13824),   # 13B shape: 320 vectors, two staged per thread
+    (4, 4096, 11008),   # several tokens: the gated skinny launch with 8-bit steps
+    (16, 4096, 11008),
+    (8, 5120, 13824),
+])
+def test_8bit_codes_equal_the_sequence_and_match_the_oracle(M, D, F):
+    """W8A16 (the router's affine g64 8-bit scheme for whole layers): the gate/up
+    launch with the activation in its epilogue against gate/up GEMV + activation
+    launches, bit for bit, and the chain against the oracle."""
+    scheme = "aff8_g64"
+    print(f"[ffn] 8-bit M={M} D={D} F={F}", flush=True)
+    host, (gate, up, down) = _ffn(D, F, scheme, f"ffn.{D}.{F}.{scheme}")
+    xh = synth.activations_bf16(M, D, 37, f"ffn.x8.{M}")
+    x = dev_bf16(xh)
+    y0, h0 = w4.ffn(gate, up, down, x, want_h=True)
+    y1, h1 = _with_path(w4.FFN_PATH_SEQUENCE, lambda: w4.ffn(gate, up, down, x, want_h=True))
+    torch.cuda.synchronize()
+    assert torch.equal(h0.view(torch.int16), h1.view(torch.int16))
+    assert torch.equal(y0, y1)
+    _check_oracle(xh, h0, y0, host, scheme)
