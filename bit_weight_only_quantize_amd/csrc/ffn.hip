@@ -292,7 +292,8 @@ __global__ __launch_bounds__(kFfnThreads) void ffn_gate_up_kernel(FfnArgs a) {
     ffn_gate_up_item<S, NV, 2, false, XV>(a, blockIdx.x, smem, nullptr);
 }
 
-// h = bf16(gelu_tanh(g) * u) elementwise (the launch sequence for M > 1).
+// h = bf16(gelu_tanh(g) * u) elementwise: the launch sequence (gate and up in
+// one GEMV launch, this, down) where the gate/up launch cannot carry it.
 __global__ __launch_bounds__(256) void ffn_act_kernel(const float* __restrict__ g,
                                                       const float* __restrict__ u,
                                                       uint16_t* __restrict__ h, int64_t n) {
