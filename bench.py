@@ -181,6 +181,57 @@ def hbm_roofline(kernel, nbytes, us, traffic=None):
             "bytes_per_launch": nbytes, "avg_launch_us": round(us, 3)}
 
 
+def stream_copy(c, nbytes=1 << 30, reps=5):
+    """A plain 1 GiB device-to-device copy timed on this machine in this run (reads and
+    writes nbytes each): what a long streaming kernel reaches here, the second
+    yardstick beside the 8 TB/s peak. Measured once per process."""
+    if getattr(c, "_copy", None) is None:
+        torch = c.torch
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=c.dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        s = e0.elapsed_time(e1) * 1e-3 / reps
+        c._copy = {"TBps": round(2 * nbytes / s / 1e12, 4), "bytes_per_copy": 2 * nbytes,
+                   "what": "torch copy_ of a 1 GiB fp32 buffer (read + write), HIP events, this box and run"}
+        del src, dst
+        torch.cuda.empty_cache()
+    return c._copy
+
+
+def gpu_clocks():
+    """The engine and memory clock levels the driver marks current (sysfs; best effort)."""
+    import glob
+    out = {}
+    for name in ("sclk", "mclk"):
+        for f in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{name}")):
+            try:
+                cur = [l.split(":", 1)[1].replace("*", "").strip() for l in open(f) if l.rstrip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                out[name] = cur[0]
+                break
+    return out or None
+
+
+def with_copy_yardstick(c, out, tbs):
+    """Attach the same-box copy rate and the decode line's share of it."""
+    cp = stream_copy(c)
+    out["stream_copy"] = cp
+    out["pct_of_stream_copy"] = round(100 * tbs / cp["TBps"], 2)
+    clk = gpu_clocks()
+    if clk:
+        out["gpu_clocks"] = clk
+    return out
+
+
 def calibration_copy(c, nbytes=1 << 30):
     """A plain elementwise copy of known size (reads and writes nbytes once each),
     run in the counter-collection mode so FETCH_SIZE / WRITE_SIZE can be scaled
@@ -401,6 +452,7 @@ def run_llama(c: Ctx, a, big: bool):
                 if c.w4.gemv_workspace_bytes(mats[0]["down"], M) else "")),
         "weights": "seeded N(0,0.02) drawn on device", "activations": "bf16 N(0,1)"})
     out["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
+    with_copy_yardstick(c, out, tbs)
     out["tok_per_s"] = round(M / (ms * 1e-3), 1)
     out["step_bytes"] = step_bytes
     traffic = None
@@ -490,6 +542,7 @@ def run_moe(c: Ctx, a):
                         "launches_per_layer": launches})
     out["hbm_TBps"] = round(tbs, 4)
     out["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
+    with_copy_yardstick(c, out, tbs)
     out["distinct_experts_per_layer"] = sum(distinct) / len(distinct)
     out["step_bytes"] = step_bytes
     traffic = (measured_traffic(f"moe_m{M}/layer")
@@ -574,6 +627,7 @@ def run_kv(c: Ctx, a):
                                                "append K and V (one launch), scores, weighted sum (+ chunk add)")},
                     dtype="f32")
     res["pct_of_hbm_peak"] = round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2)
+    with_copy_yardstick(c, res, tbs)
     res["tok_per_s"] = round(1 / (ms * 1e-3), 1)
     res["step_bytes"] = step_bytes
     traffic = (measured_traffic("kv/scores_append" if fused else "kv/scores")
