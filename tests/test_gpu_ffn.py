@@ -133,6 +133,7 @@ def test_several_tokens_match_oracle(M):
     (1, 2048, 768, "aff4_g64"),    # two launches (outside the single launch's shapes)
     (1, 9216, 1024, "sym4_g128"),  # D / 32 > 256: the sequence
     (3, 2048, 768, "aff4_g64"),
+    (64, 2048, 768, "aff4_g64"),   # the most tokens the FFN takes: multi-token VALU launches
 ])
 def test_other_shapes_take_the_sequence(M, D, F, scheme):
     print(f"[ffn] sequence M={M} D={D} F={F} {scheme}", flush=True)

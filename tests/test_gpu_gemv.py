@@ -59,6 +59,7 @@ def _run(scheme, N, K, M, name, rows=None, quantize_on_gpu=True):
     ("aff8_g64", 333, 4160, 16),      # 8-bit codes on the matrix cores: odd group count, ragged rows
     ("aff8_g64", 50, 64, 3),          # one group
     ("aff8_g64", 12370, 512, 4),      # > 256 row tiles
+    ("aff4_g64", 100, 1024, 64),      # the most tokens the GEMV takes
 ])
 def test_gemv_matches_oracle(scheme, N, K, M):
     _run(scheme, N, K, M, f"small.{scheme}.{N}x{K}")
